@@ -1,0 +1,153 @@
+/*
+ * commvq.h - C ABI of the CommVQ quantized-KV hot path for AMD MI355X (gfx950).
+ *
+ * CommVQ stores each key/value vector of the KV cache as residual vector-quantizer
+ * codes: the head dimension D is cut into groups of g scalars, every group shares
+ * one index per round into an Nc'-entry codebook, and R rounds each encode the
+ * residual the earlier rounds left ("Pith review of CommVQ", pith.science, section
+ * "What carries the argument": index sharing over group size g, R residual rounds,
+ * bit rate R*log2(Nc')/g, paper Eq. 21). Key codebook entries are blocks
+ * [[x, y], [-y, x]] that commute with the RoPE rotation of each 2-D pair (same
+ * section, paper Eq. 7; "Assumptions", Eqn 8), so a query-times-codebook table
+ * built once per decode step serves every cached position. The softmax weights
+ * are applied to the value codes before the value codebook (review, "If this is
+ * right", fourth bullet).
+ *
+ * Conventions shared by every call:
+ *  - Device pointers are HIP device allocations owned by the caller. The library
+ *    allocates nothing and keeps no state besides a thread-local error string.
+ *  - Every compute call is asynchronous on `stream` (a hipStream_t passed as
+ *    void*; NULL is the default stream) and returns before the GPU work ends.
+ *  - Calls return COMMVQ_OK (0) or a negative commvq_status; on error nothing is
+ *    launched and commvq_last_error() describes the cause.
+ *  - A codebook entry's pair (x, y) reconstructs the 2-vector (x, y) of one RoPE
+ *    pair; RoPE pairs are the interleaved channels (2p, 2p+1) with frequency
+ *    theta_p = theta_base^(-2p/D) and rotation [[cos, -sin], [sin, cos]].
+ *  - Packed record of one (token, KV head): R*(D/g) fields of log2(Nc') bits,
+ *    round-major (round outer, group inner), least significant bit first,
+ *    padded to whole bytes: commvq_code_bytes_per_token() bytes.
+ *  - Codes are chosen greedily per round: the entry nearest (squared Euclidean
+ *    distance, float32 arithmetic) to the running residual, lowest index on ties.
+ */
+#ifndef COMMVQ_H
+#define COMMVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define COMMVQ_ABI_VERSION 1
+
+typedef enum commvq_status {
+  COMMVQ_OK = 0,
+  COMMVQ_ERR_INVALID_ARG = -1, /* bad descriptor, null pointer, bad size or stride */
+  COMMVQ_ERR_UNSUPPORTED = -2, /* valid CommVQ shape that no kernel here handles */
+  COMMVQ_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  COMMVQ_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} commvq_status;
+
+typedef enum commvq_dtype { COMMVQ_F16 = 1 } commvq_dtype;
+
+/* One codebook (keys or values) for all KV heads of one layer.
+ * Pages: "What carries the argument" (codebook per subspace, group size g,
+ * R rounds, Nc' entries). */
+typedef struct commvq_codebook {
+  int32_t head_dim;    /* D: even, 2..256 */
+  int32_t group_size;  /* g scalars sharing one index: even, divides D, 2..16 */
+  int32_t n_entries;   /* Nc': power of two, 2..256 */
+  int32_t n_rounds;    /* R: 1..4 */
+  int32_t n_kv_heads;  /* Hkv >= 1 */
+  int32_t dtype;       /* COMMVQ_F16 */
+  const void* entries; /* device fp16 [Hkv][D/g][R][Nc'][g]; within a group the
+                          scalars are the interleaved (x, y) pairs */
+} commvq_codebook;
+
+/* RoPE description (review, "Assumptions": block-diagonal 2x2 rotations, Eqns 5-6). */
+typedef struct commvq_rope {
+  double theta_base; /* > 1; e.g. 500000 */
+  int32_t pairing;   /* 0 = interleaved pairs (2p, 2p+1); other values are rejected */
+  int32_t reserved;  /* must be 0 */
+} commvq_rope;
+
+/* ---- host-only queries (no GPU needed) --------------------------------- */
+
+/* COMMVQ_ABI_VERSION of the library. */
+int32_t commvq_abi_version(void);
+
+/* Text of the last error on the calling thread ("" if none). Owned by the
+ * library; valid until the thread's next call. */
+const char* commvq_last_error(void);
+
+/* Checks a descriptor's sizes (not its device pointer). COMMVQ_OK or
+ * COMMVQ_ERR_INVALID_ARG. */
+int32_t commvq_validate_codebook(const commvq_codebook* cb);
+
+/* Average stored bits per scalar, R*log2(Nc')/g (paper Eq. 21 as quoted in the
+ * review, "What carries the argument"); negative if the descriptor is invalid. */
+double commvq_bits_per_scalar(const commvq_codebook* cb);
+
+/* Bytes of one packed (token, KV head) record, ceil(R*(D/g)*log2(Nc')/8);
+ * negative commvq_status if the descriptor is invalid. */
+int64_t commvq_code_bytes_per_token(const commvq_codebook* cb);
+
+/* Workspace bytes that commvq_decode_attention needs for this shape (split-
+ * context partials); negative commvq_status on invalid arguments. */
+int64_t commvq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
+                                      const commvq_codebook* kcb, const commvq_codebook* vcb);
+
+/* ---- compute ------------------------------------------------------------ */
+
+/* Encode n_tokens tokens of all KV heads into packed records.
+ *   x      device fp16, token t head h scalar d at x[t*x_token_stride + h*D + d]
+ *          (x_token_stride in elements, >= Hkv*D)
+ *   codes  device bytes; record (t, h) starts at
+ *          codes + t*code_token_stride + h*code_head_stride (strides in bytes);
+ *          records must not overlap; every byte of each record is written.
+ * n_tokens == 0 launches nothing. Pages: "What carries the argument" (shared
+ * index per group, R residual rounds). */
+int32_t commvq_encode(const commvq_codebook* cb, const void* x, int64_t n_tokens,
+                      int64_t x_token_stride, uint8_t* codes, int64_t code_token_stride,
+                      int64_t code_head_stride, void* stream);
+
+/* Encode one new token per sequence and write it into a contiguous cache at a
+ * per-sequence position held on the device.
+ *   x          device fp16 [batch][Hkv][D]
+ *   positions  device int32 [batch]; a position outside [0, cache_len) skips
+ *              that sequence (nothing written)
+ *   cache      device bytes [batch][Hkv][cache_len][code_bytes_per_token] */
+int32_t commvq_append(const commvq_codebook* cb, const void* x, int32_t batch,
+                      const int32_t* positions, uint8_t* cache, int32_t cache_len, void* stream);
+
+/* One decode step of grouped-query attention directly on packed codes.
+ *   q        device fp32 [batch][n_q_heads][D], not yet rotated
+ *   q_pos    device int32 [batch]: the query's RoPE position (normally len-1)
+ *   kcodes, vcodes  device bytes [batch][Hkv][cache_len][bytes_per_token]
+ *   seq_lens device int32 [batch]: keys at positions [0, seq_lens[b]) are
+ *            attended; contract 1 <= seq_lens[b] <= max_seq_len <= cache_len.
+ *            Lengths are clamped to [0, max_seq_len]; a length of 0 gives a
+ *            zero output row.
+ *   n_q_heads must be a multiple of Hkv; query head hq reads KV head
+ *   hq / (n_q_heads / Hkv).
+ *   sm_scale multiplies q.k (normally 1/sqrt(D)).
+ *   out      device fp32 [batch][n_q_heads][D]
+ *   workspace device, >= commvq_decode_workspace_bytes(batch, n_q_heads,
+ *            max_seq_len, kcb, vcb) bytes, 256-byte aligned.
+ * Pages: "What carries the argument" (query-codebook factors computed once and
+ * reused over cached positions); "If this is right", fourth bullet (weights
+ * applied to value codes before the codebook). */
+int32_t commvq_decode_attention(const commvq_codebook* kcb, const commvq_codebook* vcb,
+                                const commvq_rope* rope, const float* q, const int32_t* q_pos,
+                                const uint8_t* kcodes, const uint8_t* vcodes,
+                                const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
+                                int32_t cache_len, int32_t max_seq_len, float sm_scale,
+                                float* out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COMMVQ_H */

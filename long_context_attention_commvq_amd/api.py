@@ -1,0 +1,91 @@
+"""Tensor-level conveniences over the C ABI: allocate outputs and workspace with
+torch (device memory and streams only) and call the HIP library."""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+
+class Quantizer:
+    """One residual codebook (keys or values) living on the GPU.
+
+    entries: fp16 tensor [Hkv, D/g, R, Nc', g] on a CUDA/HIP device."""
+
+    def __init__(self, entries: torch.Tensor, group_size: int):
+        if entries.dtype != torch.float16 or entries.dim() != 5:
+            raise ValueError("entries must be fp16 [Hkv, D/g, R, Nc', g]")
+        self.entries = entries.contiguous()
+        Hkv, G, R, Nc, g = self.entries.shape
+        if g != group_size:
+            raise ValueError("group_size does not match the entries' last axis")
+        self.head_dim, self.group_size, self.n_entries, self.n_rounds, self.n_kv_heads = G * g, g, Nc, R, Hkv
+        self.desc = _lib.make_codebook(self.entries, self.head_dim, g, Nc, R, Hkv)
+
+    @property
+    def bytes_per_token(self) -> int:
+        n = _lib.commvq_code_bytes_per_token(self.desc)
+        if n < 0:
+            raise _lib.CommvqError(int(n), _lib.commvq_last_error())
+        return int(n)
+
+    @property
+    def bits_per_scalar(self) -> float:
+        return _lib.commvq_bits_per_scalar(self.desc)
+
+
+def encode(quant: Quantizer, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """x fp16 [N, Hkv, D] -> packed codes uint8 [N, Hkv, bytes_per_token]."""
+    N, H, D = x.shape
+    x = x.contiguous()
+    bpt = quant.bytes_per_token
+    if out is None:
+        out = torch.empty((N, H, bpt), dtype=torch.uint8, device=x.device)
+    _lib.commvq_encode(quant.desc, x, N, H * D, out, out.stride(0), out.stride(1))
+    return out
+
+
+def encode_into_cache(quant: Quantizer, x: torch.Tensor, cache: torch.Tensor, b: int, pos0: int) -> None:
+    """Prefill: x fp16 [N, Hkv, D] -> cache[b, :, pos0:pos0+N] (cache uint8 [B, Hkv, Lmax, bpt])."""
+    N, H, D = x.shape
+    x = x.contiguous()
+    view = cache[b, :, pos0:pos0 + N]
+    _lib.commvq_encode(quant.desc, x, N, H * D, view, cache.stride(2), cache.stride(1))
+
+
+def append(quant: Quantizer, x: torch.Tensor, positions: torch.Tensor, cache: torch.Tensor) -> None:
+    """x fp16 [B, Hkv, D], positions int32 [B] (device) -> cache[b, :, positions[b]]."""
+    B = x.shape[0]
+    _lib.commvq_append(quant.desc, x.contiguous(), B, positions, cache, cache.shape[2])
+
+
+class DecodeWorkspace:
+    """Workspace sized for (batch, n_q_heads, max_seq_len) and reused across calls."""
+
+    def __init__(self, kq: Quantizer, vq: Quantizer, batch: int, n_q_heads: int, max_seq_len: int, device):
+        n = _lib.commvq_decode_workspace_bytes(batch, n_q_heads, max_seq_len, kq.desc, vq.desc)
+        if n < 0:
+            raise _lib.CommvqError(int(n), _lib.commvq_last_error())
+        self.nbytes = int(n)
+        self.buf = torch.empty(max(self.nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def decode_attention(kq: Quantizer, vq: Quantizer, q: torch.Tensor, q_pos: torch.Tensor, kcache: torch.Tensor,
+                     vcache: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, theta_base: float,
+                     sm_scale: float | None = None, out: torch.Tensor | None = None,
+                     workspace: DecodeWorkspace | None = None) -> torch.Tensor:
+    """q fp32 [B, Hq, D] -> out fp32 [B, Hq, D] over packed caches [B, Hkv, Lmax, bpt]."""
+    B, Hq, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = DecodeWorkspace(kq, vq, B, Hq, max_seq_len, q.device)
+    rope = _lib.make_rope(theta_base)
+    _lib.commvq_decode_attention(kq.desc, vq.desc, rope, q, q_pos, kcache, vcache, seq_lens, B, Hq,
+                                 kcache.shape[2], max_seq_len, sm_scale, out, workspace.buf, workspace.nbytes)
+    return out

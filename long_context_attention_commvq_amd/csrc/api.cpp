@@ -1,0 +1,276 @@
+// C ABI of libcommvq: argument validation, size queries, dispatch to kernels.
+// Validation runs entirely on the host before any HIP call, so every error path
+// is testable without a GPU.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/commvq.h"
+#include "commvq_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int32_t fail(int32_t status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int ilog2(int64_t v) {
+  int b = 0;
+  while ((int64_t(1) << b) < v) ++b;
+  return b;
+}
+
+// Shape checks shared by every entry point (descriptor sizes only).
+int32_t check_shape(const commvq_codebook* cb, const char* name, commvq::CbShape* out) {
+  if (!cb) return fail(COMMVQ_ERR_INVALID_ARG, "%s: null codebook descriptor", name);
+  const int D = cb->head_dim, g = cb->group_size, Nc = cb->n_entries, R = cb->n_rounds;
+  if (D < 2 || D > 2 * commvq::kMaxPairs || (D & 1))
+    return fail(COMMVQ_ERR_INVALID_ARG, "%s: head_dim %d must be even and in [2, %d]", name, D,
+                2 * commvq::kMaxPairs);
+  if (g < 2 || g > 16 || (g & 1) || D % g)
+    return fail(COMMVQ_ERR_INVALID_ARG, "%s: group_size %d must be even, in [2, 16] and divide head_dim %d",
+                name, g, D);
+  if (!is_pow2(Nc) || Nc < 2 || Nc > 256)
+    return fail(COMMVQ_ERR_INVALID_ARG, "%s: n_entries %d must be a power of two in [2, 256]", name, Nc);
+  if (R < 1 || R > 4) return fail(COMMVQ_ERR_INVALID_ARG, "%s: n_rounds %d must be in [1, 4]", name, R);
+  if (cb->n_kv_heads < 1) return fail(COMMVQ_ERR_INVALID_ARG, "%s: n_kv_heads %d < 1", name, cb->n_kv_heads);
+  if (cb->dtype != COMMVQ_F16) return fail(COMMVQ_ERR_INVALID_ARG, "%s: dtype %d is not COMMVQ_F16", name, cb->dtype);
+  if (out) {
+    out->D = D;
+    out->g = g;
+    out->G = D / g;
+    out->Nc = Nc;
+    out->R = R;
+    out->Hkv = cb->n_kv_heads;
+    out->bits = ilog2(Nc);
+    out->bpt = (R * (D / g) * out->bits + 7) / 8;
+  }
+  return COMMVQ_OK;
+}
+
+int32_t check_entries(const commvq_codebook* cb, const char* name) {
+  if (!cb->entries) return fail(COMMVQ_ERR_INVALID_ARG, "%s: null entries pointer", name);
+  if (reinterpret_cast<uintptr_t>(cb->entries) & 15)
+    return fail(COMMVQ_ERR_INVALID_ARG, "%s: entries pointer must be 16-byte aligned", name);
+  return COMMVQ_OK;
+}
+
+int32_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return COMMVQ_OK;
+  return fail(COMMVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int32_t decode_shapes(const commvq_codebook* kcb, const commvq_codebook* vcb, int32_t batch,
+                      int32_t n_q_heads, int32_t max_seq_len, commvq::CbShape* k, commvq::CbShape* v) {
+  int32_t st = check_shape(kcb, "key codebook", k);
+  if (st) return st;
+  st = check_shape(vcb, "value codebook", v);
+  if (st) return st;
+  if (k->D != v->D || k->g != v->g || k->Hkv != v->Hkv)
+    return fail(COMMVQ_ERR_INVALID_ARG, "key and value codebooks disagree on head_dim, group_size or n_kv_heads");
+  if (batch < 1) return fail(COMMVQ_ERR_INVALID_ARG, "batch %d < 1", batch);
+  if (n_q_heads < 1 || n_q_heads % k->Hkv)
+    return fail(COMMVQ_ERR_INVALID_ARG, "n_q_heads %d must be a positive multiple of n_kv_heads %d", n_q_heads,
+                k->Hkv);
+  const int NH = n_q_heads / k->Hkv;
+  if (NH != 1 && NH != 2 && NH != 4 && NH != 8)
+    return fail(COMMVQ_ERR_UNSUPPORTED, "query heads per KV head %d not in {1, 2, 4, 8}", NH);
+  if (max_seq_len < 1) return fail(COMMVQ_ERR_INVALID_ARG, "max_seq_len %d < 1", max_seq_len);
+  if (k->g != 2 && k->g != 4 && k->g != 8 && k->g != 16)
+    return fail(COMMVQ_ERR_UNSUPPORTED, "decode supports group_size 2, 4, 8 or 16, not %d", k->g);
+  return COMMVQ_OK;
+}
+
+void phase_table(double base, int D, commvq::PhaseTable* ph) {
+  // F_p = frac(theta_p / 2pi) * 2^64 with theta_p = base^(-2p/D), in long double.
+  const long double two_pi = 6.283185307179586476925286766559L;
+  for (int p = 0; p < D / 2; ++p) {
+    long double theta = powl((long double)base, -2.0L * p / D);
+    long double turns = theta / two_pi;
+    turns -= floorl(turns);
+    long double f = ldexpl(turns, 64);
+    unsigned long long F = f >= 18446744073709551615.0L ? ~0ULL : (unsigned long long)f;
+    ph->lo[p] = (uint32_t)(F & 0xffffffffULL);
+    ph->hi[p] = (uint32_t)(F >> 32);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t commvq_abi_version(void) { return COMMVQ_ABI_VERSION; }
+
+const char* commvq_last_error(void) { return g_err; }
+
+int32_t commvq_validate_codebook(const commvq_codebook* cb) {
+  g_err[0] = 0;
+  return check_shape(cb, "codebook", nullptr);
+}
+
+double commvq_bits_per_scalar(const commvq_codebook* cb) {
+  g_err[0] = 0;
+  commvq::CbShape s;
+  int32_t st = check_shape(cb, "codebook", &s);
+  if (st) return (double)st;
+  return (double)s.R * (double)s.bits / (double)s.g;
+}
+
+int64_t commvq_code_bytes_per_token(const commvq_codebook* cb) {
+  g_err[0] = 0;
+  commvq::CbShape s;
+  int32_t st = check_shape(cb, "codebook", &s);
+  if (st) return st;
+  return s.bpt;
+}
+
+int64_t commvq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
+                                      const commvq_codebook* kcb, const commvq_codebook* vcb) {
+  g_err[0] = 0;
+  commvq::CbShape k, v;
+  int32_t st = decode_shapes(kcb, vcb, batch, n_q_heads, max_seq_len, &k, &v);
+  if (st) return st;
+  const int chunk = commvq::decode_chunk_len(k, v, batch, n_q_heads, max_seq_len);
+  const int64_t n_chunks = (max_seq_len + chunk - 1) / chunk;
+  return (int64_t)batch * n_q_heads * n_chunks * (k.D + 2) * (int64_t)sizeof(float);
+}
+
+int32_t commvq_encode(const commvq_codebook* cb, const void* x, int64_t n_tokens, int64_t x_token_stride,
+                      uint8_t* codes, int64_t code_token_stride, int64_t code_head_stride, void* stream) {
+  g_err[0] = 0;
+  commvq::CbShape s;
+  int32_t st = check_shape(cb, "codebook", &s);
+  if (st) return st;
+  if (n_tokens < 0) return fail(COMMVQ_ERR_INVALID_ARG, "n_tokens %lld < 0", (long long)n_tokens);
+  if (n_tokens == 0) return COMMVQ_OK;
+  st = check_entries(cb, "codebook");
+  if (st) return st;
+  if (!x || !codes) return fail(COMMVQ_ERR_INVALID_ARG, "null x or codes pointer");
+  if (reinterpret_cast<uintptr_t>(x) & 3) return fail(COMMVQ_ERR_INVALID_ARG, "x must be 4-byte aligned");
+  if (x_token_stride < (int64_t)s.Hkv * s.D || (x_token_stride & 1))
+    return fail(COMMVQ_ERR_INVALID_ARG, "x_token_stride %lld must be even and >= n_kv_heads*head_dim",
+                (long long)x_token_stride);
+  if (code_token_stride < 0 || code_head_stride < 0)
+    return fail(COMMVQ_ERR_INVALID_ARG, "negative code strides are not supported");
+  {
+    // Records (t, h) at t*ts + h*hs must be at least a record apart: either heads
+    // nest inside tokens (hs >= bpt, ts >= Hkv*hs) or tokens inside heads.
+    const int64_t ts = code_token_stride, hs = code_head_stride, n = n_tokens, H = s.Hkv, r = s.bpt;
+    const bool heads_inner = (H == 1 || hs >= r) && (n == 1 || ts >= H * (H == 1 ? r : hs));
+    const bool tokens_inner = (n == 1 || ts >= r) && (H == 1 || hs >= n * (n == 1 ? r : ts));
+    if (!heads_inner && !tokens_inner)
+      return fail(COMMVQ_ERR_INVALID_ARG, "code strides (token %lld, head %lld) make %d-byte records overlap",
+                  (long long)ts, (long long)hs, s.bpt);
+  }
+  commvq::EncodeArgs a{};
+  a.x = static_cast<const _Float16*>(x);
+  a.cb = static_cast<const _Float16*>(cb->entries);
+  a.codes = codes;
+  a.n_tokens = n_tokens;
+  a.x_token_stride = x_token_stride;
+  a.code_token_stride = code_token_stride;
+  a.code_head_stride = code_head_stride;
+  a.positions = nullptr;
+  a.cache_len = 0;
+  a.s = s;
+  return hip_status(commvq::launch_encode(a, static_cast<hipStream_t>(stream)), "commvq_encode launch");
+}
+
+int32_t commvq_append(const commvq_codebook* cb, const void* x, int32_t batch, const int32_t* positions,
+                      uint8_t* cache, int32_t cache_len, void* stream) {
+  g_err[0] = 0;
+  commvq::CbShape s;
+  int32_t st = check_shape(cb, "codebook", &s);
+  if (st) return st;
+  if (batch < 0) return fail(COMMVQ_ERR_INVALID_ARG, "batch %d < 0", batch);
+  if (batch == 0) return COMMVQ_OK;
+  st = check_entries(cb, "codebook");
+  if (st) return st;
+  if (!x || !positions || !cache) return fail(COMMVQ_ERR_INVALID_ARG, "null x, positions or cache pointer");
+  if (reinterpret_cast<uintptr_t>(x) & 3) return fail(COMMVQ_ERR_INVALID_ARG, "x must be 4-byte aligned");
+  if (cache_len < 1) return fail(COMMVQ_ERR_INVALID_ARG, "cache_len %d < 1", cache_len);
+  commvq::EncodeArgs a{};
+  a.x = static_cast<const _Float16*>(x);
+  a.cb = static_cast<const _Float16*>(cb->entries);
+  a.codes = cache;
+  a.n_tokens = batch;
+  a.x_token_stride = (int64_t)s.Hkv * s.D;
+  a.code_token_stride = (int64_t)s.Hkv * cache_len * s.bpt;
+  a.code_head_stride = (int64_t)cache_len * s.bpt;
+  a.positions = positions;
+  a.cache_len = cache_len;
+  a.s = s;
+  return hip_status(commvq::launch_encode(a, static_cast<hipStream_t>(stream)), "commvq_append launch");
+}
+
+int32_t commvq_decode_attention(const commvq_codebook* kcb, const commvq_codebook* vcb, const commvq_rope* rope,
+                                const float* q, const int32_t* q_pos, const uint8_t* kcodes,
+                                const uint8_t* vcodes, const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
+                                int32_t cache_len, int32_t max_seq_len, float sm_scale, float* out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  commvq::CbShape k, v;
+  int32_t st = decode_shapes(kcb, vcb, batch, n_q_heads, max_seq_len, &k, &v);
+  if (st) return st;
+  if (!rope) return fail(COMMVQ_ERR_INVALID_ARG, "null rope descriptor");
+  if (!(rope->theta_base > 1.0) || !std::isfinite(rope->theta_base))
+    return fail(COMMVQ_ERR_INVALID_ARG, "rope theta_base must be finite and > 1");
+  if (rope->pairing != 0 || rope->reserved != 0)
+    return fail(COMMVQ_ERR_UNSUPPORTED, "rope pairing %d: only interleaved pairs (0) are supported", rope->pairing);
+  if (cache_len < max_seq_len)
+    return fail(COMMVQ_ERR_INVALID_ARG, "max_seq_len %d exceeds cache_len %d", max_seq_len, cache_len);
+  if (!std::isfinite(sm_scale)) return fail(COMMVQ_ERR_INVALID_ARG, "sm_scale is not finite");
+  st = check_entries(kcb, "key codebook");
+  if (st) return st;
+  st = check_entries(vcb, "value codebook");
+  if (st) return st;
+  if (!q || !q_pos || !kcodes || !vcodes || !seq_lens || !out)
+    return fail(COMMVQ_ERR_INVALID_ARG, "null q, q_pos, codes, seq_lens or out pointer");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return fail(COMMVQ_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(kcodes) | reinterpret_cast<uintptr_t>(vcodes)) & 15)
+    return fail(COMMVQ_ERR_INVALID_ARG, "code caches must be 16-byte aligned");
+  const int64_t need = commvq_decode_workspace_bytes(batch, n_q_heads, max_seq_len, kcb, vcb);
+  if (need < 0) return (int32_t)need;
+  if (!workspace || workspace_bytes < (size_t)need)
+    return fail(COMMVQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %lld required", workspace_bytes,
+                (long long)need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(COMMVQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  commvq::DecodeArgs a{};
+  a.q = q;
+  a.q_pos = q_pos;
+  a.kcodes = kcodes;
+  a.vcodes = vcodes;
+  a.seq_lens = seq_lens;
+  a.kcb = static_cast<const _Float16*>(kcb->entries);
+  a.vcb = static_cast<const _Float16*>(vcb->entries);
+  a.part = static_cast<float*>(workspace);
+  a.out = out;
+  a.B = batch;
+  a.Hq = n_q_heads;
+  a.NH = n_q_heads / k.Hkv;
+  a.cache_len = cache_len;
+  a.max_len = max_seq_len;
+  a.chunk = commvq::decode_chunk_len(k, v, batch, n_q_heads, max_seq_len);
+  a.n_chunks = (max_seq_len + a.chunk - 1) / a.chunk;
+  a.sm_scale = sm_scale;
+  a.k = k;
+  a.v = v;
+  commvq::PhaseTable ph;
+  phase_table(rope->theta_base, k.D, &ph);
+  return hip_status(commvq::launch_decode(a, ph, static_cast<hipStream_t>(stream)),
+                    "commvq_decode_attention launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Internal interface between the C ABI (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace commvq {
+
+constexpr int kMaxPairs = 128;  // D <= 256
+
+// Validated shape of one codebook.
+struct CbShape {
+  int D, g, G, Nc, R, Hkv, bits, bpt;
+};
+
+struct EncodeArgs {
+  const _Float16* x;
+  const _Float16* cb;  // [Hkv][G][R][Nc][g]
+  uint8_t* codes;
+  int64_t n_tokens;
+  int64_t x_token_stride;     // elements
+  int64_t code_token_stride;  // bytes
+  int64_t code_head_stride;   // bytes
+  const int32_t* positions;   // append mode when non-null
+  int32_t cache_len;
+  CbShape s;
+};
+
+// Position phase: the RoPE angle m*theta_p is carried as a 64-bit fixed-point
+// fraction of a turn, F_p = theta_p / (2 pi) * 2^64, so (m * F_p) mod 2^64 is the
+// exact phase of position m to within 2^-64 turn per unit of m.
+struct PhaseTable {
+  uint32_t lo[kMaxPairs];
+  uint32_t hi[kMaxPairs];
+};
+
+struct DecodeArgs {
+  const float* q;
+  const int32_t* q_pos;
+  const uint8_t* kcodes;
+  const uint8_t* vcodes;
+  const int32_t* seq_lens;
+  const _Float16* kcb;
+  const _Float16* vcb;
+  float* part;  // [B][Hq][n_chunks][D + 2]: (max, sum, o[D])
+  float* out;   // [B][Hq][D]
+  int B, Hq, NH, cache_len, max_len, n_chunks, chunk;
+  float sm_scale;
+  CbShape k, v;
+};
+
+// Chunk length (tokens per workgroup) chosen for a decode shape; the workspace
+// query and the launch use the same rule.
+int decode_chunk_len(const CbShape& k, const CbShape& v, int B, int Hq, int max_len);
+bool decode_fast_path(const CbShape& k, const CbShape& v, int NH);
+
+hipError_t launch_encode(const EncodeArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream);
+
+}  // namespace commvq

@@ -1,0 +1,302 @@
+// CommVQ decode attention on packed codes (any supported shape).
+//
+// Per workgroup: one (sequence b, KV head h, context chunk). For the NH query
+// heads that read KV head h:
+//   1. rotate q to its position and, for each (group j, round r), build the
+//      query x codebook table T[a][l][p] = conj(q~_{a,p}) * z_{j,r,l,p} in LDS
+//      ("Pith review of CommVQ", "What carries the argument": the query- and
+//      codebook-dependent factors are computed once and reused for every
+//      cached position);
+//   2. every cached position m gathers T at its code and adds
+//      Re(T * e^{i m theta_p}) to the score - the RoPE rotation of the key is a
+//      phase because the codebook blocks commute with the rotation (paper Eq. 7);
+//   3. softmax over the chunk (max and sum reduced across the workgroup);
+//   4. the weights are scattered into per-code histograms (LDS integer atomics on
+//      fixed-point weights) and the histograms are multiplied by the value
+//      codebook (review, "If this is right", fourth bullet);
+//   5. the chunk's (max, sum, unnormalised output) go to the workspace and a
+//      combine kernel merges the chunks.
+// Positions' phases come from 64-bit fixed-point turn counts, exact for any
+// position below 2^31.
+
+#include "commvq_internal.hpp"
+
+namespace commvq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kGenericTPT = 4;  // tokens per lane in the generic kernel
+constexpr int kHistShift = 20;  // fixed-point weights: w * 2^20 (chunk <= 1024 keeps sums < 2^31)
+
+__device__ __forceinline__ float2 position_phase(uint32_t m, uint32_t flo, uint32_t fhi) {
+  // top 32 bits of (m * F) mod 2^64 = the phase in turns, as a signed fraction
+  const uint32_t turns = m * fhi + __umulhi(m, flo);
+  const float x = (float)(int32_t)turns * 0x1p-31f;  // angle / pi in [-1, 1)
+  float s, c;
+  sincospif(x, &s, &c);
+  return make_float2(c, s);
+}
+
+__device__ __forceinline__ int read_field(const uint8_t* rec, int f, int bits) {
+  const int o = f * bits, byte = o >> 3, sh = o & 7;
+  uint32_t v = rec[byte];
+  if (sh + bits > 8) v |= (uint32_t)rec[byte + 1] << 8;
+  return (int)((v >> sh) & ((1u << bits) - 1u));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <int NH, int GS>
+__global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, PhaseTable ph) {
+  constexpr int PP = GS / 2;
+  constexpr int TPT = kGenericTPT;
+  constexpr int NW = kThreads / 64;
+  extern __shared__ float4 dec_smem4[];
+  float* sm = reinterpret_cast<float*>(dec_smem4);
+  const CbShape K = a.k, V = a.v;
+  const int D = K.D, P = D / 2, G = K.G;
+  const int chunk_id = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int L = min(max(a.seq_lens[b], 0), a.max_len);
+  const int m0 = chunk_id * a.chunk;
+  const int hq0 = h * NH;
+  const size_t pstride = (size_t)a.n_chunks * (D + 2);
+  float* part = a.part + ((size_t)b * a.Hq + hq0) * pstride + (size_t)chunk_id * (D + 2);
+  if (m0 >= L) {
+    for (int i = tid; i < NH * (D + 2); i += kThreads) {
+      const int hh = i / (D + 2), k = i % (D + 2);
+      part[hh * pstride + k] = (k == 0) ? -INFINITY : 0.f;
+    }
+    return;
+  }
+  float2* qz = reinterpret_cast<float2*>(sm);  // [NH][P]
+  float* oacc = sm + 2 * NH * P;               // [NH][D]
+  float* red = oacc + NH * D;                  // [NH][NW]
+  float* uni = red + ((NH * (NW > 2 ? NW : 2) + 3) & ~3);  // table or histogram
+  float2* table = reinterpret_cast<float2*>(uni);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(uni);
+
+  const uint32_t qp = (uint32_t)max(a.q_pos[b], 0);
+  for (int i = tid; i < NH * P; i += kThreads) {
+    const int hh = i / P, p = i % P;
+    const float* qrow = a.q + ((size_t)b * a.Hq + hq0 + hh) * D;
+    const float x = qrow[2 * p], y = qrow[2 * p + 1];
+    const float2 w = position_phase(qp, ph.lo[p], ph.hi[p]);
+    qz[i] = make_float2(x * w.x - y * w.y, x * w.y + y * w.x);
+  }
+  for (int i = tid; i < NH * D; i += kThreads) oacc[i] = 0.f;
+
+  float s[TPT][NH];
+#pragma unroll
+  for (int t = 0; t < TPT; ++t)
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) s[t][hh] = 0.f;
+
+  const uint8_t* kbase = a.kcodes + ((size_t)b * K.Hkv + h) * (size_t)a.cache_len * K.bpt;
+  const uint8_t* vbase = a.vcodes + ((size_t)b * V.Hkv + h) * (size_t)a.cache_len * V.bpt;
+
+  for (int j = 0; j < G; ++j) {
+    for (int r = 0; r < K.R; ++r) {
+      __syncthreads();
+      const _Float16* cbp = a.kcb + ((((size_t)h * G + j) * K.R + r) * K.Nc) * GS;
+      for (int i = tid; i < NH * K.Nc * PP; i += kThreads) {
+        const int hh = i / (K.Nc * PP), rem = i % (K.Nc * PP), l = rem / PP, pp = rem % PP;
+        const float x = (float)cbp[l * GS + 2 * pp], y = (float)cbp[l * GS + 2 * pp + 1];
+        const float2 qv = qz[hh * P + j * PP + pp];
+        table[i] = make_float2(qv.x * x + qv.y * y, qv.x * y - qv.y * x);  // conj(q~) * z
+      }
+      __syncthreads();
+      const int f = r * G + j;
+#pragma unroll
+      for (int t = 0; t < TPT; ++t) {
+        const int m = m0 + tid + kThreads * t;
+        if (m < L) {
+          const int code = read_field(kbase + (size_t)m * K.bpt, f, K.bits);
+#pragma unroll
+          for (int pp = 0; pp < PP; ++pp) {
+            const int p = j * PP + pp;
+            const float2 w = position_phase((uint32_t)m, ph.lo[p], ph.hi[p]);
+#pragma unroll
+            for (int hh = 0; hh < NH; ++hh) {
+              const float2 T = table[(hh * K.Nc + code) * PP + pp];
+              s[t][hh] += T.x * w.x - T.y * w.y;
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // softmax over the chunk
+  float M[NH], lsum[NH];
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < TPT; ++t)
+      if (m0 + tid + kThreads * t < L) mx = fmaxf(mx, s[t][hh] * a.sm_scale);
+    mx = wave_max(mx);
+    if (lane == 0) red[hh * NW + wave] = mx;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    float mx = red[hh * NW];
+    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, red[hh * NW + w]);
+    M[hh] = mx;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < TPT; ++t) {
+      const bool ok = m0 + tid + kThreads * t < L;
+      const float pw = ok ? __expf(s[t][hh] * a.sm_scale - M[hh]) : 0.f;
+      s[t][hh] = pw;
+      acc += pw;
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) red[hh * NW + wave] = acc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    float acc = 0.f;
+    for (int w = 0; w < NW; ++w) acc += red[hh * NW + w];
+    lsum[hh] = acc;
+  }
+
+  // value histograms and contraction with the value codebook
+  for (int j = 0; j < G; ++j) {
+    for (int r = 0; r < V.R; ++r) {
+      __syncthreads();
+      for (int i = tid; i < NH * V.Nc; i += kThreads) hist[i] = 0u;
+      __syncthreads();
+      const int f = r * G + j;
+#pragma unroll
+      for (int t = 0; t < TPT; ++t) {
+        const int m = m0 + tid + kThreads * t;
+        if (m < L) {
+          const int code = read_field(vbase + (size_t)m * V.bpt, f, V.bits);
+#pragma unroll
+          for (int hh = 0; hh < NH; ++hh) {
+            const uint32_t fx = (uint32_t)fmaf(s[t][hh], (float)(1 << kHistShift), 0.5f);
+            atomicAdd(&hist[hh * V.Nc + code], fx);
+          }
+        }
+      }
+      __syncthreads();
+      const _Float16* cvp = a.vcb + ((((size_t)h * G + j) * V.R + r) * V.Nc) * GS;
+      for (int i = tid; i < NH * GS; i += kThreads) {
+        const int hh = i / GS, e = i % GS;
+        float acc = 0.f;
+        for (int l = 0; l < V.Nc; ++l) acc = fmaf((float)hist[hh * V.Nc + l], (float)cvp[l * GS + e], acc);
+        oacc[hh * D + j * GS + e] += acc * (1.0f / (float)(1 << kHistShift));
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      red[2 * hh] = M[hh];
+      red[2 * hh + 1] = lsum[hh];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < NH * (D + 2); i += kThreads) {
+    const int hh = i / (D + 2), k = i % (D + 2);
+    part[hh * pstride + k] = k < 2 ? red[2 * hh + k] : oacc[hh * D + k - 2];
+  }
+}
+
+// Merge the chunks of one (b, hq): o = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part, float* __restrict__ out,
+                                                      int n_chunks, int D) {
+  const int row = blockIdx.x;
+  const float* pr = part + (size_t)row * n_chunks * (D + 2);
+  float M = -INFINITY;
+  for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, pr[(size_t)c * (D + 2)]);
+  float lsum = 0.f;
+  if (M > -INFINITY)
+    for (int c = 0; c < n_chunks; ++c) {
+      const float mc = pr[(size_t)c * (D + 2)];
+      if (mc > -INFINITY) lsum += __expf(mc - M) * pr[(size_t)c * (D + 2) + 1];
+    }
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float acc = 0.f;
+    if (M > -INFINITY)
+      for (int c = 0; c < n_chunks; ++c) {
+        const float mc = pr[(size_t)c * (D + 2)];
+        if (mc > -INFINITY) acc = fmaf(__expf(mc - M), pr[(size_t)c * (D + 2) + 2 + d], acc);
+      }
+    out[(size_t)row * D + d] = lsum > 0.f ? acc / lsum : 0.f;
+  }
+}
+
+template <int NH, int GS>
+hipError_t launch_generic(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
+  const int P = a.k.D / 2;
+  const int NW = kThreads / 64;
+  size_t table_bytes = (size_t)NH * a.k.Nc * (GS / 2) * sizeof(float2);
+  size_t hist_bytes = (size_t)NH * a.v.Nc * sizeof(uint32_t);
+  size_t smem = (2 * NH * P + NH * a.k.D + ((NH * (NW > 2 ? NW : 2) + 3) & ~3)) * sizeof(float) +
+                (table_bytes > hist_bytes ? table_bytes : hist_bytes);
+  if (smem > 160 * 1024) return hipErrorInvalidValue;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_generic_kernel<NH, GS>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_generic_kernel<NH, GS>), dim3(a.n_chunks, a.k.Hkv, a.B), dim3(kThreads), smem, stream,
+                     a, ph);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.Hq), dim3(a.k.D < 256 ? a.k.D : 256), 0, stream, a.part, a.out,
+                     a.n_chunks, a.k.D);
+  return hipGetLastError();
+}
+
+template <int NH>
+hipError_t launch_generic_nh(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
+  switch (a.k.g) {
+    case 2: return launch_generic<NH, 2>(a, ph, stream);
+    case 4: return launch_generic<NH, 4>(a, ph, stream);
+    case 8: return launch_generic<NH, 8>(a, ph, stream);
+    case 16: return launch_generic<NH, 16>(a, ph, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int decode_chunk_len(const CbShape& k, const CbShape& v, int B, int Hq, int max_len) {
+  (void)k; (void)v; (void)B; (void)Hq; (void)max_len;
+  return kThreads * kGenericTPT;
+}
+
+bool decode_fast_path(const CbShape& k, const CbShape& v, int NH) {
+  (void)k; (void)v; (void)NH;
+  return false;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
+  switch (a.NH) {
+    case 1: return launch_generic_nh<1>(a, ph, stream);
+    case 2: return launch_generic_nh<2>(a, ph, stream);
+    case 4: return launch_generic_nh<4>(a, ph, stream);
+    case 8: return launch_generic_nh<8>(a, ph, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace commvq

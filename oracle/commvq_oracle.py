@@ -256,6 +256,8 @@ def decode_attention(q, q_pos, k_hat, v_hat, seq_lens, thetas, sm_scale):
     out = np.zeros((B, Hq, D), dtype=np.float64)
     for b in range(B):
         L = int(seq_lens[b])
+        if L <= 0:
+            continue  # nothing to attend: the row stays zero
         pos = np.arange(L)
         qr = apply_rope(q[b], np.full(Hq, int(q_pos[b])), thetas)  # one position per row
         for h in range(Hkv):
@@ -284,6 +286,8 @@ def decode_attention_from_packed(q, q_pos, kpacked, vpacked, seq_lens, kcb, vcb,
     out = np.zeros((B, Hq, D), dtype=np.float64)
     for b in range(B):
         L = int(seq_lens[b])
+        if L <= 0:
+            continue  # nothing to attend: the row stays zero
         pos = np.arange(L)
         qr = apply_rope(q[b], np.full(Hq, int(q_pos[b])), thetas)
         for h in range(Hkv):

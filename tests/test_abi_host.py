@@ -1,0 +1,131 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, answers size queries, and rejects bad arguments with the
+documented status before any GPU call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_attention_commvq_amd import _lib
+from oracle import commvq_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "commvq.h")
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(commvq_\w+)\s*\(", text, flags=re.M)))
+
+
+def cb(D=128, g=8, Nc=256, R=2, H=8, entries=FAKE):
+    return _lib.make_codebook(entries, D, g, Nc, R, H)
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED), names
+    L = _lib.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert _lib.commvq_abi_version() == 1
+
+
+def test_size_queries_match_the_oracle():
+    for (D, g, Nc, R) in [(128, 8, 256, 2), (128, 8, 256, 1), (64, 16, 64, 2), (48, 6, 2, 3), (128, 4, 8, 3)]:
+        c = cb(D, g, Nc, R)
+        assert _lib.commvq_validate_codebook(c) == 0
+        assert _lib.commvq_bits_per_scalar(c) == O.bits_per_scalar(g, Nc, R)
+        assert _lib.commvq_code_bytes_per_token(c) == O.code_bytes_per_token(D, g, Nc, R)
+
+
+def test_workspace_query():
+    k = cb()
+    n = _lib.commvq_decode_workspace_bytes(1, 32, 131072, k, k)
+    assert n > 0 and n % 4 == 0
+    assert _lib.commvq_decode_workspace_bytes(1, 32, 1, k, k) > 0
+    assert _lib.commvq_decode_workspace_bytes(1, 30, 1000, k, k) == _lib.COMMVQ_ERR_INVALID_ARG
+    assert _lib.commvq_decode_workspace_bytes(1, 24, 1000, k, k) == _lib.COMMVQ_ERR_UNSUPPORTED  # 3 q per kv
+    assert _lib.commvq_decode_workspace_bytes(0, 32, 1000, k, k) == _lib.COMMVQ_ERR_INVALID_ARG
+    assert _lib.commvq_decode_workspace_bytes(1, 32, 0, k, k) == _lib.COMMVQ_ERR_INVALID_ARG
+    assert _lib.commvq_decode_workspace_bytes(1, 32, 1000, k, cb(D=64)) == _lib.COMMVQ_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", [
+    dict(D=127), dict(D=0), dict(D=512), dict(g=7), dict(g=0), dict(g=18), dict(D=128, g=12),
+    dict(Nc=100), dict(Nc=1), dict(Nc=512), dict(R=0), dict(R=5), dict(H=0),
+])
+def test_invalid_descriptors(bad):
+    c = cb(**bad)
+    assert _lib.commvq_validate_codebook(c) == _lib.COMMVQ_ERR_INVALID_ARG
+    assert _lib.commvq_last_error() != ""
+    assert _lib.commvq_bits_per_scalar(c) < 0
+    assert _lib.commvq_code_bytes_per_token(c) == _lib.COMMVQ_ERR_INVALID_ARG
+
+
+def test_null_descriptor():
+    L = _lib.lib()
+    assert L.commvq_validate_codebook(None) == _lib.COMMVQ_ERR_INVALID_ARG
+    assert "null" in _lib.commvq_last_error()
+
+
+def _raw_encode(c, x, n, xs, codes, ts, hs):
+    return _lib.lib().commvq_encode(ctypes.byref(c), x, n, xs, codes, ts, hs, None)
+
+
+def test_encode_validation_without_launch():
+    c = cb(H=2)
+    bpt = 32
+    assert _raw_encode(c, FAKE, 0, 256, FAKE, 64, 32) == 0          # nothing to do
+    assert _raw_encode(c, None, 4, 256, FAKE, 64, 32) == _lib.COMMVQ_ERR_INVALID_ARG
+    assert _raw_encode(c, FAKE, 4, 256, None, 64, 32) == _lib.COMMVQ_ERR_INVALID_ARG
+    assert _raw_encode(c, FAKE, -1, 256, FAKE, 64, 32) == _lib.COMMVQ_ERR_INVALID_ARG
+    assert _raw_encode(c, FAKE, 4, 255, FAKE, 64, 32) == _lib.COMMVQ_ERR_INVALID_ARG   # stride < H*D
+    assert _raw_encode(c, FAKE + 2, 4, 256, FAKE, 64, 32) == _lib.COMMVQ_ERR_INVALID_ARG  # misaligned x
+    assert _raw_encode(c, FAKE, 4, 256, FAKE, bpt, bpt) == _lib.COMMVQ_ERR_INVALID_ARG   # records overlap
+    assert _raw_encode(c, FAKE, 4, 256, FAKE, -64, 32) == _lib.COMMVQ_ERR_INVALID_ARG
+    assert _raw_encode(cb(H=2, entries=None), FAKE, 4, 256, FAKE, 64, 32) == _lib.COMMVQ_ERR_INVALID_ARG
+    assert _raw_encode(cb(H=2, entries=FAKE + 8), FAKE, 4, 256, FAKE, 64, 32) == _lib.COMMVQ_ERR_INVALID_ARG
+
+
+def test_append_validation_without_launch():
+    c = cb()
+    L = _lib.lib()
+    assert L.commvq_append(ctypes.byref(c), FAKE, 0, FAKE, FAKE, 16, None) == 0
+    assert L.commvq_append(ctypes.byref(c), FAKE, -1, FAKE, FAKE, 16, None) == _lib.COMMVQ_ERR_INVALID_ARG
+    assert L.commvq_append(ctypes.byref(c), FAKE, 2, None, FAKE, 16, None) == _lib.COMMVQ_ERR_INVALID_ARG
+    assert L.commvq_append(ctypes.byref(c), FAKE, 2, FAKE, FAKE, 0, None) == _lib.COMMVQ_ERR_INVALID_ARG
+
+
+def _raw_decode(k, v, rope, B=1, Hq=32, cache_len=1024, max_len=1024, scale=0.088, ws=FAKE, ws_bytes=1 << 30,
+                q=FAKE, out=FAKE, codes=FAKE):
+    L = _lib.lib()
+    return L.commvq_decode_attention(ctypes.byref(k), ctypes.byref(v), ctypes.byref(rope) if rope else None,
+                                     q, FAKE, codes, codes, FAKE, B, Hq, cache_len, max_len, scale, out, ws,
+                                     ws_bytes, None)
+
+
+def test_decode_validation_without_launch():
+    k, rope = cb(), _lib.make_rope(500000.0)
+    E = _lib
+    assert _raw_decode(k, k, None) == E.COMMVQ_ERR_INVALID_ARG
+    assert _raw_decode(k, k, _lib.make_rope(1.0)) == E.COMMVQ_ERR_INVALID_ARG
+    assert _raw_decode(k, k, _lib.make_rope(float("nan"))) == E.COMMVQ_ERR_INVALID_ARG
+    assert _raw_decode(k, k, _lib.make_rope(500000.0, pairing=1)) == E.COMMVQ_ERR_UNSUPPORTED
+    assert _raw_decode(k, k, rope, Hq=31) == E.COMMVQ_ERR_INVALID_ARG
+    assert _raw_decode(k, k, rope, Hq=24) == E.COMMVQ_ERR_UNSUPPORTED
+    assert _raw_decode(k, k, rope, max_len=2048) == E.COMMVQ_ERR_INVALID_ARG  # beyond the cache
+    assert _raw_decode(k, k, rope, B=0) == E.COMMVQ_ERR_INVALID_ARG
+    assert _raw_decode(k, k, rope, scale=float("inf")) == E.COMMVQ_ERR_INVALID_ARG
+    assert _raw_decode(k, k, rope, ws_bytes=16) == E.COMMVQ_ERR_WORKSPACE
+    assert _raw_decode(k, k, rope, ws=None) == E.COMMVQ_ERR_WORKSPACE
+    assert _raw_decode(k, k, rope, ws=FAKE + 64) == E.COMMVQ_ERR_WORKSPACE  # 256-byte alignment
+    assert _raw_decode(k, k, rope, q=FAKE + 4) == E.COMMVQ_ERR_INVALID_ARG
+    assert _raw_decode(k, k, rope, codes=FAKE + 1) == E.COMMVQ_ERR_INVALID_ARG
+    assert _raw_decode(k, k, rope, out=None) == E.COMMVQ_ERR_INVALID_ARG
+    assert _raw_decode(k, cb(D=64), rope) == E.COMMVQ_ERR_INVALID_ARG
+    assert _raw_decode(cb(g=6, D=96), cb(g=6, D=96), rope) == E.COMMVQ_ERR_UNSUPPORTED
+    assert "workspace" in (_raw_decode(k, k, rope, ws_bytes=16) and _lib.commvq_last_error())

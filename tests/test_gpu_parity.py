@@ -1,0 +1,228 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on the
+same seeded inputs. Encoded bytes must match exactly (near-ties excepted and
+logged); attention outputs must match within 2e-3 of each row's max |ref|."""
+
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_attention_commvq_amd import api, synth
+from long_context_attention_commvq_amd import _lib
+from oracle import commvq_oracle as O
+from tests.parity import ATTN_TOL, check_encoding, row_errors
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def gpu_encode(x, cb, n_entries):
+    g = cb.shape[-1]
+    q = api.Quantizer(dev(cb), g)
+    out = api.encode(q, dev(x))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _report(name, hard, ties, n_fields):
+    print(f"[{name}] near-ties accepted: {len(ties)} of {n_fields} fields; hard mismatches: {len(hard)}", flush=True)
+    for t in ties[:10]:
+        print(f"  near-tie (token, head, round, group, rel_gap) = {t}", flush=True)
+
+
+# ---------------------------------------------------------------- encoder
+
+def test_encode_tiny_workload():
+    w = synth.WORKLOADS["tiny_gqa4_ctx2k_2bit"]
+    x = synth.kv(w.seed + 10, w.context, w.n_kv_heads, w.head_dim)
+    cb = synth.codebook(w.seed + 1, w.n_kv_heads, w.head_dim, w.group_size, w.n_entries, w.n_rounds)
+    got = gpu_encode(x, cb, w.n_entries)
+    hard, ties = check_encoding(x, cb, got, w.n_entries)
+    _report("encode tiny", hard, ties, x.shape[0] * w.n_rounds * 16)
+    assert not hard, hard[:5]
+
+
+@pytest.mark.parametrize("D,g,Nc,R,H,N", [
+    (128, 8, 256, 1, 2, 300),
+    (128, 8, 256, 3, 1, 257),
+    (64, 2, 16, 2, 2, 129),
+    (64, 4, 4, 4, 1, 65),
+    (64, 16, 64, 2, 3, 37),    # 6-bit fields straddle bytes
+    (48, 6, 2, 3, 1, 1),       # 1-bit fields, 8 groups of 6, single token
+    (256, 16, 128, 2, 1, 33),
+    (128, 4, 8, 3, 2, 100),    # 3-bit fields
+])
+def test_encode_shapes(D, g, Nc, R, H, N):
+    seed = D * 7 + g * 11 + Nc + R
+    x = synth.kv(seed, N, H, D)
+    cb = synth.codebook(seed + 1, H, D, g, Nc, R)
+    got = gpu_encode(x, cb, Nc)
+    hard, ties = check_encoding(x, cb, got, Nc)
+    _report(f"encode D{D} g{g} Nc{Nc} R{R}", hard, ties, N * H * R * (D // g))
+    assert not hard, hard[:5]
+
+
+def test_encode_into_cache_strides_and_append():
+    H, D, g, Nc, R, B, Lmax = 2, 64, 8, 256, 2, 3, 40
+    cb = synth.codebook(71, H, D, g, Nc, R)
+    q = api.Quantizer(dev(cb), g)
+    bpt = q.bytes_per_token
+    cache = torch.full((B, H, Lmax, bpt), 0xAB, dtype=torch.uint8, device=DEV)
+    x = synth.kv(72, 11, H, D)
+    api.encode_into_cache(q, dev(x), cache, 1, 5)
+    # append one token per sequence; sequence 2 gets an out-of-range position (skipped)
+    xa = synth.kv(73, B, H, D)
+    pos = torch.tensor([0, 20, Lmax], dtype=torch.int32, device=DEV)
+    api.append(q, dev(xa), pos, cache)
+    torch.cuda.synchronize()
+    c = cache.cpu().numpy()
+    ref_codes, _ = O.encode(x, cb)
+    ref = O.pack_codes(ref_codes, Nc)  # [11, H, bpt]
+    hard, _ = check_encoding(x, cb, np.transpose(c[1, :, 5:16], (1, 0, 2)), Nc)
+    assert not hard
+    hard, _ = check_encoding(xa[:2], cb, np.stack([c[0, :, 0], c[1, :, 20]]), Nc)
+    assert not hard
+    # untouched bytes stay untouched
+    mask = np.ones(c.shape, dtype=bool)
+    mask[1, :, 5:16] = False
+    mask[0, :, 0] = False
+    mask[1, :, 20] = False
+    assert np.all(c[mask] == 0xAB)
+    assert ref.shape == (11, H, bpt)
+
+
+def test_encode_error_paths_on_device():
+    cb = synth.codebook(5, 1, 64, 8, 256, 1)
+    q = api.Quantizer(dev(cb), 8)
+    x = dev(synth.kv(6, 4, 1, 64))
+    out = torch.empty((4, 1, 8), dtype=torch.uint8, device=DEV)
+    with pytest.raises(_lib.CommvqError):
+        _lib.commvq_encode(q.desc, x, 4, 63, out, 8, 8)  # odd token stride
+    with pytest.raises(_lib.CommvqError):
+        _lib.commvq_encode(q.desc, x, 4, 64, out, 4, 8)  # overlapping records
+
+
+# ---------------------------------------------------------------- decode
+
+def _pack_cache(codes, n_entries):
+    """codes [B, L, Hkv, R, G] -> packed [B, Hkv, L, bpt] via the oracle's packer."""
+    return np.ascontiguousarray(np.stack([O.pack_codes(codes[b], n_entries) for b in range(codes.shape[0])])
+                                .transpose(0, 2, 1, 3))
+
+
+def run_decode_case(seed, B, Hq, Hkv, D, g, Nc, R, lens, Lmax, Ncv=None, Rv=None, q_scale=1.0,
+                    q_pos=None, theta=500000.0, max_len=None, sm_scale=None):
+    Ncv = Nc if Ncv is None else Ncv
+    Rv = R if Rv is None else Rv
+    G = D // g
+    rng = np.random.default_rng(seed)
+    kcb = synth.codebook(seed + 1, Hkv, D, g, Nc, R)
+    vcb = synth.codebook(seed + 2, Hkv, D, g, Ncv, Rv)
+    kc = rng.integers(0, Nc, size=(B, Lmax, Hkv, R, G))
+    vc = rng.integers(0, Ncv, size=(B, Lmax, Hkv, Rv, G))
+    kp, vp = _pack_cache(kc, Nc), _pack_cache(vc, Ncv)
+    q = synth.queries(seed + 3, B, Hq, D) * np.float32(q_scale)
+    lens = np.asarray(lens, dtype=np.int32)
+    qpos = (np.maximum(lens, 1) - 1) if q_pos is None else np.asarray(q_pos, dtype=np.int32)
+    max_len = int(lens.max()) if max_len is None else max_len
+    scale = 1.0 / math.sqrt(D) if sm_scale is None else sm_scale
+    ref = O.decode_attention_from_packed(q, qpos, kp, vp, np.minimum(lens, max_len), kcb, vcb, theta, scale)
+    kq, vq = api.Quantizer(dev(kcb), g), api.Quantizer(dev(vcb), g)
+    out = api.decode_attention(kq, vq, dev(q), dev(qpos), dev(kp), dev(vp), dev(lens), max_len, theta, scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    err = row_errors(got.reshape(-1, D), ref.reshape(-1, D))
+    return got, ref, err
+
+
+def test_decode_tiny_workload_end_to_end():
+    """Tiny workload: oracle-encoded K/V, one decode step at L = 2048."""
+    w = synth.WORKLOADS["tiny_gqa4_ctx2k_2bit"]
+    L, H, D = w.context, w.n_kv_heads, w.head_dim
+    k = synth.kv(w.seed + 10, L, H, D)
+    v = synth.kv(w.seed + 11, L, H, D)
+    kcb = synth.codebook(w.seed + 1, H, D, w.group_size, w.n_entries, w.n_rounds)
+    vcb = synth.codebook(w.seed + 2, H, D, w.group_size, w.n_entries, w.n_rounds)
+    kcodes, _ = O.encode(k, kcb)
+    vcodes, _ = O.encode(v, vcb)
+    kp = np.ascontiguousarray(O.pack_codes(kcodes, w.n_entries).transpose(1, 0, 2)[None])
+    vp = np.ascontiguousarray(O.pack_codes(vcodes, w.n_entries).transpose(1, 0, 2)[None])
+    q = synth.queries(w.seed + 12, 1, w.n_q_heads, D)
+    lens = np.array([L], dtype=np.int32)
+    ref = O.decode_attention_from_packed(q, lens - 1, kp, vp, lens, kcb, vcb, w.theta_base)
+    kq, vq = api.Quantizer(dev(kcb), w.group_size), api.Quantizer(dev(vcb), w.group_size)
+    out = api.decode_attention(kq, vq, dev(q), dev(lens - 1), dev(kp), dev(vp), dev(lens), L, w.theta_base)
+    torch.cuda.synchronize()
+    err = row_errors(out.cpu().numpy()[0], ref[0])
+    print(f"[decode tiny] max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= ATTN_TOL
+    # and the whole GPU pipeline: GPU encode feeding GPU decode
+    kg = api.encode(kq, dev(k)).permute(1, 0, 2).contiguous()[None]
+    vg = api.encode(vq, dev(v)).permute(1, 0, 2).contiguous()[None]
+    out2 = api.decode_attention(kq, vq, dev(q), dev(lens - 1), kg, vg, dev(lens), L, w.theta_base)
+    torch.cuda.synchronize()
+    assert row_errors(out2.cpu().numpy()[0], ref[0]).max() <= ATTN_TOL
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=1, Hq=4, Hkv=1, D=128, g=8, Nc=256, R=2, lens=[2048], Lmax=2048),
+    dict(B=2, Hq=8, Hkv=2, D=128, g=8, Nc=256, R=1, lens=[1500, 3001], Lmax=3100),
+    dict(B=3, Hq=4, Hkv=4, D=64, g=4, Nc=16, R=3, lens=[1, 700, 1025], Lmax=1100),
+    dict(B=1, Hq=16, Hkv=2, D=64, g=16, Nc=256, R=2, lens=[999], Lmax=1024),
+    dict(B=2, Hq=2, Hkv=1, D=64, g=2, Nc=16, R=1, lens=[33, 64], Lmax=64),
+    dict(B=2, Hq=8, Hkv=4, D=128, g=8, Nc=256, R=2, Ncv=16, Rv=3, lens=[1024, 2047], Lmax=2048),
+    dict(B=1, Hq=4, Hkv=1, D=256, g=16, Nc=256, R=1, lens=[1800], Lmax=1800),
+])
+def test_decode_shapes(case):
+    got, ref, err = run_decode_case(seed=zlib.crc32(repr(sorted(case.items())).encode()) % 10000, **case)
+    print(f"[decode {case}] max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= ATTN_TOL
+
+
+@pytest.mark.parametrize("q_scale", [8.0, 30.0])
+def test_decode_peaked_queries(q_scale):
+    got, ref, err = run_decode_case(77, B=2, Hq=8, Hkv=2, D=128, g=8, Nc=256, R=2, lens=[4000, 2500], Lmax=4096,
+                                    q_scale=q_scale)
+    print(f"[decode peaked x{q_scale}] max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= ATTN_TOL
+
+
+def test_decode_edge_cases():
+    # length 1, a length that ends exactly on a chunk boundary, a zero length
+    got, ref, err = run_decode_case(91, B=4, Hq=4, Hkv=1, D=128, g=8, Nc=256, R=2, lens=[1, 1024, 2048, 0],
+                                    Lmax=2048, max_len=2048)
+    assert np.all(got[3] == 0.0)
+    assert err.max() <= ATTN_TOL
+    # query position unrelated to the length; large positions (phase exactness)
+    got, ref, err = run_decode_case(92, B=2, Hq=4, Hkv=1, D=128, g=8, Nc=256, R=1, lens=[300, 1000], Lmax=1024,
+                                    q_pos=[2_000_000_000, 131071])
+    assert err.max() <= ATTN_TOL
+    # lengths beyond max_seq_len are clamped to it
+    got, ref, err = run_decode_case(93, B=2, Hq=4, Hkv=1, D=64, g=8, Nc=256, R=1, lens=[500, 900], Lmax=1024,
+                                    max_len=600, q_pos=[499, 899])
+    assert err.max() <= ATTN_TOL
+
+
+def test_decode_rejects_bad_arguments():
+    cb = synth.codebook(1, 1, 64, 8, 256, 1)
+    kq = api.Quantizer(dev(cb), 8)
+    q = torch.zeros((1, 4, 64), dtype=torch.float32, device=DEV)
+    pos = torch.zeros(1, dtype=torch.int32, device=DEV)
+    cache = torch.zeros((1, 1, 16, 8), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(q)
+    ws = api.DecodeWorkspace(kq, kq, 1, 4, 16, DEV)
+    rope = _lib.make_rope(500000.0)
+    with pytest.raises(_lib.CommvqError) as e:
+        _lib.commvq_decode_attention(kq.desc, kq.desc, rope, q, pos, cache, cache, pos, 1, 4, 16, 16, 0.1, out,
+                                     ws.buf, ws.nbytes - 4)
+    assert e.value.status == _lib.COMMVQ_ERR_WORKSPACE
+    with pytest.raises(_lib.CommvqError) as e:
+        _lib.commvq_decode_attention(kq.desc, kq.desc, rope, q, pos, cache, cache, pos, 1, 3, 16, 16, 0.1, out,
+                                     ws.buf, ws.nbytes)
+    assert e.value.status == _lib.COMMVQ_ERR_UNSUPPORTED  # three query heads per KV head
