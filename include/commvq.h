@@ -51,6 +51,15 @@ typedef enum commvq_status {
 
 typedef enum commvq_dtype { COMMVQ_F16 = 1 } commvq_dtype;
 
+/* commvq_decode_attention flags. By default shapes with head_dim 128, g = 8,
+ * Nc' = 256, R = 1 or 2 and four query heads per KV head run a kernel that keeps
+ * the query x codebook table and the position phases in fp16 (products summed in
+ * fp32): its score error is about 4e-4 of |q||k|/sqrt(D), which keeps outputs
+ * within 1e-4 of an fp64 reference for unit-variance queries but grows with the
+ * spread of the scores. COMMVQ_DECODE_EXACT keeps the table in fp32 and every
+ * phase exact (slower), for strongly peaked attention. */
+#define COMMVQ_DECODE_EXACT 1u
+
 /* One codebook (keys or values) for all KV heads of one layer.
  * Pages: "What carries the argument" (codebook per subspace, group size g,
  * R rounds, Nc' entries). */
@@ -93,8 +102,9 @@ double commvq_bits_per_scalar(const commvq_codebook* cb);
  * negative commvq_status if the descriptor is invalid. */
 int64_t commvq_code_bytes_per_token(const commvq_codebook* cb);
 
-/* Workspace bytes that commvq_decode_attention needs for this shape (split-
- * context partials); negative commvq_status on invalid arguments. */
+/* Workspace bytes that commvq_decode_attention needs for this shape (arrival
+ * counters and split-context partials, enough for every flags value); negative
+ * commvq_status on invalid arguments. */
 int64_t commvq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
                                       const commvq_codebook* kcb, const commvq_codebook* vcb);
 
@@ -134,7 +144,10 @@ int32_t commvq_append(const commvq_codebook* cb, const void* x, int32_t batch,
  *   sm_scale multiplies q.k (normally 1/sqrt(D)).
  *   out      device fp32 [batch][n_q_heads][D]
  *   workspace device, >= commvq_decode_workspace_bytes(batch, n_q_heads,
- *            max_seq_len, kcb, vcb) bytes, 256-byte aligned.
+ *            max_seq_len, kcb, vcb) bytes, 256-byte aligned, zero-filled
+ *            before its first use; every call leaves it ready for the next.
+ *            Calls sharing one workspace must not overlap in time.
+ *   flags    0 or COMMVQ_DECODE_EXACT.
  * Pages: "What carries the argument" (query-codebook factors computed once and
  * reused over cached positions); "If this is right", fourth bullet (weights
  * applied to value codes before the codebook). */
@@ -144,7 +157,7 @@ int32_t commvq_decode_attention(const commvq_codebook* kcb, const commvq_codeboo
                                 const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
                                 int32_t cache_len, int32_t max_seq_len, float sm_scale,
                                 float* out, void* workspace, size_t workspace_bytes,
-                                void* stream);
+                                uint32_t flags, void* stream);
 
 #ifdef __cplusplus
 }

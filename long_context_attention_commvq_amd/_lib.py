@@ -21,6 +21,7 @@ COMMVQ_ERR_UNSUPPORTED = -2
 COMMVQ_ERR_WORKSPACE = -3
 COMMVQ_ERR_HIP = -4
 COMMVQ_F16 = 1
+COMMVQ_DECODE_EXACT = 1
 
 STATUS_NAMES = {
     COMMVQ_OK: "COMMVQ_OK",
@@ -83,7 +84,7 @@ def lib():
         L.commvq_decode_attention.restype = c_int32
         L.commvq_decode_attention.argtypes = [CB, CB, POINTER(commvq_rope), c_void_p, c_void_p, c_void_p,
                                               c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
-                                              c_float, c_void_p, c_void_p, c_size_t, c_void_p]
+                                              c_float, c_void_p, c_void_p, c_size_t, ctypes.c_uint32, c_void_p]
         _lib = L
     return _lib
 
@@ -164,8 +165,9 @@ def commvq_append(cb: commvq_codebook, x, batch: int, positions, cache, cache_le
 
 def commvq_decode_attention(kcb: commvq_codebook, vcb: commvq_codebook, rope: commvq_rope, q, q_pos, kcodes,
                             vcodes, seq_lens, batch: int, n_q_heads: int, cache_len: int, max_seq_len: int,
-                            sm_scale: float, out, workspace, workspace_bytes: int, stream=None) -> int:
+                            sm_scale: float, out, workspace, workspace_bytes: int, flags: int = 0,
+                            stream=None) -> int:
     return _check(lib().commvq_decode_attention(
         ctypes.byref(kcb), ctypes.byref(vcb), ctypes.byref(rope), _ptr(q), _ptr(q_pos), _ptr(kcodes),
         _ptr(vcodes), _ptr(seq_lens), batch, n_q_heads, cache_len, max_seq_len, float(sm_scale), _ptr(out),
-        _ptr(workspace), int(workspace_bytes), _stream(stream, q, out)))
+        _ptr(workspace), int(workspace_bytes), int(flags), _stream(stream, q, out)))

@@ -70,13 +70,14 @@ class DecodeWorkspace:
         if n < 0:
             raise _lib.CommvqError(int(n), _lib.commvq_last_error())
         self.nbytes = int(n)
-        self.buf = torch.empty(max(self.nbytes, 256), dtype=torch.uint8, device=device)
+        # zero-filled once: the arrival counters at its start must read zero on first use
+        self.buf = torch.zeros(max(self.nbytes, 256), dtype=torch.uint8, device=device)
 
 
 def decode_attention(kq: Quantizer, vq: Quantizer, q: torch.Tensor, q_pos: torch.Tensor, kcache: torch.Tensor,
                      vcache: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, theta_base: float,
                      sm_scale: float | None = None, out: torch.Tensor | None = None,
-                     workspace: DecodeWorkspace | None = None) -> torch.Tensor:
+                     workspace: DecodeWorkspace | None = None, exact: bool = False) -> torch.Tensor:
     """q fp32 [B, Hq, D] -> out fp32 [B, Hq, D] over packed caches [B, Hkv, Lmax, bpt]."""
     B, Hq, D = q.shape
     if sm_scale is None:
@@ -87,5 +88,6 @@ def decode_attention(kq: Quantizer, vq: Quantizer, q: torch.Tensor, q_pos: torch
         workspace = DecodeWorkspace(kq, vq, B, Hq, max_seq_len, q.device)
     rope = _lib.make_rope(theta_base)
     _lib.commvq_decode_attention(kq.desc, vq.desc, rope, q, q_pos, kcache, vcache, seq_lens, B, Hq,
-                                 kcache.shape[2], max_seq_len, sm_scale, out, workspace.buf, workspace.nbytes)
+                                 kcache.shape[2], max_seq_len, sm_scale, out, workspace.buf, workspace.nbytes,
+                                 _lib.COMMVQ_DECODE_EXACT if exact else 0)
     return out

@@ -8,7 +8,7 @@
 #include <cstring>
 
 #include "../../include/commvq.h"
-#include "commvq_internal.hpp"
+#include "decode_common.hpp"
 
 namespace {
 
@@ -91,6 +91,15 @@ int32_t decode_shapes(const commvq_codebook* kcb, const commvq_codebook* vcb, in
   return COMMVQ_OK;
 }
 
+void fast_phase(double base, int D, commvq::FastPhase* fp) {
+  // e^{i 512 theta_p} per pair (a fast-kernel lane steps 512 positions)
+  for (int p = 0; p < D / 2 && p < commvq::kMaxPairs / 2; ++p) {
+    const long double theta = powl((long double)base, -2.0L * p / D);
+    fp->step_c[p] = (float)cosl(512.0L * theta);
+    fp->step_s[p] = (float)sinl(512.0L * theta);
+  }
+}
+
 void phase_table(double base, int D, commvq::PhaseTable* ph) {
   // F_p = frac(theta_p / 2pi) * 2^64 with theta_p = base^(-2p/D), in long double.
   const long double two_pi = 6.283185307179586476925286766559L;
@@ -140,9 +149,8 @@ int64_t commvq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t 
   commvq::CbShape k, v;
   int32_t st = decode_shapes(kcb, vcb, batch, n_q_heads, max_seq_len, &k, &v);
   if (st) return st;
-  const int chunk = commvq::decode_chunk_len(k, v, batch, n_q_heads, max_seq_len);
-  const int64_t n_chunks = (max_seq_len + chunk - 1) / chunk;
-  return (int64_t)batch * n_q_heads * n_chunks * (k.D + 2) * (int64_t)sizeof(float);
+  // the smallest chunk any path uses bounds the partials
+  return (int64_t)commvq::decode_workspace_bytes(k, batch, n_q_heads, max_seq_len, 1024);
 }
 
 int32_t commvq_encode(const commvq_codebook* cb, const void* x, int64_t n_tokens, int64_t x_token_stride,
@@ -217,7 +225,7 @@ int32_t commvq_decode_attention(const commvq_codebook* kcb, const commvq_codeboo
                                 const float* q, const int32_t* q_pos, const uint8_t* kcodes,
                                 const uint8_t* vcodes, const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
                                 int32_t cache_len, int32_t max_seq_len, float sm_scale, float* out,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+                                void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
   g_err[0] = 0;
   commvq::CbShape k, v;
   int32_t st = decode_shapes(kcb, vcb, batch, n_q_heads, max_seq_len, &k, &v);
@@ -230,6 +238,7 @@ int32_t commvq_decode_attention(const commvq_codebook* kcb, const commvq_codeboo
   if (cache_len < max_seq_len)
     return fail(COMMVQ_ERR_INVALID_ARG, "max_seq_len %d exceeds cache_len %d", max_seq_len, cache_len);
   if (!std::isfinite(sm_scale)) return fail(COMMVQ_ERR_INVALID_ARG, "sm_scale is not finite");
+  if (flags & ~(uint32_t)COMMVQ_DECODE_EXACT) return fail(COMMVQ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   st = check_entries(kcb, "key codebook");
   if (st) return st;
   st = check_entries(vcb, "value codebook");
@@ -255,22 +264,30 @@ int32_t commvq_decode_attention(const commvq_codebook* kcb, const commvq_codeboo
   a.seq_lens = seq_lens;
   a.kcb = static_cast<const _Float16*>(kcb->entries);
   a.vcb = static_cast<const _Float16*>(vcb->entries);
-  a.part = static_cast<float*>(workspace);
+  a.counters = static_cast<uint32_t*>(workspace);
+  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + commvq::counter_bytes(batch, k.Hkv));
   a.out = out;
   a.B = batch;
   a.Hq = n_q_heads;
   a.NH = n_q_heads / k.Hkv;
   a.cache_len = cache_len;
   a.max_len = max_seq_len;
-  a.chunk = commvq::decode_chunk_len(k, v, batch, n_q_heads, max_seq_len);
+  a.chunk = commvq::decode_chunk_len(k, v, batch, n_q_heads, max_seq_len, (int)flags);
   a.n_chunks = (max_seq_len + a.chunk - 1) / a.chunk;
   a.sm_scale = sm_scale;
   a.k = k;
   a.v = v;
   commvq::PhaseTable ph;
   phase_table(rope->theta_base, k.D, &ph);
-  return hip_status(commvq::launch_decode(a, ph, static_cast<hipStream_t>(stream)),
-                    "commvq_decode_attention launch");
+  hipError_t e;
+  if (commvq::decode_fast_path(k, v, a.NH, (int)flags)) {
+    commvq::FastPhase fp;
+    fast_phase(rope->theta_base, k.D, &fp);
+    e = commvq::launch_decode_fast(a, ph, fp, static_cast<hipStream_t>(stream));
+  } else {
+    e = commvq::launch_decode_generic(a, ph, static_cast<hipStream_t>(stream));
+  }
+  return hip_status(e, "commvq_decode_attention launch");
 }
 
 }  // extern "C"

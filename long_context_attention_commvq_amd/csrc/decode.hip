@@ -14,12 +14,14 @@
 //   4. the weights are scattered into per-code histograms (LDS integer atomics on
 //      fixed-point weights) and the histograms are multiplied by the value
 //      codebook (review, "If this is right", fourth bullet);
-//   5. the chunk's (max, sum, unnormalised output) go to the workspace and a
-//      combine kernel merges the chunks.
+//   5. the chunk's (max, sum, unnormalised output) go to the workspace and the
+//      last workgroup to finish for (b, h) merges the chunks.
+// This kernel keeps the table in fp32 and computes every phase exactly; it serves
+// every supported shape and the exact-precision mode.
 // Positions' phases come from 64-bit fixed-point turn counts, exact for any
 // position below 2^31.
 
-#include "commvq_internal.hpp"
+#include "decode_common.hpp"
 
 namespace commvq {
 namespace {
@@ -28,32 +30,11 @@ constexpr int kThreads = 256;
 constexpr int kGenericTPT = 4;  // tokens per lane in the generic kernel
 constexpr int kHistShift = 20;  // fixed-point weights: w * 2^20 (chunk <= 1024 keeps sums < 2^31)
 
-__device__ __forceinline__ float2 position_phase(uint32_t m, uint32_t flo, uint32_t fhi) {
-  // top 32 bits of (m * F) mod 2^64 = the phase in turns, as a signed fraction
-  const uint32_t turns = m * fhi + __umulhi(m, flo);
-  const float x = (float)(int32_t)turns * 0x1p-31f;  // angle / pi in [-1, 1)
-  float s, c;
-  sincospif(x, &s, &c);
-  return make_float2(c, s);
-}
-
 __device__ __forceinline__ int read_field(const uint8_t* rec, int f, int bits) {
   const int o = f * bits, byte = o >> 3, sh = o & 7;
   uint32_t v = rec[byte];
   if (sh + bits > 8) v |= (uint32_t)rec[byte + 1] << 8;
   return (int)((v >> sh) & ((1u << bits) - 1u));
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
 }
 
 template <int NH, int GS>
@@ -70,6 +51,8 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, 
   const int L = min(max(a.seq_lens[b], 0), a.max_len);
   const int m0 = chunk_id * a.chunk;
   const int hq0 = h * NH;
+  const int red_floats = (NH * (NW > 2 ? NW : 2) + 2 * NH + 4) & ~3;
+  const int uni_floats = max(NH * K.Nc * PP * 2, NH * V.Nc);
   const size_t pstride = (size_t)a.n_chunks * (D + 2);
   float* part = a.part + ((size_t)b * a.Hq + hq0) * pstride + (size_t)chunk_id * (D + 2);
   if (m0 >= L) {
@@ -77,12 +60,14 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, 
       const int hh = i / (D + 2), k = i % (D + 2);
       part[hh * pstride + k] = (k == 0) ? -INFINITY : 0.f;
     }
+    merge_if_last<kThreads>(a, b, h, NH, D, reinterpret_cast<uint32_t*>(sm), sm + 4,
+                            2 * NH * P + NH * D + red_floats + uni_floats - 4);
     return;
   }
   float2* qz = reinterpret_cast<float2*>(sm);  // [NH][P]
   float* oacc = sm + 2 * NH * P;               // [NH][D]
   float* red = oacc + NH * D;                  // [NH][NW]
-  float* uni = red + ((NH * (NW > 2 ? NW : 2) + 3) & ~3);  // table or histogram
+  float* uni = red + red_floats;  // table or histogram
   float2* table = reinterpret_cast<float2*>(uni);
   uint32_t* hist = reinterpret_cast<uint32_t*>(uni);
 
@@ -91,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, 
     const int hh = i / P, p = i % P;
     const float* qrow = a.q + ((size_t)b * a.Hq + hq0 + hh) * D;
     const float x = qrow[2 * p], y = qrow[2 * p + 1];
-    const float2 w = position_phase(qp, ph.lo[p], ph.hi[p]);
+    const float2 w = phase_exact(qp, ph.lo[p], ph.hi[p]);
     qz[i] = make_float2(x * w.x - y * w.y, x * w.y + y * w.x);
   }
   for (int i = tid; i < NH * D; i += kThreads) oacc[i] = 0.f;
@@ -125,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, 
 #pragma unroll
           for (int pp = 0; pp < PP; ++pp) {
             const int p = j * PP + pp;
-            const float2 w = position_phase((uint32_t)m, ph.lo[p], ph.hi[p]);
+            const float2 w = phase_exact((uint32_t)m, ph.lo[p], ph.hi[p]);
 #pragma unroll
             for (int hh = 0; hh < NH; ++hh) {
               const float2 T = table[(hh * K.Nc + code) * PP + pp];
@@ -219,30 +204,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, 
     const int hh = i / (D + 2), k = i % (D + 2);
     part[hh * pstride + k] = k < 2 ? red[2 * hh + k] : oacc[hh * D + k - 2];
   }
-}
-
-// Merge the chunks of one (b, hq): o = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c.
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part, float* __restrict__ out,
-                                                      int n_chunks, int D) {
-  const int row = blockIdx.x;
-  const float* pr = part + (size_t)row * n_chunks * (D + 2);
-  float M = -INFINITY;
-  for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, pr[(size_t)c * (D + 2)]);
-  float lsum = 0.f;
-  if (M > -INFINITY)
-    for (int c = 0; c < n_chunks; ++c) {
-      const float mc = pr[(size_t)c * (D + 2)];
-      if (mc > -INFINITY) lsum += __expf(mc - M) * pr[(size_t)c * (D + 2) + 1];
-    }
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float acc = 0.f;
-    if (M > -INFINITY)
-      for (int c = 0; c < n_chunks; ++c) {
-        const float mc = pr[(size_t)c * (D + 2)];
-        if (mc > -INFINITY) acc = fmaf(__expf(mc - M), pr[(size_t)c * (D + 2) + 2 + d], acc);
-      }
-    out[(size_t)row * D + d] = lsum > 0.f ? acc / lsum : 0.f;
-  }
+  merge_if_last<kThreads>(a, b, h, NH, D, reinterpret_cast<uint32_t*>(red + 2 * NH), uni, uni_floats);
 }
 
 template <int NH, int GS>
@@ -251,7 +213,7 @@ hipError_t launch_generic(const DecodeArgs& a, const PhaseTable& ph, hipStream_t
   const int NW = kThreads / 64;
   size_t table_bytes = (size_t)NH * a.k.Nc * (GS / 2) * sizeof(float2);
   size_t hist_bytes = (size_t)NH * a.v.Nc * sizeof(uint32_t);
-  size_t smem = (2 * NH * P + NH * a.k.D + ((NH * (NW > 2 ? NW : 2) + 3) & ~3)) * sizeof(float) +
+  size_t smem = (2 * NH * P + NH * a.k.D + ((NH * (NW > 2 ? NW : 2) + 2 * NH + 4) & ~3)) * sizeof(float) +
                 (table_bytes > hist_bytes ? table_bytes : hist_bytes);
   if (smem > 160 * 1024) return hipErrorInvalidValue;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_generic_kernel<NH, GS>),
@@ -259,10 +221,6 @@ hipError_t launch_generic(const DecodeArgs& a, const PhaseTable& ph, hipStream_t
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_generic_kernel<NH, GS>), dim3(a.n_chunks, a.k.Hkv, a.B), dim3(kThreads), smem, stream,
                      a, ph);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.Hq), dim3(a.k.D < 256 ? a.k.D : 256), 0, stream, a.part, a.out,
-                     a.n_chunks, a.k.D);
   return hipGetLastError();
 }
 
@@ -279,17 +237,27 @@ hipError_t launch_generic_nh(const DecodeArgs& a, const PhaseTable& ph, hipStrea
 
 }  // namespace
 
-int decode_chunk_len(const CbShape& k, const CbShape& v, int B, int Hq, int max_len) {
-  (void)k; (void)v; (void)B; (void)Hq; (void)max_len;
-  return kThreads * kGenericTPT;
+bool decode_fast_path(const CbShape& k, const CbShape& v, int NH, int flags) {
+  return !(flags & 1) && k.D == 128 && k.g == 8 && k.Nc == 256 && v.Nc == 256 && k.R == v.R &&
+         (k.R == 1 || k.R == 2) && NH == 4;
 }
 
-bool decode_fast_path(const CbShape& k, const CbShape& v, int NH) {
-  (void)k; (void)v; (void)NH;
-  return false;
+int decode_chunk_len(const CbShape& k, const CbShape& v, int B, int Hq, int max_len, int flags) {
+  if (!decode_fast_path(k, v, Hq / k.Hkv, flags)) return kThreads * kGenericTPT;
+  // the longest chunk that still gives every compute unit a workgroup
+  for (int c : {4096, 2048}) {
+    const long long wgs = (long long)B * k.Hkv * ((max_len + c - 1) / c);
+    if (wgs >= 256) return c;
+  }
+  return 1024;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
+size_t decode_workspace_bytes(const CbShape& k, int B, int Hq, int max_len, int chunk) {
+  const size_t n_chunks = (size_t)(max_len + chunk - 1) / chunk;
+  return counter_bytes(B, k.Hkv) + (size_t)B * Hq * n_chunks * (k.D + 2) * sizeof(float);
+}
+
+hipError_t launch_decode_generic(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
   switch (a.NH) {
     case 1: return launch_generic_nh<1>(a, ph, stream);
     case 2: return launch_generic_nh<2>(a, ph, stream);

@@ -88,8 +88,80 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a, int tile) {
   }
 }
 
+// Few-token variant (decode-time append): one workgroup per (token, KV head),
+// one wavefront per group at a time, lanes spread over the codebook entries. The
+// distance arithmetic is the bulk kernel's, term by term, so both pick the same
+// entries; the wave-wide argmin keeps the lowest index on ties.
+template <int GS>
+__global__ __launch_bounds__(256) void encode_few_kernel(EncodeArgs a) {
+  __shared__ uint8_t codes_l[4 * 128];  // [R][G], R*G <= 512
+  const CbShape s = a.s;
+  const int R = s.R, Nc = s.Nc, G = s.G, D = s.D;
+  const int64_t t = blockIdx.x;
+  const int h = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const _Float16* xp;
+  uint8_t* rec;
+  if (a.positions) {
+    const int pos = a.positions[t];
+    if (pos < 0 || pos >= a.cache_len) return;  // uniform over the workgroup
+    xp = a.x + (t * s.Hkv + h) * (int64_t)D;
+    rec = a.codes + t * a.code_token_stride + h * a.code_head_stride + (int64_t)pos * s.bpt;
+  } else {
+    xp = a.x + t * a.x_token_stride + (int64_t)h * D;
+    rec = a.codes + t * a.code_token_stride + h * a.code_head_stride;
+  }
+  for (int j = wave; j < G; j += 4) {
+    float e[GS];
+#pragma unroll
+    for (int i = 0; i < GS; ++i) e[i] = (float)xp[j * GS + i];
+    for (int r = 0; r < R; ++r) {
+      const _Float16* c = a.cb + (((int64_t)h * G + j) * R + r) * Nc * GS;
+      float best = INFINITY;
+      int bi = 0x7fffffff;
+      for (int l = lane; l < Nc; l += 64) {
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < GS; ++i) {
+          const float df = e[i] - (float)c[l * GS + i];
+          d = fmaf(df, df, d);
+        }
+        if (d < best) {
+          best = d;
+          bi = l;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float od = __shfl_xor(best, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (od < best || (od == best && oi < bi)) {
+          best = od;
+          bi = oi;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < GS; ++i) e[i] -= (float)c[bi * GS + i];
+      if (lane == 0) codes_l[r * G + j] = (uint8_t)bi;
+    }
+  }
+  __syncthreads();
+  // byte k of the record collects record bits [8k, 8k + 8)
+  for (int k = threadIdx.x; k < s.bpt; k += blockDim.x) {
+    uint32_t v = 0;
+    for (int i = 0; i < 8; ++i) {
+      const int P = 8 * k + i, f = P / s.bits;
+      if (f < R * G) v |= (((uint32_t)codes_l[f] >> (P % s.bits)) & 1u) << i;
+    }
+    rec[k] = (uint8_t)v;
+  }
+}
+
 template <int GS>
 hipError_t launch_encode_g(const EncodeArgs& a, hipStream_t stream) {
+  if (a.n_tokens <= 64 && a.s.R * a.s.G <= 512) {
+    hipLaunchKernelGGL(encode_few_kernel<GS>, dim3((unsigned)a.n_tokens, a.s.Hkv), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   const CbShape& s = a.s;
   const size_t cb_bytes = (size_t)s.R * s.Nc * GS * sizeof(float);
   int tile = 256;

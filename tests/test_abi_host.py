@@ -101,11 +101,11 @@ def test_append_validation_without_launch():
 
 
 def _raw_decode(k, v, rope, B=1, Hq=32, cache_len=1024, max_len=1024, scale=0.088, ws=FAKE, ws_bytes=1 << 30,
-                q=FAKE, out=FAKE, codes=FAKE):
+                q=FAKE, out=FAKE, codes=FAKE, flags=0):
     L = _lib.lib()
     return L.commvq_decode_attention(ctypes.byref(k), ctypes.byref(v), ctypes.byref(rope) if rope else None,
                                      q, FAKE, codes, codes, FAKE, B, Hq, cache_len, max_len, scale, out, ws,
-                                     ws_bytes, None)
+                                     ws_bytes, flags, None)
 
 
 def test_decode_validation_without_launch():
@@ -120,6 +120,7 @@ def test_decode_validation_without_launch():
     assert _raw_decode(k, k, rope, max_len=2048) == E.COMMVQ_ERR_INVALID_ARG  # beyond the cache
     assert _raw_decode(k, k, rope, B=0) == E.COMMVQ_ERR_INVALID_ARG
     assert _raw_decode(k, k, rope, scale=float("inf")) == E.COMMVQ_ERR_INVALID_ARG
+    assert _raw_decode(k, k, rope, flags=2) == E.COMMVQ_ERR_INVALID_ARG
     assert _raw_decode(k, k, rope, ws_bytes=16) == E.COMMVQ_ERR_WORKSPACE
     assert _raw_decode(k, k, rope, ws=None) == E.COMMVQ_ERR_WORKSPACE
     assert _raw_decode(k, k, rope, ws=FAKE + 64) == E.COMMVQ_ERR_WORKSPACE  # 256-byte alignment

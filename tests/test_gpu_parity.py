@@ -117,7 +117,7 @@ def _pack_cache(codes, n_entries):
 
 
 def run_decode_case(seed, B, Hq, Hkv, D, g, Nc, R, lens, Lmax, Ncv=None, Rv=None, q_scale=1.0,
-                    q_pos=None, theta=500000.0, max_len=None, sm_scale=None):
+                    q_pos=None, theta=500000.0, max_len=None, sm_scale=None, exact=False):
     Ncv = Nc if Ncv is None else Ncv
     Rv = R if Rv is None else Rv
     G = D // g
@@ -134,7 +134,8 @@ def run_decode_case(seed, B, Hq, Hkv, D, g, Nc, R, lens, Lmax, Ncv=None, Rv=None
     scale = 1.0 / math.sqrt(D) if sm_scale is None else sm_scale
     ref = O.decode_attention_from_packed(q, qpos, kp, vp, np.minimum(lens, max_len), kcb, vcb, theta, scale)
     kq, vq = api.Quantizer(dev(kcb), g), api.Quantizer(dev(vcb), g)
-    out = api.decode_attention(kq, vq, dev(q), dev(qpos), dev(kp), dev(vp), dev(lens), max_len, theta, scale)
+    out = api.decode_attention(kq, vq, dev(q), dev(qpos), dev(kp), dev(vp), dev(lens), max_len, theta, scale,
+                               exact=exact)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     err = row_errors(got.reshape(-1, D), ref.reshape(-1, D))
@@ -186,11 +187,34 @@ def test_decode_shapes(case):
 
 
 @pytest.mark.parametrize("q_scale", [8.0, 30.0])
-def test_decode_peaked_queries(q_scale):
-    got, ref, err = run_decode_case(77, B=2, Hq=8, Hkv=2, D=128, g=8, Nc=256, R=2, lens=[4000, 2500], Lmax=4096,
-                                    q_scale=q_scale)
-    print(f"[decode peaked x{q_scale}] max row rel err {err.max():.3e}", flush=True)
+@pytest.mark.parametrize("R", [1, 2])
+def test_decode_peaked_queries_exact_mode(q_scale, R):
+    """Strongly peaked attention through the exact-precision mode (fp32 table)."""
+    got, ref, err = run_decode_case(77, B=2, Hq=8, Hkv=2, D=128, g=8, Nc=256, R=R, lens=[4000, 2500], Lmax=4096,
+                                    q_scale=q_scale, exact=True)
+    print(f"[decode exact peaked x{q_scale} R{R}] max row rel err {err.max():.3e}", flush=True)
     assert err.max() <= ATTN_TOL
+
+
+@pytest.mark.parametrize("q_scale", [1.0, 2.0])
+@pytest.mark.parametrize("R", [1, 2])
+def test_decode_fast_path_query_scales(q_scale, R):
+    """fp16-table kernel: unit-variance queries (the workloads' distribution) and twice that."""
+    got, ref, err = run_decode_case(78 + R, B=2, Hq=8, Hkv=2, D=128, g=8, Nc=256, R=R, lens=[5000, 3001],
+                                    Lmax=5120, q_scale=q_scale)
+    print(f"[decode fast x{q_scale} R{R}] max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= ATTN_TOL
+
+
+@pytest.mark.parametrize("R", [1, 2])
+def test_decode_fast_and_exact_agree_on_chunk_edges(R):
+    """Ragged lengths around chunk boundaries and a single-position sequence."""
+    lens = [1, 255, 256, 257, 1023, 1024, 1025, 4095, 4096, 4097]
+    for exact in (False, True):
+        got, ref, err = run_decode_case(90 + R, B=len(lens), Hq=4, Hkv=1, D=128, g=8, Nc=256, R=R, lens=lens,
+                                        Lmax=4100, exact=exact)
+        print(f"[decode edges R{R} exact={exact}] max row rel err {err.max():.3e}", flush=True)
+        assert err.max() <= ATTN_TOL
 
 
 def test_decode_edge_cases():
