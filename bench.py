@@ -119,8 +119,8 @@ def main():
 
     # per-step inputs: new K/V token, query, device-side positions and lengths
     n_total = args.warmup + args.steps
-    knew = torch.from_numpy(synth.kv(w.seed + 30, n_total, H, D)).to(dev).reshape(n_total, 1, H, D)
-    vnew = torch.from_numpy(synth.kv(w.seed + 31, n_total, H, D)).to(dev).reshape(n_total, 1, H, D)
+    knew = torch.from_numpy(synth.kv(w.seed + 30, n_total, H, D)).to(dev).reshape(n_total, 1, 1, H, D)
+    vnew = torch.from_numpy(synth.kv(w.seed + 31, n_total, H, D)).to(dev).reshape(n_total, 1, 1, H, D)
     qs = torch.from_numpy(synth.queries(w.seed + 32, n_total, Hq, D)).to(dev).reshape(n_total, 1, Hq, D)
     positions = torch.arange(PREFILL, PREFILL + N_POSITIONS, dtype=torch.int32, device=dev).reshape(-1, 1)
     lens = positions + 1
@@ -135,12 +135,11 @@ def main():
 
     def run_step(i, timed_idx=None):
         li, t = layer_and_pos(i)
-        api.append(kq, knew[i], positions[t], kcaches[li])
-        api.append(vq, vnew[i], positions[t], vcaches[li])
         if timed_idx is not None:
             ev[timed_idx][0].record(stream)
-        api.decode_attention(kq, vq, qs[i], positions[t], kcaches[li], vcaches[li], lens[t], Lmax, w.theta_base,
-                             out=out, workspace=ws)
+        # append the new token's K and V codes at position t, then attend over [0, t]
+        api.decode_step(kq, vq, knew[i][0], vnew[i][0], positions[t], qs[i], positions[t], kcaches[li], vcaches[li],
+                        lens[t], Lmax, w.theta_base, out=out, workspace=ws)
         if timed_idx is not None:
             ev[timed_idx][1].record(stream)
 
@@ -192,15 +191,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "fp16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "batch": B, "n_q_heads": Hq, "n_kv_heads": H, "head_dim": D,
                    "context": Lmax, "prefill": PREFILL, "group_size": w.group_size, "n_entries": w.n_entries,
                    "n_rounds": w.n_rounds, "bits_per_scalar": w.n_rounds * math.log2(w.n_entries) / w.group_size,
-                   "layer_slices": NL, "step": "append K+V (1 token, 8 KV heads) + decode attention"},
+                   "layer_slices": NL, "step": "commvq_decode_step: encode+append K and V of 1 token (8 KV heads), then attention"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "decode attention", "bytes_per_launch": bytes_per_launch,
+                     "kernel": "decode step (fused append + attention)", "bytes_per_launch": bytes_per_launch,
                      "avg_launch_us": dec_avg_ms * 1e3},
         "cpu_baseline": cpu,
     }

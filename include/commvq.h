@@ -159,6 +159,26 @@ int32_t commvq_decode_attention(const commvq_codebook* kcb, const commvq_codeboo
                                 float* out, void* workspace, size_t workspace_bytes,
                                 uint32_t flags, void* stream);
 
+/* One decode step: encode the new token's key and value (all KV heads), write
+ * them into the caches at positions[b], then attend exactly as
+ * commvq_decode_attention does over keys [0, seq_lens[b]).
+ *   k_new, v_new device fp16 [batch][Hkv][D], 16-byte aligned
+ *   positions    device int32 [batch]; a position outside [0, cache_len) skips
+ *                the append for that sequence (attention still runs)
+ *   kcodes, vcodes are written (the new records) and read.
+ * Other arguments as commvq_decode_attention. For the fp16-table shapes the new
+ * token is encoded inside the attention kernel, so the whole step is one launch.
+ * Pages: abstract (each new K/V vector is encoded to a low-bit code); "What
+ * carries the argument" (shared index per group, R residual rounds, codebook
+ * factors reused over cached positions). */
+int32_t commvq_decode_step(const commvq_codebook* kcb, const commvq_codebook* vcb,
+                           const commvq_rope* rope, const void* k_new, const void* v_new,
+                           const int32_t* positions, const float* q, const int32_t* q_pos,
+                           uint8_t* kcodes, uint8_t* vcodes, const int32_t* seq_lens,
+                           int32_t batch, int32_t n_q_heads, int32_t cache_len,
+                           int32_t max_seq_len, float sm_scale, float* out, void* workspace,
+                           size_t workspace_bytes, uint32_t flags, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

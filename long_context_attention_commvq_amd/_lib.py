@@ -34,7 +34,7 @@ STATUS_NAMES = {
 EXPORTED = [
     "commvq_abi_version", "commvq_last_error", "commvq_validate_codebook", "commvq_bits_per_scalar",
     "commvq_code_bytes_per_token", "commvq_decode_workspace_bytes", "commvq_encode", "commvq_append",
-    "commvq_decode_attention",
+    "commvq_decode_attention", "commvq_decode_step",
 ]
 
 
@@ -85,6 +85,10 @@ def lib():
         L.commvq_decode_attention.argtypes = [CB, CB, POINTER(commvq_rope), c_void_p, c_void_p, c_void_p,
                                               c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                               c_float, c_void_p, c_void_p, c_size_t, ctypes.c_uint32, c_void_p]
+        L.commvq_decode_step.restype = c_int32
+        L.commvq_decode_step.argtypes = [CB, CB, POINTER(commvq_rope), c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
+                                         c_float, c_void_p, c_void_p, c_size_t, ctypes.c_uint32, c_void_p]
         _lib = L
     return _lib
 
@@ -171,3 +175,12 @@ def commvq_decode_attention(kcb: commvq_codebook, vcb: commvq_codebook, rope: co
         ctypes.byref(kcb), ctypes.byref(vcb), ctypes.byref(rope), _ptr(q), _ptr(q_pos), _ptr(kcodes),
         _ptr(vcodes), _ptr(seq_lens), batch, n_q_heads, cache_len, max_seq_len, float(sm_scale), _ptr(out),
         _ptr(workspace), int(workspace_bytes), int(flags), _stream(stream, q, out)))
+
+
+def commvq_decode_step(kcb: commvq_codebook, vcb: commvq_codebook, rope: commvq_rope, k_new, v_new, positions, q,
+                       q_pos, kcodes, vcodes, seq_lens, batch: int, n_q_heads: int, cache_len: int, max_seq_len: int,
+                       sm_scale: float, out, workspace, workspace_bytes: int, flags: int = 0, stream=None) -> int:
+    return _check(lib().commvq_decode_step(
+        ctypes.byref(kcb), ctypes.byref(vcb), ctypes.byref(rope), _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(q),
+        _ptr(q_pos), _ptr(kcodes), _ptr(vcodes), _ptr(seq_lens), batch, n_q_heads, cache_len, max_seq_len,
+        float(sm_scale), _ptr(out), _ptr(workspace), int(workspace_bytes), int(flags), _stream(stream, q, out)))

@@ -91,3 +91,23 @@ def decode_attention(kq: Quantizer, vq: Quantizer, q: torch.Tensor, q_pos: torch
                                  kcache.shape[2], max_seq_len, sm_scale, out, workspace.buf, workspace.nbytes,
                                  _lib.COMMVQ_DECODE_EXACT if exact else 0)
     return out
+
+
+def decode_step(kq: Quantizer, vq: Quantizer, k_new: torch.Tensor, v_new: torch.Tensor, positions: torch.Tensor,
+                q: torch.Tensor, q_pos: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
+                seq_lens: torch.Tensor, max_seq_len: int, theta_base: float, sm_scale: float | None = None,
+                out: torch.Tensor | None = None, workspace: DecodeWorkspace | None = None,
+                exact: bool = False) -> torch.Tensor:
+    """Append k_new/v_new fp16 [B, Hkv, D] at positions[b], then attend (one call)."""
+    B, Hq, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = DecodeWorkspace(kq, vq, B, Hq, max_seq_len, q.device)
+    rope = _lib.make_rope(theta_base)
+    _lib.commvq_decode_step(kq.desc, vq.desc, rope, k_new.contiguous(), v_new.contiguous(), positions, q, q_pos,
+                            kcache, vcache, seq_lens, B, Hq, kcache.shape[2], max_seq_len, sm_scale, out,
+                            workspace.buf, workspace.nbytes, _lib.COMMVQ_DECODE_EXACT if exact else 0)
+    return out

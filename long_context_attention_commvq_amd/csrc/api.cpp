@@ -221,11 +221,21 @@ int32_t commvq_append(const commvq_codebook* cb, const void* x, int32_t batch, c
   return hip_status(commvq::launch_encode(a, static_cast<hipStream_t>(stream)), "commvq_append launch");
 }
 
-int32_t commvq_decode_attention(const commvq_codebook* kcb, const commvq_codebook* vcb, const commvq_rope* rope,
-                                const float* q, const int32_t* q_pos, const uint8_t* kcodes,
-                                const uint8_t* vcodes, const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
-                                int32_t cache_len, int32_t max_seq_len, float sm_scale, float* out,
-                                void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+}  // extern "C"
+
+namespace {
+
+struct StepArgs {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* positions;
+};
+
+int32_t decode_impl(const commvq_codebook* kcb, const commvq_codebook* vcb, const commvq_rope* rope, const float* q,
+                    const int32_t* q_pos, const uint8_t* kcodes, const uint8_t* vcodes, const int32_t* seq_lens,
+                    int32_t batch, int32_t n_q_heads, int32_t cache_len, int32_t max_seq_len, float sm_scale,
+                    float* out, void* workspace, size_t workspace_bytes, uint32_t flags, const StepArgs* step,
+                    void* stream) {
   g_err[0] = 0;
   commvq::CbShape k, v;
   int32_t st = decode_shapes(kcb, vcb, batch, n_q_heads, max_seq_len, &k, &v);
@@ -249,6 +259,12 @@ int32_t commvq_decode_attention(const commvq_codebook* kcb, const commvq_codeboo
     return fail(COMMVQ_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(kcodes) | reinterpret_cast<uintptr_t>(vcodes)) & 15)
     return fail(COMMVQ_ERR_INVALID_ARG, "code caches must be 16-byte aligned");
+  if (step) {
+    if (!step->k_new || !step->v_new || !step->positions)
+      return fail(COMMVQ_ERR_INVALID_ARG, "null k_new, v_new or positions pointer");
+    if ((reinterpret_cast<uintptr_t>(step->k_new) | reinterpret_cast<uintptr_t>(step->v_new)) & 15)
+      return fail(COMMVQ_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+  }
   const int64_t need = commvq_decode_workspace_bytes(batch, n_q_heads, max_seq_len, kcb, vcb);
   if (need < 0) return (int32_t)need;
   if (!workspace || workspace_bytes < (size_t)need)
@@ -279,15 +295,66 @@ int32_t commvq_decode_attention(const commvq_codebook* kcb, const commvq_codeboo
   a.v = v;
   commvq::PhaseTable ph;
   phase_table(rope->theta_base, k.D, &ph);
-  hipError_t e;
-  if (commvq::decode_fast_path(k, v, a.NH, (int)flags)) {
-    commvq::FastPhase fp;
-    fast_phase(rope->theta_base, k.D, &fp);
-    e = commvq::launch_decode_fast(a, ph, fp, static_cast<hipStream_t>(stream));
-  } else {
-    e = commvq::launch_decode_generic(a, ph, static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fast = commvq::decode_fast_path(k, v, a.NH, (int)flags);
+  hipError_t e = hipSuccess;
+  if (step && fast) {
+    // the fast kernel encodes the new token inside the workgroup that reads it
+    a.k_new = static_cast<const _Float16*>(step->k_new);
+    a.v_new = static_cast<const _Float16*>(step->v_new);
+    a.positions = step->positions;
+    a.kcodes_w = const_cast<uint8_t*>(kcodes);
+    a.vcodes_w = const_cast<uint8_t*>(vcodes);
+  } else if (step) {
+    for (int kv = 0; kv < 2 && e == hipSuccess; ++kv) {
+      const commvq::CbShape& sh = kv ? v : k;
+      commvq::EncodeArgs ea{};
+      ea.x = static_cast<const _Float16*>(kv ? step->v_new : step->k_new);
+      ea.cb = static_cast<const _Float16*>(kv ? vcb->entries : kcb->entries);
+      ea.codes = const_cast<uint8_t*>(kv ? vcodes : kcodes);
+      ea.n_tokens = batch;
+      ea.x_token_stride = (int64_t)sh.Hkv * sh.D;
+      ea.code_token_stride = (int64_t)sh.Hkv * cache_len * sh.bpt;
+      ea.code_head_stride = (int64_t)cache_len * sh.bpt;
+      ea.positions = step->positions;
+      ea.cache_len = cache_len;
+      ea.s = sh;
+      e = commvq::launch_encode(ea, s);
+    }
   }
-  return hip_status(e, "commvq_decode_attention launch");
+  if (e == hipSuccess) {
+    if (fast) {
+      commvq::FastPhase fp;
+      fast_phase(rope->theta_base, k.D, &fp);
+      e = commvq::launch_decode_fast(a, ph, fp, s);
+    } else {
+      e = commvq::launch_decode_generic(a, ph, s);
+    }
+  }
+  return hip_status(e, step ? "commvq_decode_step launch" : "commvq_decode_attention launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t commvq_decode_attention(const commvq_codebook* kcb, const commvq_codebook* vcb, const commvq_rope* rope,
+                                const float* q, const int32_t* q_pos, const uint8_t* kcodes,
+                                const uint8_t* vcodes, const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
+                                int32_t cache_len, int32_t max_seq_len, float sm_scale, float* out,
+                                void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+  return decode_impl(kcb, vcb, rope, q, q_pos, kcodes, vcodes, seq_lens, batch, n_q_heads, cache_len, max_seq_len,
+                     sm_scale, out, workspace, workspace_bytes, flags, nullptr, stream);
+}
+
+int32_t commvq_decode_step(const commvq_codebook* kcb, const commvq_codebook* vcb, const commvq_rope* rope,
+                           const void* k_new, const void* v_new, const int32_t* positions, const float* q,
+                           const int32_t* q_pos, uint8_t* kcodes, uint8_t* vcodes, const int32_t* seq_lens,
+                           int32_t batch, int32_t n_q_heads, int32_t cache_len, int32_t max_seq_len, float sm_scale,
+                           float* out, void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+  StepArgs st{k_new, v_new, positions};
+  return decode_impl(kcb, vcb, rope, q, q_pos, kcodes, vcodes, seq_lens, batch, n_q_heads, cache_len, max_seq_len,
+                     sm_scale, out, workspace, workspace_bytes, flags, &st, stream);
 }
 
 }  // extern "C"

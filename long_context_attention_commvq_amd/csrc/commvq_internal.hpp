@@ -42,6 +42,13 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   const _Float16* kcb;
   const _Float16* vcb;
+  // fused decode step: when k_new is set, the new token of sequence b (fp16
+  // [B][Hkv][D] keys / values) is encoded into the caches at positions[b]
+  const _Float16* k_new;
+  const _Float16* v_new;
+  const int32_t* positions;
+  uint8_t* kcodes_w;
+  uint8_t* vcodes_w;
   uint32_t* counters;  // [B][Hkv] arrival counters (zero between calls)
   float* part;         // [B][Hq][n_chunks][D + 2]: (max, sum, o[D]) per chunk
   float* out;          // [B][Hq][D]

@@ -31,6 +31,7 @@
 // (sequence, KV head) merges the chunks.
 
 #include "decode_common.hpp"
+#include "encode_common.hpp"
 
 namespace commvq {
 namespace {
@@ -56,10 +57,12 @@ struct FastCfg {
 };
 
 // aux LDS: phase tables [64][HI_N] + [64][16], step multipliers [64], rotated
-// query [4][64], reductions [64], MFMA staging [2][64][4], flag
+// query [4][64], reductions [64], MFMA staging [2][64][4], flag, and a decode
+// step's new token: codes [2][2][16], scores [4], value [128]
 constexpr int EHI_BYTES = FPR * HI_N * 8;
 constexpr int ELO_BYTES = FPR * 16 * 8;
-constexpr int AUX_BYTES = EHI_BYTES + ELO_BYTES + FPR * 8 + FNH * FPR * 8 + 64 * 4 + 2 * 64 * 4 * 4 + 16;
+constexpr int NEW_BYTES = 64 + FNH * 4 + FD * 4;
+constexpr int AUX_BYTES = EHI_BYTES + ELO_BYTES + FPR * 8 + FNH * FPR * 8 + 64 * 4 + 2 * 64 * 4 * 4 + 16 + NEW_BYTES;
 static_assert(131072 + AUX_BYTES <= 160 * 1024, "LDS budget");
 static_assert(EHI_BYTES >= 4 * 4096, "value-codebook slabs reuse the phase table");
 
@@ -98,6 +101,9 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   float* red = reinterpret_cast<float*>(qz + FNH * FPR);     // [64] reductions
   float* stage = red + 64;                                   // [2][64][4] MFMA partials
   uint32_t* flag = reinterpret_cast<uint32_t*>(stage + 2 * 64 * 4);
+  uint8_t* new_codes = reinterpret_cast<uint8_t*>(flag + 4);         // [2][R][16]
+  float* new_s = reinterpret_cast<float*>(new_codes + 64);           // [4] scaled scores
+  float* new_v = new_s + FNH;                                        // [128]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -105,6 +111,29 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   const int m0 = chunk * C;
   const size_t pstride = (size_t)a.n_chunks * (FD + 2);
   float* part = a.part + ((size_t)b * a.Hq + h * FNH) * pstride + (size_t)chunk * (FD + 2);
+  // decode step: the workgroup whose chunk holds the new position encodes the new
+  // key and value of its KV head (all 32 group searches at once, 16 lanes each)
+  // and writes the records; its table path leaves that position out and the
+  // token joins the chunk's partial with an exact fp32 score at the end
+  const int pb = a.k_new ? a.positions[b] : -1;
+  const bool appended = a.k_new && pb >= 0 && pb < a.cache_len;
+  const int skip_pos = appended ? pb : -1;
+  const bool owner = appended && chunk == min(pb / C, a.n_chunks - 1);
+  if (owner) {
+    const int row = tid >> 4, kv = row / FG, j = row % FG;
+    const _Float16* x = (kv ? a.v_new : a.k_new) + ((size_t)b * a.k.Hkv + h) * FD + j * 8;
+    float e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = (float)x[i];
+    const _Float16* cbg = (kv ? a.vcb : a.kcb) + ((size_t)h * FG + j) * R * FNC * 8;
+    greedy_group_row16(e, cbg, FNC, R, tid & 15, new_codes + kv * R * FG + j, FG);
+    __syncthreads();
+    if (tid < 2 * BPT) {  // 8-bit fields: the record is the codes, round-major
+      const int kv2 = tid / BPT, k = tid % BPT;
+      uint8_t* cache = kv2 ? a.vcodes_w : a.kcodes_w;
+      cache[(((size_t)b * a.k.Hkv + h) * a.cache_len + pb) * BPT + k] = new_codes[kv2 * BPT + k];
+    }
+  }
   if (m0 >= L) {
     for (int i = tid; i < FNH * (FD + 2); i += FT) {
       const int hh = i / (FD + 2), k = i % (FD + 2);
@@ -119,7 +148,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
 
   // ---- scores -------------------------------------------------------------
   // A slice's code bytes of every owned position, rotated so that byte kj belongs
-  // to group pass*J + ((kj + gr) & (J-1)); loaded one slice ahead of use.
+  // to group pass*J + ((kj + gr) & (J-1)).
   auto load_codes = [&](int pass, uint32_t (&cw)[TL][R][J / 4]) {
 #pragma unroll
     for (int t = 0; t < TL; ++t) {
@@ -140,10 +169,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
       }
     }
   };
-  // R = 1 keeps the next slice's codes in flight during the current one; R = 2 has
-  // no registers to spare and loads them at the start of each slice instead.
-  constexpr bool PREFETCH = (R == 1);
-  uint32_t cw[TL][R][J / 4], cwn[PREFETCH ? TL : 1][R][J / 4];
+  uint32_t cw[TL][R][J / 4];
   load_codes(0, cw);
 
   // ---- per-workgroup constants ------------------------------------------
@@ -166,6 +192,36 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     qz[tid] = make_float2(x * w.x - y * w.y, x * w.y + y * w.x);
   }
 
+  const bool fold = owner && pb < L;
+  if (fold) {
+    __syncthreads();  // rotated query visible
+    if (wave == 0) {
+      // exact fp32 score of the new key for the four query heads (lane = RoPE pair)
+      const int p = lane, j = p >> 2, pp = p & 3;
+      float kx = 0.f, ky = 0.f;
+      for (int r = 0; r < R; ++r) {
+        const _Float16* ce = a.kcb + ((((size_t)h * FG + j) * R + r) * FNC + new_codes[r * FG + j]) * 8 + 2 * pp;
+        kx += (float)ce[0];
+        ky += (float)ce[1];
+      }
+      const float2 wk = phase_exact((uint32_t)pb, ph.lo[p], ph.hi[p]);
+      const float krx = kx * wk.x - ky * wk.y, kry = kx * wk.y + ky * wk.x;
+#pragma unroll
+      for (int k = 0; k < FNH; ++k) {
+        const float2 qv = qz[k * FPR + p];
+        const float sc = wave_sum(qv.x * krx + qv.y * kry);
+        if (lane == 0) new_s[k] = sc * a.sm_scale;
+      }
+    } else if (tid >= 128 && tid < 256) {
+      // its dequantised value, one dimension per lane
+      const int d = tid - 128, j = d >> 3, ee = d & 7;
+      float v = 0.f;
+      for (int r = 0; r < R; ++r)
+        v += (float)a.vcb[((((size_t)h * FG + j) * R + r) * FNC + new_codes[BPT + r * FG + j]) * 8 + ee];
+      new_v[d] = v;
+    }
+  }
+
   float s[TL][FNH];
 #pragma unroll
   for (int t = 0; t < TL; ++t)
@@ -179,7 +235,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
 
 #pragma unroll 1
   for (int pass = 0; pass < NPASS; ++pass) {
-    if (!PREFETCH && pass > 0) load_codes(pass, cw);
+    if (pass > 0) load_codes(pass, cw);  // in flight during the table build
     __syncthreads();  // previous slice fully consumed; constants visible
     {
       // table slice: this lane builds every (round, code) row of group pass*J + (tid % J)
@@ -212,9 +268,6 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
       }
     }
     __syncthreads();  // slice built
-    if constexpr (PREFETCH) {
-      if (pass + 1 < NPASS) load_codes(pass + 1, cwn);
-    }
 
 #pragma unroll
     for (int hf = 0; hf < NHALF; ++hf) {
@@ -282,23 +335,14 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
         }
       }
     }
-    if constexpr (PREFETCH) {
-      if (pass + 1 < NPASS) {
-#pragma unroll
-        for (int t = 0; t < TL; ++t)
-#pragma unroll
-          for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int x = 0; x < J / 4; ++x) cw[t][r][x] = cwn[t][r][x];
-      }
-    }
   }
 
   // ---- softmax over the chunk ---------------------------------------------
   float M[FNH], lsum[FNH];
 #pragma unroll
   for (int t = 0; t < TL; ++t) {
-    const bool ok = m0 + tid + FT * t < L;
+    const int mt = m0 + tid + FT * t;
+    const bool ok = mt < L && mt != skip_pos;
     float v[FNH];
 #pragma unroll
     for (int k = 0; k < FNH; ++k) {
@@ -329,9 +373,10 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
 #pragma unroll
   for (int k = 0; k < FNH; ++k) {
     float acc = 0.f;
+    const float ref = M[k] == -INFINITY ? 0.f : M[k];  // a chunk may hold only the skipped new position
 #pragma unroll
     for (int t = 0; t < TL; ++t) {
-      const float pw = __expf(s[t][k] - M[k]);  // exp(-inf) = 0 for masked positions
+      const float pw = __expf(s[t][k] - ref);  // exp(-inf) = 0 for masked positions
       s[t][k] = pw;
       acc += pw;
     }
@@ -381,7 +426,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
 #pragma unroll
     for (int t = 0; t < TL; ++t) {
       const int m = m0 + tid + FT * t;
-      if (m < L) {
+      if (m < L && m != skip_pos) {
         const uint8_t* rec = vb + (size_t)m * BPT;
         uint32_t e[R][4];
 #pragma unroll
@@ -464,13 +509,31 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
       for (int k = 0; k < 4; ++k) stage[(sI * 64 + lane) * 4 + k] = acc[k];
     }
     __syncthreads();
-    if (active && kh == 0) {
+    // with the new token folded in (decode step owner): M' = max(M, s_new),
+    // o' = o e^{M - M'} + v_new e^{s_new - M'}, l' = l e^{M - M'} + e^{s_new - M'}
+    float al[FNH], be[FNH], Mf[FNH];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) part[k * pstride + 2 + 8 * j + e] = acc[k] + stage[(sI * 64 + lane) * 4 + k];
+    for (int k = 0; k < FNH; ++k) {
+      if (fold) {
+        const float sn = new_s[k];
+        Mf[k] = fmaxf(M[k], sn);
+        al[k] = M[k] == -INFINITY ? 0.f : __expf(M[k] - Mf[k]);
+        be[k] = __expf(sn - Mf[k]);
+      } else {
+        Mf[k] = M[k];
+        al[k] = 1.f;
+        be[k] = 0.f;
+      }
+    }
+    if (active && kh == 0) {
+      const float vn = fold ? new_v[8 * j + e] : 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        part[k * pstride + 2 + 8 * j + e] = (acc[k] + stage[(sI * 64 + lane) * 4 + k]) * al[k] + vn * be[k];
     }
     if (tid < FNH) {
-      part[tid * pstride + 0] = M[tid];
-      part[tid * pstride + 1] = lsum[tid];
+      part[tid * pstride + 0] = Mf[tid];
+      part[tid * pstride + 1] = lsum[tid] * al[tid] + be[tid];
     }
   }
   merge_if_last<FT>(a, b, h, FNH, FD, flag, reinterpret_cast<float*>(lds), Cfg::TAB / 4);

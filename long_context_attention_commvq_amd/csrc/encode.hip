@@ -12,7 +12,7 @@
 // float and read by every lane at the same address (broadcast, no conflicts).
 // Codes collect in LDS and each lane packs its own record at the end.
 
-#include "commvq_internal.hpp"
+#include "encode_common.hpp"
 
 namespace commvq {
 namespace {
@@ -114,35 +114,7 @@ __global__ __launch_bounds__(256) void encode_few_kernel(EncodeArgs a) {
     float e[GS];
 #pragma unroll
     for (int i = 0; i < GS; ++i) e[i] = (float)xp[j * GS + i];
-    for (int r = 0; r < R; ++r) {
-      const _Float16* c = a.cb + (((int64_t)h * G + j) * R + r) * Nc * GS;
-      float best = INFINITY;
-      int bi = 0x7fffffff;
-      for (int l = lane; l < Nc; l += 64) {
-        float d = 0.f;
-#pragma unroll
-        for (int i = 0; i < GS; ++i) {
-          const float df = e[i] - (float)c[l * GS + i];
-          d = fmaf(df, df, d);
-        }
-        if (d < best) {
-          best = d;
-          bi = l;
-        }
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float od = __shfl_xor(best, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (od < best || (od == best && oi < bi)) {
-          best = od;
-          bi = oi;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < GS; ++i) e[i] -= (float)c[bi * GS + i];
-      if (lane == 0) codes_l[r * G + j] = (uint8_t)bi;
-    }
+    greedy_group_wave<GS>(e, a.cb + ((int64_t)h * G + j) * R * Nc * GS, Nc, R, lane, codes_l + j, G);
   }
   __syncthreads();
   // byte k of the record collects record bits [8k, 8k + 8)

@@ -130,3 +130,18 @@ def test_decode_validation_without_launch():
     assert _raw_decode(k, cb(D=64), rope) == E.COMMVQ_ERR_INVALID_ARG
     assert _raw_decode(cb(g=6, D=96), cb(g=6, D=96), rope) == E.COMMVQ_ERR_UNSUPPORTED
     assert "workspace" in (_raw_decode(k, k, rope, ws_bytes=16) and _lib.commvq_last_error())
+
+
+def test_decode_step_validation_without_launch():
+    k, rope = cb(), _lib.make_rope(500000.0)
+    L = _lib.lib()
+
+    def step(k_new=FAKE, v_new=FAKE, positions=FAKE, ws_bytes=1 << 30):
+        return L.commvq_decode_step(ctypes.byref(k), ctypes.byref(k), ctypes.byref(rope), k_new, v_new, positions,
+                                    FAKE, FAKE, FAKE, FAKE, FAKE, 1, 32, 1024, 1024, 0.088, FAKE, FAKE, ws_bytes, 0,
+                                    None)
+    assert step(k_new=None) == _lib.COMMVQ_ERR_INVALID_ARG
+    assert step(v_new=None) == _lib.COMMVQ_ERR_INVALID_ARG
+    assert step(positions=None) == _lib.COMMVQ_ERR_INVALID_ARG
+    assert step(k_new=FAKE + 8) == _lib.COMMVQ_ERR_INVALID_ARG
+    assert step(ws_bytes=16) == _lib.COMMVQ_ERR_WORKSPACE

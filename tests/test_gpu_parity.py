@@ -250,3 +250,49 @@ def test_decode_rejects_bad_arguments():
         _lib.commvq_decode_attention(kq.desc, kq.desc, rope, q, pos, cache, cache, pos, 1, 3, 16, 16, 0.1, out,
                                      ws.buf, ws.nbytes)
     assert e.value.status == _lib.COMMVQ_ERR_UNSUPPORTED  # three query heads per KV head
+
+
+@pytest.mark.parametrize("R,exact", [(1, False), (2, False), (1, True), (2, True)])
+def test_decode_step_appends_then_attends(R, exact):
+    """One call appends the new token's codes and attends over the grown cache."""
+    B, Hq, Hkv, D, g, Nc, Lmax = 4, 8, 2, 128, 8, 256, 3000
+    G = D // g
+    lens = np.array([1, 2049, 2999, 1500], dtype=np.int32)        # lengths after the append
+    positions = np.array([0, 2048, 2998, Lmax], dtype=np.int32)   # last one: no append
+    rng = np.random.default_rng(500 + R)
+    kcb = synth.codebook(501, Hkv, D, g, Nc, R)
+    vcb = synth.codebook(502, Hkv, D, g, Nc, R)
+    kc = rng.integers(0, Nc, size=(B, Lmax, Hkv, R, G))
+    vc = rng.integers(0, Nc, size=(B, Lmax, Hkv, R, G))
+    kp, vp = _pack_cache(kc, Nc), _pack_cache(vc, Nc)
+    k_new = synth.kv(503, B, Hkv, D)
+    v_new = synth.kv(504, B, Hkv, D)
+    q = synth.queries(505, B, Hq, D)
+    # expected caches: the oracle's records of the new tokens at their positions
+    kexp, vexp = kp.copy(), vp.copy()
+    kn_codes, _ = O.encode(k_new, kcb)
+    vn_codes, _ = O.encode(v_new, vcb)
+    for b in range(B):
+        if 0 <= positions[b] < Lmax:
+            kexp[b, :, positions[b]] = O.pack_codes(kn_codes[b], Nc)
+            vexp[b, :, positions[b]] = O.pack_codes(vn_codes[b], Nc)
+    ref = O.decode_attention_from_packed(q, lens - 1, kexp, vexp, lens, kcb, vcb, 500000.0)
+    kq, vq = api.Quantizer(dev(kcb), g), api.Quantizer(dev(vcb), g)
+    kd, vd = dev(kp), dev(vp)
+    out = api.decode_step(kq, vq, dev(k_new), dev(v_new), dev(positions), dev(q), dev(lens - 1), kd, vd, dev(lens),
+                          Lmax, 500000.0, exact=exact)
+    torch.cuda.synchronize()
+    kgot, vgot = kd.cpu().numpy(), vd.cpu().numpy()
+    for b in range(B):
+        p = positions[b]
+        if 0 <= p < Lmax:
+            hard, _ = check_encoding(k_new[b][None], kcb, kgot[b, :, p][None], Nc)
+            assert not hard, (b, hard)
+            hard, _ = check_encoding(v_new[b][None], vcb, vgot[b, :, p][None], Nc)
+            assert not hard, (b, hard)
+            kgot[b, :, p] = kexp[b, :, p]
+            vgot[b, :, p] = vexp[b, :, p]
+    assert np.array_equal(kgot, kexp) and np.array_equal(vgot, vexp)  # nothing else written
+    err = row_errors(out.cpu().numpy().reshape(-1, D), ref.reshape(-1, D))
+    print(f"[decode step R{R} exact={exact}] max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= ATTN_TOL
