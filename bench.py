@@ -35,6 +35,28 @@ WORKLOAD = "llama8b_ctx128k_1bit_64steps"
 PREFILL = 131008
 N_POSITIONS = 64
 
+# HBM bytes per launch of the decode kernel from rocprofv3 counters (FETCH_SIZE
+# and WRITE_SIZE, each scaled by what the counter reads on a plain streaming
+# kernel of known size; profiles/decode_fast_llama8b_ctx128k_1bit.md), valid for
+# the kernel sources whose SHA-256 is given: any change to them voids it.
+KERNEL_SOURCES = ['decode_fast.hip', 'decode_common.hpp', 'encode_common.hpp', 'commvq_internal.hpp']
+TRAFFIC = {"sha256": "a38feac76ef76ab5660025be26838f5419064c64d77871b94a7adf8b0a69d831",
+           "read_bytes": 36352340, "write_bytes": 601897}
+
+
+def measured_traffic():
+    """Counter-measured HBM bytes per launch, or None once the kernel's sources
+    differ from the ones the counters were taken on."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "long_context_attention_commvq_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != TRAFFIC["sha256"]:
+        return None
+    return TRAFFIC["read_bytes"] + TRAFFIC["write_bytes"]
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -44,27 +66,51 @@ def parse():
     ap.add_argument("--layers", type=int, default=16, help="layer slices rotated over (caches > MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain streaming kernel (fp32 negate) over this many MiB, 5 times, and exit; "
+                         "its FETCH_SIZE/WRITE_SIZE counters calibrate the decode kernel's")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int):
+    """A plain streaming kernel of known size: reads and writes `mib` MiB once
+    per launch, so hardware byte counters taken over it give the factor between
+    counted and actual HBM bytes."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "fp32 negate", "bytes_read_per_launch": n * 4,
+                      "bytes_written_per_launch": n * 4, "launches": 5}), flush=True)
 
 
 def cpu_baseline(budget_s: float):
     """Time the fp64 oracle (unpack -> dequantise -> RoPE -> dense softmax) on
-    one KV head (its 4 query heads) of a step at full context, repeated over
-    heads until the budget is spent, scaled to the 8-head step."""
+    (KV head, decode position) units of the workload at full context: one unit
+    is one KV head with its 4 query heads at L = 131009 + t. Units are run until
+    the budget is spent (at least one step's 8 heads), then the mean unit time
+    is scaled to one 8-head step. BLAS may use every host core this process is
+    allowed (at most 16); the rest of NumPy runs on one thread."""
     from threadpoolctl import threadpool_limits
 
     from long_context_attention_commvq_amd import synth
     from oracle import commvq_oracle as O
 
     w = synth.WORKLOADS[WORKLOAD]
-    L = PREFILL + 1
     G = w.head_dim // w.group_size
     kcb = synth.codebook(w.seed + 1, 1, w.head_dim, w.group_size, w.n_entries, w.n_rounds)
     vcb = synth.codebook(w.seed + 2, 1, w.head_dim, w.group_size, w.n_entries, w.n_rounds)
     rep = w.n_q_heads // w.n_kv_heads
-    units, t_total = 0, 0.0
-    with threadpool_limits(limits=1):
-        while units < w.n_kv_heads and (units == 0 or t_total < budget_s):
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    units, t_total, toks = 0, 0.0, 0
+    with threadpool_limits(limits=cores):
+        while units < N_POSITIONS * w.n_kv_heads and (units < w.n_kv_heads or t_total < budget_s):
+            t = units // w.n_kv_heads
+            L = PREFILL + t + 1
             kc = synth.random_codes(w.seed + 100 + units, (L, 1, w.n_rounds, G), w.n_entries)
             vc = synth.random_codes(w.seed + 200 + units, (L, 1, w.n_rounds, G), w.n_entries)
             kp = O.pack_codes(kc, w.n_entries).transpose(1, 0, 2)[None]
@@ -74,21 +120,27 @@ def cpu_baseline(budget_s: float):
             O.decode_attention_from_packed(q, np.array([L - 1]), kp, vp, np.array([L]), kcb, vcb, w.theta_base)
             t_total += time.perf_counter() - t0
             units += 1
+            toks += L
     t_step = t_total / units * w.n_kv_heads
-    return {"value": L / t_step, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{units} of 8 KV heads (4 query heads each) at L={L}, fp64 NumPy, 1 thread; "
-                      f"{t_total:.1f} s measured, scaled x{w.n_kv_heads / units:.1f} to one 8-head step"}
+    L_mean = toks / units
+    return {"value": L_mean / t_step, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{units} (KV head, step) units of the {WORKLOAD} workload, mean L={L_mean:.0f}, "
+                      f"fp64 NumPy, BLAS threads={cores}; {t_total:.1f} s measured, "
+                      f"mean unit time scaled x{w.n_kv_heads} to one 8-head step"}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
-              "(the path shards by KV head or context chunk, see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the decode path would "
+              "shard by KV head or by context chunk, and no multi-GPU launcher is provided", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration_mib > 0:
+        copy_calibration(args.copy_calibration_mib)
+        return
     import torch
 
-    from long_context_attention_commvq_amd import api, synth
+    from long_context_attention_commvq_amd import _lib, api, synth
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -119,8 +171,8 @@ def main():
 
     # per-step inputs: new K/V token, query, device-side positions and lengths
     n_total = args.warmup + args.steps
-    knew = torch.from_numpy(synth.kv(w.seed + 30, n_total, H, D)).to(dev).reshape(n_total, 1, 1, H, D)
-    vnew = torch.from_numpy(synth.kv(w.seed + 31, n_total, H, D)).to(dev).reshape(n_total, 1, 1, H, D)
+    knew = torch.from_numpy(synth.kv(w.seed + 30, n_total, H, D)).to(dev).reshape(n_total, 1, H, D)
+    vnew = torch.from_numpy(synth.kv(w.seed + 31, n_total, H, D)).to(dev).reshape(n_total, 1, H, D)
     qs = torch.from_numpy(synth.queries(w.seed + 32, n_total, Hq, D)).to(dev).reshape(n_total, 1, Hq, D)
     positions = torch.arange(PREFILL, PREFILL + N_POSITIONS, dtype=torch.int32, device=dev).reshape(-1, 1)
     lens = positions + 1
@@ -130,18 +182,24 @@ def main():
     def layer_and_pos(i):
         return i % NL, (i // NL) % N_POSITIONS
 
+    # Each step is one commvq_decode_step call (append the new token's K and V codes
+    # at position t, then attend over [0, t]). Its arguments are marshalled once,
+    # before timing, so the timed loop issues launches back to back.
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-
-    def run_step(i, timed_idx=None):
+    sid = stream.cuda_stream
+    rope = _lib.make_rope(w.theta_base)
+    sm_scale = 1.0 / math.sqrt(D)
+    n_total = args.warmup + args.steps
+    calls = []
+    for i in range(n_total):
         li, t = layer_and_pos(i)
-        if timed_idx is not None:
-            ev[timed_idx][0].record(stream)
-        # append the new token's K and V codes at position t, then attend over [0, t]
-        api.decode_step(kq, vq, knew[i][0], vnew[i][0], positions[t], qs[i], positions[t], kcaches[li], vcaches[li],
-                        lens[t], Lmax, w.theta_base, out=out, workspace=ws)
-        if timed_idx is not None:
-            ev[timed_idx][1].record(stream)
+        calls.append((knew[i].data_ptr(), vnew[i].data_ptr(), positions[t].data_ptr(), qs[i].data_ptr(),
+                      positions[t].data_ptr(), kcaches[li].data_ptr(), vcaches[li].data_ptr(), lens[t].data_ptr()))
+
+    def run_step(i):
+        kn, vn, pos, q, qp, kc, vc, ln = calls[i]
+        _lib.commvq_decode_step(kq.desc, vq.desc, rope, kn, vn, pos, q, qp, kc, vc, ln, B, Hq, Lmax, Lmax, sm_scale,
+                                out, ws.buf, ws.nbytes, 0, sid)
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -153,14 +211,15 @@ def main():
     t_wall = time.perf_counter()
     start.record(stream)
     for k in range(args.steps):
-        run_step(args.warmup + k, timed_idx=k)
+        run_step(args.warmup + k)
     stop.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
-    dec_ms = [a.elapsed_time(b) for a, b in ev]
-    dec_avg_ms = float(np.mean(dec_ms))
+    # one step is exactly one kernel launch on `stream` (the fused append +
+    # attention kernel), so the launch average is the timed region over K
+    dec_avg_ms = ms_step
     # cached tokens per step and packed-code bytes per decode launch
     toks, code_bytes = 0, 0
     for k in range(args.steps):
@@ -171,8 +230,7 @@ def main():
     toks_per_step = toks / args.steps
     bytes_per_launch = code_bytes / args.steps
     achieved = bytes_per_launch / (dec_avg_ms * 1e-3) / 1e9
-    print(f"[bench] step {ms_step * 1e3:.1f} us, decode kernel {dec_avg_ms * 1e3:.1f} us "
-          f"(median {np.median(dec_ms) * 1e3:.1f}), wall {t_wall / args.steps * 1e6:.1f} us/step",
+    print(f"[bench] step {ms_step * 1e3:.1f} us (one launch each), host issue {t_wall / args.steps * 1e6:.1f} us/step",
           file=sys.stderr, flush=True)
 
     cpu = None
@@ -198,7 +256,7 @@ def main():
                    "n_rounds": w.n_rounds, "bits_per_scalar": w.n_rounds * math.log2(w.n_entries) / w.group_size,
                    "layer_slices": NL, "step": "commvq_decode_step: encode+append K and V of 1 token (8 KV heads), then attention"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(), "traffic_unit": "bytes per launch",
                      "kernel": "decode step (fused append + attention)", "bytes_per_launch": bytes_per_launch,
                      "avg_launch_us": dec_avg_ms * 1e3},
         "cpu_baseline": cpu,

@@ -68,7 +68,7 @@ typedef struct commvq_codebook {
   int32_t group_size;  /* g scalars sharing one index: even, divides D, 2..16 */
   int32_t n_entries;   /* Nc': power of two, 2..256 */
   int32_t n_rounds;    /* R: 1..4 */
-  int32_t n_kv_heads;  /* Hkv >= 1 */
+  int32_t n_kv_heads;  /* 1 <= Hkv <= 65535 (larger: COMMVQ_ERR_UNSUPPORTED) */
   int32_t dtype;       /* COMMVQ_F16 */
   const void* entries; /* device fp16 [Hkv][D/g][R][Nc'][g]; within a group the
                           scalars are the interleaved (x, y) pairs */
@@ -140,7 +140,9 @@ int32_t commvq_append(const commvq_codebook* cb, const void* x, int32_t batch,
  *            Lengths are clamped to [0, max_seq_len]; a length of 0 gives a
  *            zero output row.
  *   n_q_heads must be a multiple of Hkv; query head hq reads KV head
- *   hq / (n_q_heads / Hkv).
+ *   hq / (n_q_heads / Hkv). n_q_heads / Hkv must be 1, 2, 4 or 8, group_size
+ *   2, 4, 8 or 16, batch <= 65535 and ceil(max_seq_len / 1024) * Hkv < 2^31
+ *   (otherwise COMMVQ_ERR_UNSUPPORTED).
  *   sm_scale multiplies q.k (normally 1/sqrt(D)).
  *   out      device fp32 [batch][n_q_heads][D]
  *   workspace device, >= commvq_decode_workspace_bytes(batch, n_q_heads,

@@ -2,6 +2,7 @@
 // Validation runs entirely on the host before any HIP call, so every error path
 // is testable without a GPU.
 
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -44,6 +45,7 @@ int32_t check_shape(const commvq_codebook* cb, const char* name, commvq::CbShape
     return fail(COMMVQ_ERR_INVALID_ARG, "%s: n_entries %d must be a power of two in [2, 256]", name, Nc);
   if (R < 1 || R > 4) return fail(COMMVQ_ERR_INVALID_ARG, "%s: n_rounds %d must be in [1, 4]", name, R);
   if (cb->n_kv_heads < 1) return fail(COMMVQ_ERR_INVALID_ARG, "%s: n_kv_heads %d < 1", name, cb->n_kv_heads);
+  if (cb->n_kv_heads > 65535) return fail(COMMVQ_ERR_UNSUPPORTED, "%s: n_kv_heads %d > 65535", name, cb->n_kv_heads);
   if (cb->dtype != COMMVQ_F16) return fail(COMMVQ_ERR_INVALID_ARG, "%s: dtype %d is not COMMVQ_F16", name, cb->dtype);
   if (out) {
     out->D = D;
@@ -86,6 +88,10 @@ int32_t decode_shapes(const commvq_codebook* kcb, const commvq_codebook* vcb, in
   if (NH != 1 && NH != 2 && NH != 4 && NH != 8)
     return fail(COMMVQ_ERR_UNSUPPORTED, "query heads per KV head %d not in {1, 2, 4, 8}", NH);
   if (max_seq_len < 1) return fail(COMMVQ_ERR_INVALID_ARG, "max_seq_len %d < 1", max_seq_len);
+  // launch grid: (context chunks x KV heads, batch); chunks are at least 1024 positions
+  if (batch > 65535) return fail(COMMVQ_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if ((int64_t)((max_seq_len + 1023) / 1024) * k->Hkv > INT32_MAX)
+    return fail(COMMVQ_ERR_UNSUPPORTED, "max_seq_len %d x n_kv_heads %d exceeds the launch grid", max_seq_len, k->Hkv);
   if (k->g != 2 && k->g != 4 && k->g != 8 && k->g != 16)
     return fail(COMMVQ_ERR_UNSUPPORTED, "decode supports group_size 2, 4, 8 or 16, not %d", k->g);
   return COMMVQ_OK;
@@ -112,6 +118,26 @@ void phase_table(double base, int D, commvq::PhaseTable* ph) {
     ph->lo[p] = (uint32_t)(F & 0xffffffffULL);
     ph->hi[p] = (uint32_t)(F >> 32);
   }
+}
+
+// The phase constants of one (theta_base, head_dim), kept per thread for the
+// next call with the same rotary base (one model reuses it every step).
+struct PhaseConsts {
+  double base = 0.0;
+  int D = 0;
+  commvq::PhaseTable ph;
+  commvq::FastPhase fp;
+};
+
+const PhaseConsts& phase_consts(double base, int D) {
+  thread_local PhaseConsts c;
+  if (c.base != base || c.D != D) {
+    phase_table(base, D, &c.ph);
+    fast_phase(base, D, &c.fp);
+    c.base = base;
+    c.D = D;
+  }
+  return c;
 }
 
 }  // namespace
@@ -293,8 +319,7 @@ int32_t decode_impl(const commvq_codebook* kcb, const commvq_codebook* vcb, cons
   a.sm_scale = sm_scale;
   a.k = k;
   a.v = v;
-  commvq::PhaseTable ph;
-  phase_table(rope->theta_base, k.D, &ph);
+  const PhaseConsts& pc = phase_consts(rope->theta_base, k.D);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool fast = commvq::decode_fast_path(k, v, a.NH, (int)flags);
   hipError_t e = hipSuccess;
@@ -324,11 +349,9 @@ int32_t decode_impl(const commvq_codebook* kcb, const commvq_codebook* vcb, cons
   }
   if (e == hipSuccess) {
     if (fast) {
-      commvq::FastPhase fp;
-      fast_phase(rope->theta_base, k.D, &fp);
-      e = commvq::launch_decode_fast(a, ph, fp, s);
+      e = commvq::launch_decode_fast(a, pc.ph, pc.fp, s);
     } else {
-      e = commvq::launch_decode_generic(a, ph, s);
+      e = commvq::launch_decode_generic(a, pc.ph, s);
     }
   }
   return hip_status(e, step ? "commvq_decode_step launch" : "commvq_decode_attention launch");

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace commvq {
 
 constexpr int kMaxPairs = 128;  // D <= 256
@@ -66,6 +68,19 @@ struct FastPhase {
 
 // Chunk length (tokens per workgroup) chosen for a decode shape; the workspace
 // query and the launch use the same rule.
+// Raises a kernel's dynamic-LDS limit to the whole 160 KiB of a CU, once per
+// device: `done` is a per-kernel bit set of the devices already configured.
+inline hipError_t allow_full_lds(const void* kernel, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t(1) << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
+
 int decode_chunk_len(const CbShape& k, const CbShape& v, int B, int Hq, int max_len, int flags);
 bool decode_fast_path(const CbShape& k, const CbShape& v, int NH, int flags);
 size_t decode_workspace_bytes(const CbShape& k, int B, int Hq, int max_len, int chunk);

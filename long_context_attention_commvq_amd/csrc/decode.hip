@@ -46,7 +46,8 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, 
   float* sm = reinterpret_cast<float*>(dec_smem4);
   const CbShape K = a.k, V = a.v;
   const int D = K.D, P = D / 2, G = K.G;
-  const int chunk_id = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  // KV head fastest in launch order: one head's chunks share an XCD's L2 (8 heads)
+  const int h = blockIdx.x % a.k.Hkv, chunk_id = blockIdx.x / a.k.Hkv, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int L = min(max(a.seq_lens[b], 0), a.max_len);
   const int m0 = chunk_id * a.chunk;
@@ -216,10 +217,10 @@ hipError_t launch_generic(const DecodeArgs& a, const PhaseTable& ph, hipStream_t
   size_t smem = (2 * NH * P + NH * a.k.D + ((NH * (NW > 2 ? NW : 2) + 2 * NH + 4) & ~3)) * sizeof(float) +
                 (table_bytes > hist_bytes ? table_bytes : hist_bytes);
   if (smem > 160 * 1024) return hipErrorInvalidValue;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_generic_kernel<NH, GS>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  static std::atomic<uint64_t> configured{0};
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&decode_generic_kernel<NH, GS>), configured);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_generic_kernel<NH, GS>), dim3(a.n_chunks, a.k.Hkv, a.B), dim3(kThreads), smem, stream,
+  hipLaunchKernelGGL((decode_generic_kernel<NH, GS>), dim3(a.n_chunks * a.k.Hkv, a.B), dim3(kThreads), smem, stream,
                      a, ph);
   return hipGetLastError();
 }

@@ -106,7 +106,10 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   float* new_v = new_s + FNH;                                        // [128]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // Workgroups are handed to the 8 XCDs round-robin in launch order; putting the
+  // KV head in the fastest-varying position keeps one head's chunks (and its
+  // codebooks) on one XCD's L2 when there are 8 KV heads.
+  const int h = blockIdx.x % a.k.Hkv, chunk = blockIdx.x / a.k.Hkv, b = blockIdx.y;
   const int L = min(max(a.seq_lens[b], 0), a.max_len);
   const int m0 = chunk * C;
   const size_t pstride = (size_t)a.n_chunks * (FD + 2);
@@ -542,10 +545,10 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
 template <int R, int TL, bool HROT>
 hipError_t launch_fast_t(const DecodeArgs& a, const PhaseTable& ph, const FastPhase& fp, hipStream_t stream) {
   const size_t smem = FastCfg<R>::TAB + AUX_BYTES;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_fast_kernel<R, TL, HROT>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  static std::atomic<uint64_t> configured{0};
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&decode_fast_kernel<R, TL, HROT>), configured);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_fast_kernel<R, TL, HROT>), dim3(a.n_chunks, a.k.Hkv, a.B), dim3(FT), smem, stream, a,
+  hipLaunchKernelGGL((decode_fast_kernel<R, TL, HROT>), dim3(a.n_chunks * a.k.Hkv, a.B), dim3(FT), smem, stream, a,
                      ph, fp);
   return hipGetLastError();
 }

@@ -139,8 +139,8 @@ hipError_t launch_encode_g(const EncodeArgs& a, hipStream_t stream) {
   int tile = 256;
   while (tile > 64 && cb_bytes + (size_t)tile * s.R * s.G > 160 * 1024) tile /= 2;
   const size_t smem = cb_bytes + (size_t)tile * s.R * s.G;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&encode_kernel<GS>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  static std::atomic<uint64_t> configured{0};
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&encode_kernel<GS>), configured);
   if (e != hipSuccess) return e;
   const int64_t nblk = (a.n_tokens + tile - 1) / tile;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;

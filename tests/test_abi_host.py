@@ -129,6 +129,13 @@ def test_decode_validation_without_launch():
     assert _raw_decode(k, k, rope, out=None) == E.COMMVQ_ERR_INVALID_ARG
     assert _raw_decode(k, cb(D=64), rope) == E.COMMVQ_ERR_INVALID_ARG
     assert _raw_decode(cb(g=6, D=96), cb(g=6, D=96), rope) == E.COMMVQ_ERR_UNSUPPORTED
+    # launch-grid limits: batch on the grid's y axis, chunks x KV heads on x
+    assert _raw_decode(k, k, rope, B=65536) == E.COMMVQ_ERR_UNSUPPORTED
+    assert "batch" in _lib.commvq_last_error()
+    assert _raw_decode(cb(H=65536), cb(H=65536), rope, Hq=65536) == E.COMMVQ_ERR_UNSUPPORTED
+    big = 2**31 - 1
+    assert _raw_decode(cb(H=2048), cb(H=2048), rope, Hq=8192, cache_len=big, max_len=big) == E.COMMVQ_ERR_UNSUPPORTED
+    assert "launch grid" in _lib.commvq_last_error()
     assert "workspace" in (_raw_decode(k, k, rope, ws_bytes=16) and _lib.commvq_last_error())
 
 
