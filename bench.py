@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=16, help="layer slices rotated over (caches > MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--encode", action="store_true",
+                    help="time the prefill encoder instead (131072 tokens x 8 KV heads of K and V, 2-bit)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain streaming kernel (fp32 negate) over this many MiB, 5 times, and exit; "
                          "its FETCH_SIZE/WRITE_SIZE counters calibrate the decode kernel's")
@@ -129,6 +131,71 @@ def cpu_baseline(budget_s: float):
                       f"mean unit time scaled x{w.n_kv_heads} to one 8-head step"}
 
 
+VALU_PEAK_LANE_OPS = 256 * 64 * 2.4e9  # CUs x vector lanes per clock per CU x clock
+
+
+def bench_encode(args):
+    """Prefill encoder on the 128K heavy-tailed workload: one step = commvq_encode
+    of K then V (131072 tokens x 8 KV heads each), inputs resident in HBM."""
+    import torch
+
+    from long_context_attention_commvq_amd import _lib, api, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wname = "llama8b_encode128k_b4_2bit"
+    w = synth.WORKLOADS[wname]
+    N, H, D = w.context, w.n_kv_heads, w.head_dim
+    G = D // w.group_size
+    kq = api.Quantizer(torch.from_numpy(synth.codebook(w.seed + 1, H, D, w.group_size, w.n_entries, w.n_rounds)).to(dev),
+                       w.group_size)
+    vq = api.Quantizer(torch.from_numpy(synth.codebook(w.seed + 2, H, D, w.group_size, w.n_entries, w.n_rounds)).to(dev),
+                       w.group_size)
+    print(f"[bench] encode: generating {N} x {H} x {D} K and V", file=sys.stderr, flush=True)
+    kx = torch.from_numpy(synth.kv(w.seed + 10, N, H, D, heavy_tail=True)).to(dev)
+    vx = torch.from_numpy(synth.kv(w.seed + 11, N, H, D, heavy_tail=True)).to(dev)
+    bpt = kq.bytes_per_token
+    kc = torch.empty((N, H, bpt), dtype=torch.uint8, device=dev)
+    vc = torch.empty((N, H, bpt), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sid = stream.cuda_stream
+
+    def step():
+        _lib.commvq_encode(kq.desc, kx.data_ptr(), N, H * D, kc.data_ptr(), H * bpt, bpt, sid)
+        _lib.commvq_encode(vq.desc, vx.data_ptr(), N, H * D, vc.data_ptr(), H * bpt, bpt, sid)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    launch_s = ms_step * 1e-3 / 2  # two equal launches per step (K, V)
+    token_heads = N * H
+    candidates = token_heads * G * w.n_rounds * w.n_entries  # per launch
+    ops = 3 * candidates  # compare + two selects per candidate score
+    rec = {
+        "metric": "prefill encode token-heads/s (K and V, 131072 tokens x 8 KV heads, 2-bit)",
+        "value": 2 * token_heads / (ms_step * 1e-3),
+        "unit": "token-heads/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16 products, fp32 sums", "data": "synthetic",
+        "config": {"workload": wname, "tokens": N, "n_kv_heads": H, "head_dim": D, "group_size": w.group_size,
+                   "n_entries": w.n_entries, "n_rounds": w.n_rounds, "heavy_tail": True,
+                   "step": "commvq_encode of K then V"},
+        "roofline": {"bound": "alu", "achieved": ops / launch_s / 1e12, "peak": VALU_PEAK_LANE_OPS / 1e12,
+                     "unit": "T lane-ops/s", "frac": ops / launch_s / VALU_PEAK_LANE_OPS,
+                     "hbm_GBps": (N * H * D * 2 + N * H * bpt) / launch_s / 1e9,
+                     "avg_launch_us": launch_s * 1e6,
+                     "work": "3 vector ops per (token, head, group, round, entry) candidate score"},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -137,6 +204,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration_mib > 0:
         copy_calibration(args.copy_calibration_mib)
+        return
+    if args.encode:
+        bench_encode(args)
         return
     import torch
 

@@ -68,6 +68,75 @@ def test_encode_shapes(D, g, Nc, R, H, N):
     assert not hard, hard[:5]
 
 
+@pytest.mark.parametrize("R,H,N,heavy", [
+    (1, 8, 65, False),      # smallest count past the few-token kernel
+    (2, 3, 1000, False),    # 4 tiles of 256, ragged tail
+    (2, 8, 4097, True),     # heavy-tailed channels, 17 tiles
+    (1, 1, 513, True),
+])
+def test_encode_matrix_core_search(R, H, N, heavy):
+    """g = 8, Nc' = 256, R <= 2 with more than 64 tokens: the distance GEMM runs
+    on the matrix cores; codes must match the oracle's up to logged near-ties."""
+    seed = 9100 + 10 * R + H
+    x = synth.kv(seed, N, H, 128, heavy_tail=heavy)
+    cb = synth.codebook(seed + 1, H, 128, 8, 256, R)
+    got = gpu_encode(x, cb, 256)
+    hard, ties = check_encoding(x, cb, got, 256)
+    _report(f"encode mfma R{R} H{H} N{N} heavy={heavy}", hard, ties, N * H * R * 16)
+    assert not hard, hard[:5]
+
+
+def test_encode_matrix_core_unaligned_records_and_positions():
+    """Byte-granular record addresses and the positions (append) form with more
+    than 64 tokens both go through the matrix-core encoder."""
+    H, D, R, N = 2, 128, 2, 130
+    cb = synth.codebook(9201, H, D, 8, 256, R)
+    q = api.Quantizer(dev(cb), 8)
+    bpt = q.bytes_per_token
+    x = synth.kv(9202, N, H, D)
+    # records packed back to back from an odd byte offset
+    buf = torch.full((N * H * bpt + 1,), 0x5A, dtype=torch.uint8, device=DEV)
+    _lib.commvq_encode(q.desc, dev(x), N, H * D, buf.data_ptr() + 1, H * bpt, bpt)
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy()
+    assert b[0] == 0x5A
+    hard, _ = check_encoding(x, cb, b[1:].reshape(N, H, bpt), 256)
+    assert not hard, hard[:5]
+    # append N tokens (one per sequence) at scattered positions, some skipped
+    B, Lmax = N, 16
+    cache = torch.full((B, H, Lmax, bpt), 0xAB, dtype=torch.uint8, device=DEV)
+    pos = np.arange(B, dtype=np.int32) % (Lmax + 2) - 1  # -1 and Lmax are skipped
+    api.append(q, dev(x), dev(pos), cache)
+    torch.cuda.synchronize()
+    c = cache.cpu().numpy()
+    keep = (pos >= 0) & (pos < Lmax)
+    idx = np.nonzero(keep)[0]
+    got = np.stack([c[i, :, pos[i]] for i in idx])
+    hard, _ = check_encoding(x[idx], cb, got, 256)
+    assert not hard, hard[:5]
+    mask = np.ones(c.shape, dtype=bool)
+    for i in idx:
+        mask[i, :, pos[i]] = False
+    assert np.all(c[mask] == 0xAB)
+
+
+def test_encode_full_size_128k_sampled():
+    """The prefill-encode workload at full size (131072 tokens x 8 KV heads,
+    heavy-tailed, 2-bit): the GPU encodes everything, the oracle re-encodes a
+    seeded sample of 1536 tokens (every head) plus the first and last tiles'
+    edges."""
+    w = synth.WORKLOADS["llama8b_encode128k_b4_2bit"]
+    N, H, D = w.context, w.n_kv_heads, w.head_dim
+    x = synth.kv(w.seed + 10, N, H, D, heavy_tail=True)
+    cb = synth.codebook(w.seed + 1, H, D, w.group_size, w.n_entries, w.n_rounds)
+    got = gpu_encode(x, cb, w.n_entries)
+    rng = np.random.default_rng(w.seed + 77)
+    sample = np.unique(np.concatenate([rng.choice(N, 1536, replace=False), [0, 1, 255, 256, N - 257, N - 1]]))
+    hard, ties = check_encoding(x[sample], cb, got[sample], w.n_entries)
+    _report("encode 128K x 8 sampled", hard, ties, len(sample) * H * w.n_rounds * 16)
+    assert not hard, hard[:5]
+
+
 def test_encode_into_cache_strides_and_append():
     H, D, g, Nc, R, B, Lmax = 2, 64, 8, 256, 2, 3, 40
     cb = synth.codebook(71, H, D, g, Nc, R)
