@@ -1,0 +1,132 @@
+"""GPU parity at the workloads' full sizes, through the C ABI, in the launch
+configuration the benchmark uses (every KV head and chunk of the real shape
+launched at once). The oracle recomputes a seeded sample of (sequence, KV head)
+units, each over its whole context; attention rows must match within 2e-3 of
+their max |ref|, appended records bit-exactly (near ties excepted).
+
+Packed caches are drawn as seeded random bytes: with 256-entry codebooks every
+field is one byte, so any byte string is a valid record."""
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_attention_commvq_amd import api, synth
+from oracle import commvq_oracle as O
+from tests.parity import ATTN_TOL, check_encoding, row_errors
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def random_cache(seed, B, H, Lmax, bpt):
+    return np.random.default_rng(seed).integers(0, 256, size=(B, H, Lmax, bpt), dtype=np.uint8)
+
+
+def oracle_unit(q, kp, vp, kcb, vcb, b, h, L, qpos, theta, rep):
+    """The oracle's output rows of KV head h of sequence b (its `rep` query heads)."""
+    return O.decode_attention_from_packed(
+        q[b:b + 1, h * rep:(h + 1) * rep], np.array([qpos]), kp[b:b + 1, h:h + 1, :L], vp[b:b + 1, h:h + 1, :L],
+        np.array([L]), kcb[h:h + 1], vcb[h:h + 1], theta)[0]
+
+
+def run_workload(name, units, lens=None, seed_shift=0):
+    w = synth.WORKLOADS[name]
+    B, Hq, H, D, Lmax = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.context
+    rep = Hq // H
+    print(f"[full-size {name}] B={B} Hq={Hq} Hkv={H} Lmax={Lmax} R={w.n_rounds}", flush=True)
+    kcb = synth.codebook(w.seed + 1, H, D, w.group_size, w.n_entries, w.n_rounds)
+    vcb = synth.codebook(w.seed + 2, H, D, w.group_size, w.n_entries, w.n_rounds)
+    kq, vq = api.Quantizer(dev(kcb), w.group_size), api.Quantizer(dev(vcb), w.group_size)
+    bpt = kq.bytes_per_token
+    kp = random_cache(w.seed + 40 + seed_shift, B, H, Lmax, bpt)
+    vp = random_cache(w.seed + 41 + seed_shift, B, H, Lmax, bpt)
+    q = synth.queries(w.seed + 42 + seed_shift, B, Hq, D)
+    if lens is None:
+        lens = np.full(B, Lmax, dtype=np.int32)
+    lens = np.asarray(lens, dtype=np.int32)
+    qpos = lens - 1
+    out = api.decode_attention(kq, vq, dev(q), dev(qpos), dev(kp), dev(vp), dev(lens), Lmax, w.theta_base)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    worst = 0.0
+    for b, h in units:
+        ref = oracle_unit(q, kp, vp, kcb, vcb, b, h, int(lens[b]), int(qpos[b]), w.theta_base, rep)
+        err = row_errors(got[b, h * rep:(h + 1) * rep], ref)
+        worst = max(worst, float(err.max()))
+        assert err.max() <= ATTN_TOL, (b, h, err)
+    print(f"[full-size {name}] {len(units)} units, max row rel err {worst:.3e}", flush=True)
+
+
+def test_full_size_32k_2bit_all_heads():
+    run_workload("llama8b_ctx32k_2bit", [(0, h) for h in range(8)])
+
+
+def test_full_size_b16_ragged_32k_2bit_sampled():
+    w = synth.WORKLOADS["llama8b_b16_ctx32k_ragged_2bit"]
+    lens = synth.ragged_lengths(w.seed + 5, w.batch, *w.ragged)
+    rng = np.random.default_rng(w.seed + 6)
+    units = [(int(b), int(rng.integers(0, w.n_kv_heads))) for b in rng.choice(w.batch, 10, replace=False)]
+    units += [(int(np.argmin(lens)), 0), (int(np.argmax(lens)), 7)]
+    run_workload("llama8b_b16_ctx32k_ragged_2bit", units, lens=lens)
+
+
+def test_full_size_b4_128k_2bit_sampled():
+    rng = np.random.default_rng(5077)
+    units = [(b, int(rng.integers(0, 8))) for b in range(4)] + [(3, 7)]
+    run_workload("llama8b_encode128k_b4_2bit", units)
+
+
+def test_full_size_128k_1bit_decode_steps():
+    """The benchmark's step at full size: a cache of 131008 tokens, then fused
+    append + attention calls at the first, a middle and the last of the 64
+    positions. The appended K/V records must equal the oracle's encoding and the
+    attention output the oracle's over the updated cache."""
+    w = synth.WORKLOADS["llama8b_ctx128k_1bit_64steps"]
+    B, Hq, H, D, Lmax = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.context
+    rep = Hq // H
+    prefill = Lmax - 64
+    kcb = synth.codebook(w.seed + 1, H, D, w.group_size, w.n_entries, w.n_rounds)
+    vcb = synth.codebook(w.seed + 2, H, D, w.group_size, w.n_entries, w.n_rounds)
+    kq, vq = api.Quantizer(dev(kcb), w.group_size), api.Quantizer(dev(vcb), w.group_size)
+    bpt = kq.bytes_per_token
+    kp = random_cache(w.seed + 50, B, H, Lmax, bpt)
+    vp = random_cache(w.seed + 51, B, H, Lmax, bpt)
+    kp[:, :, prefill:] = 0
+    vp[:, :, prefill:] = 0
+    kd, vd = dev(kp), dev(vp)
+    ws = api.DecodeWorkspace(kq, vq, B, Hq, Lmax, DEV)
+    rng = np.random.default_rng(w.seed + 52)
+    for t in (0, 31, 63):
+        pos = prefill + t
+        print(f"[full-size 128K step] position {pos}", flush=True)
+        kn = synth.kv(w.seed + 60 + t, 1, H, D)
+        vn = synth.kv(w.seed + 61 + t, 1, H, D)
+        q = synth.queries(w.seed + 62 + t, B, Hq, D)
+        p = np.array([pos], dtype=np.int32)
+        out = api.decode_step(kq, vq, dev(kn), dev(vn), dev(p), dev(q), dev(p), kd, vd, dev(p + 1), Lmax,
+                              w.theta_base, workspace=ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        # the appended records
+        kg = kd[0, :, pos].cpu().numpy()[None]
+        vg = vd[0, :, pos].cpu().numpy()[None]
+        hard, _ = check_encoding(kn, kcb, kg, w.n_entries)
+        assert not hard, hard[:5]
+        hard, _ = check_encoding(vn, vcb, vg, w.n_entries)
+        assert not hard, hard[:5]
+        # the oracle's own encoding of the new token goes into its copy of the cache
+        kc, _ = O.encode(kn, kcb)
+        vc, _ = O.encode(vn, vcb)
+        kp[0, :, pos] = O.pack_codes(kc, w.n_entries)[0]
+        vp[0, :, pos] = O.pack_codes(vc, w.n_entries)[0]
+        for h in sorted(set([int(rng.integers(0, H)), int(rng.integers(0, H))])):
+            ref = oracle_unit(q, kp, vp, kcb, vcb, 0, h, pos + 1, pos, w.theta_base, rep)
+            err = row_errors(got[0, h * rep:(h + 1) * rep], ref)
+            print(f"[full-size 128K step] position {pos} head {h} max row rel err {err.max():.3e}", flush=True)
+            assert err.max() <= ATTN_TOL, (pos, h, err)
