@@ -97,14 +97,6 @@ int32_t decode_shapes(const commvq_codebook* kcb, const commvq_codebook* vcb, in
   return COMMVQ_OK;
 }
 
-void fast_phase(double base, int D, commvq::FastPhase* fp) {
-  // e^{i 512 theta_p} per pair (a fast-kernel lane steps 512 positions)
-  for (int p = 0; p < D / 2 && p < commvq::kMaxPairs / 2; ++p) {
-    const long double theta = powl((long double)base, -2.0L * p / D);
-    fp->step_c[p] = (float)cosl(512.0L * theta);
-    fp->step_s[p] = (float)sinl(512.0L * theta);
-  }
-}
 
 void phase_table(double base, int D, commvq::PhaseTable* ph) {
   // F_p = frac(theta_p / 2pi) * 2^64 with theta_p = base^(-2p/D), in long double.
@@ -126,14 +118,12 @@ struct PhaseConsts {
   double base = 0.0;
   int D = 0;
   commvq::PhaseTable ph;
-  commvq::FastPhase fp;
 };
 
 const PhaseConsts& phase_consts(double base, int D) {
   thread_local PhaseConsts c;
   if (c.base != base || c.D != D) {
     phase_table(base, D, &c.ph);
-    fast_phase(base, D, &c.fp);
     c.base = base;
     c.D = D;
   }
@@ -349,7 +339,7 @@ int32_t decode_impl(const commvq_codebook* kcb, const commvq_codebook* vcb, cons
   }
   if (e == hipSuccess) {
     if (fast) {
-      e = commvq::launch_decode_fast(a, pc.ph, pc.fp, s);
+      e = commvq::launch_decode_fast(a, pc.ph, s);
     } else {
       e = commvq::launch_decode_generic(a, pc.ph, s);
     }

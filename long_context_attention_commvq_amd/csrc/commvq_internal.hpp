@@ -61,10 +61,6 @@ struct DecodeArgs {
 
 // Step multipliers of the fast decode kernel: a lane advances by 512 positions
 // per owned position, so its phase is multiplied by e^{i 512 theta_p}.
-struct FastPhase {
-  float step_c[kMaxPairs / 2];
-  float step_s[kMaxPairs / 2];
-};
 
 // Chunk length (tokens per workgroup) chosen for a decode shape; the workspace
 // query and the launch use the same rule.
@@ -84,7 +80,7 @@ inline hipError_t allow_full_lds(const void* kernel, std::atomic<uint64_t>& done
 int decode_chunk_len(const CbShape& k, const CbShape& v, int B, int Hq, int max_len, int flags);
 bool decode_fast_path(const CbShape& k, const CbShape& v, int NH, int flags);
 size_t decode_workspace_bytes(const CbShape& k, int B, int Hq, int max_len, int chunk);
-hipError_t launch_decode_fast(const DecodeArgs& a, const PhaseTable& ph, const FastPhase& fp, hipStream_t stream);
+hipError_t launch_decode_fast(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream);
 
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_generic(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream);

@@ -3,32 +3,37 @@
 // LLaMA-3.1-8B layer shape).
 //
 // One workgroup (512 lanes, two wavefronts per SIMD) owns a chunk of C = 512*TL
-// cached positions of one (sequence, KV head); lane `tid` owns positions
-// m0 + tid + 512 t, t < TL.
+// cached positions of one (sequence, KV head). Wavefront w handles blocks of 64
+// consecutive positions m_b = m0 + 512 t + 64 w (t < TL), lane d taking m_b + d.
 //
 // Scores ("Pith review of CommVQ", "What carries the argument": the commuting
-// codebook lets query- and codebook-dependent factors be computed once and
-// reused for every cached position):
-//   T[a][j][r][l][p] = conj(q~_{a,p}) * z_{j,r,l,p} is built in LDS as fp16
-//   (T_re, -T_im) pairs, in slices of J groups (the whole table does not fit).
-//   A position adds dot2(T[code], (cos, sin)(m theta_p)) for every pair - a code
-//   gather, a phase multiply-accumulate and a reduction, with fp32 accumulation.
-//   Lanes visit the J groups of a slice in a lane-rotated order, so the 16-byte
-//   gathers of neighbouring lanes fall in different LDS bank groups; each lane's
-//   code bytes and phases are kept in that rotated order. Gathers are issued one
-//   slot ahead of the multiply-accumulates that consume them.
-//   Phases follow an fp32 recurrence over the lane's positions (step 512) that
-//   starts from the product of two exactly computed phases (64-bit fixed point);
-//   a lane keeps the state of four groups (16 pairs) at a time.
+// codebook lets the query-dependent factor be formed once and reused for every
+// cached position). With the phase split e^{i m theta} = e^{i m_b theta} e^{i d theta},
+//   s = Re sum_p conj(q~_p e^{-i m_b theta_p}) (z_p e^{i d theta_p}),
+// a real dot product over D between
+//   q'_p = q~_p conj(e^{i m_b theta_p})   built once per block (fp16), and
+//   k'_p = z_p e^{i d theta_p}           one codebook gather per group and a
+//                                        rotation by lane-constant phases.
+// No per-position phase is computed: block phases advance once per block, and
+// the lane phases e^{i d theta_p}, d < 64, are constants. The dot products run
+// on v_mfma_f32_4x4x4f16: block b of 16 takes positions 4b..4b+3 of the 64 as
+// columns and the four query heads as rows, so lane d ends with its position's
+// four scores; q' is broadcast from one block per instruction (CBSZ/ABID), so a
+// lane holds it for two K-steps only. The key codebook of the head sits in LDS (64 KiB per
+// round); k' is rotated in packed fp16 (v_pk_mul_f16 + v_pk_fma_f16).
 // Values (review, "If this is right", fourth bullet: weights applied to the
 // value codes before the codebook):
 //   fixed-point weights are scattered into per-(round, code, group, head)
-//   histograms with LDS integer atomics; lanes rotate over (group, head) so the
-//   64 lanes of an atomic hit 64 different banks. The histogram is contracted
-//   with the value codebook on MFMA (v_mfma_f32_4x4x4f16, 16 blocks = 8 groups x
-//   2 dim quads, weights split into fp16 hi + lo parts).
+//   histograms with 64-bit LDS integer atomics (two heads per add); lanes
+//   rotate over (group, head pair) to spread the adds over the banks. The
+//   histogram is contracted with the value codebook on MFMA
+//   (v_mfma_f32_4x4x4f16, 16 blocks = 8 groups x 2 dim quads, weights split into
+//   fp16 hi + lo parts).
 // The chunk's (max, sum, o) go to the workspace and the last workgroup of the
 // (sequence, KV head) merges the chunks.
+
+#include <type_traits>
+#include <utility>
 
 #include "decode_common.hpp"
 #include "encode_common.hpp"
@@ -43,63 +48,79 @@ constexpr int FD = 128;     // head_dim
 constexpr int FG = 16;      // groups of g = 8
 constexpr int FPR = 64;     // RoPE pairs
 constexpr int FNC = 256;    // entries per codebook
-constexpr int HI_N = FT / 16;  // first-position phase table: tid = 16 hi + lo
 
 template <int R>
 struct FastCfg {
-  static constexpr int J = 8 / R;                      // groups per table slice
-  static constexpr int NPASS = FG / J;                 // table slices
   static constexpr int BPT = 16 * R;                   // bytes per packed record
-  static constexpr int ROW = FNH * J * 16;             // bytes per (round, code) row of a slice
-  static constexpr int TAB = R * FNC * ROW;            // slice bytes (128 KiB)
+  static constexpr int KCB = R * FG * FNC * 16;        // key codebook bytes (64 KiB per round)
   static constexpr int HIST = R * FNC * FG * FNH * 4;  // histogram bytes (64 KiB per round)
-  static_assert(TAB == 131072 && HIST <= TAB, "layout");
+  static constexpr int MAIN = 131072;                  // LDS region holding one, then the other
+  static_assert(KCB <= MAIN && HIST <= MAIN, "layout");
 };
 
-// aux LDS: phase tables [64][HI_N] + [64][16], step multipliers [64], rotated
-// query [4][64], reductions [64], MFMA staging [2][64][4], flag, and a decode
-// step's new token: codes [2][2][16], scores [4], value [128]
-constexpr int EHI_BYTES = FPR * HI_N * 8;
-constexpr int ELO_BYTES = FPR * 16 * 8;
+// aux LDS: lane phases [64 offsets][64 pairs] fp16 (16-byte chunks swizzled),
+// rotated query [4][64], reductions [64], MFMA staging [2][64][4], flag, and a
+// decode step's new token: codes [2][2][16], scores [4], value [128]
+constexpr int PHT_BYTES = 64 * FPR * 4;
 constexpr int NEW_BYTES = 64 + FNH * 4 + FD * 4;
-constexpr int AUX_BYTES = EHI_BYTES + ELO_BYTES + FPR * 8 + FNH * FPR * 8 + 64 * 4 + 2 * 64 * 4 * 4 + 16 + NEW_BYTES;
+constexpr int AUX_BYTES = PHT_BYTES + FNH * FPR * 8 + 64 * 4 + 2 * 64 * 4 * 4 + 16 + NEW_BYTES;
 static_assert(131072 + AUX_BYTES <= 160 * 1024, "LDS budget");
-static_assert(EHI_BYTES >= 4 * 4096, "value-codebook slabs reuse the phase table");
+static_assert(PHT_BYTES >= 4 * 4096, "value-codebook slabs reuse the lane phase table");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
   typedef float f2v __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){lo, hi}, half2_t));
 }
 
-__device__ __forceinline__ float sel4(float v0, float v1, float v2, float v3, int i) {
-  const float a = (i & 1) ? v1 : v0;
-  const float b = (i & 1) ? v3 : v2;
-  return (i & 2) ? b : a;
+// (x + iy)(c + is) on packed fp16 pairs z = (x, y), e = (c, s): t = (x c, y c),
+// then (x c - y s, y c + x s); the compiler folds the swaps and the negation into
+// operand selects of one v_pk_mul_f16 and one v_pk_fma_f16.
+__device__ __forceinline__ uint32_t rotate_h2(uint32_t z, uint32_t e) {
+  const half2_t zz = __builtin_bit_cast(half2_t, z), ee = __builtin_bit_cast(half2_t, e);
+  const half2_t t = zz * (half2_t){ee.x, ee.x};
+  const half2_t zs = {-zz.y, zz.x};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(zs, (half2_t){ee.y, ee.y}, t));
 }
 
-template <int R, int TL, bool HROT>
-__global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseTable ph, FastPhase fp) {
+// Packed fp16 sum of two (x, y) pairs. Elements of a 32-bit vector are passed
+// to it by value: a bit cast applied directly to a vector element expression has
+// been seen to read element 0 whatever the index.
+__device__ __forceinline__ uint32_t add_h2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) + __builtin_bit_cast(half2_t, b));
+}
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, each i a compile-time
+// constant (MFMA broadcast selectors must be immediates)
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__device__ __forceinline__ half4_t as_h4(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(half4_t, (u32x2){lo, hi});
+}
+
+template <int R, int TL>
+__global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseTable ph) {
   using Cfg = FastCfg<R>;
-  constexpr int J = Cfg::J, NPASS = Cfg::NPASS, BPT = Cfg::BPT, ROW = Cfg::ROW;
-  constexpr int ROWSH = (J == 8) ? 9 : 8;  // log2(ROW)
+  constexpr int BPT = Cfg::BPT;
   constexpr int C = FT * TL;
   constexpr int FXSHIFT = 31 - (C == 4096 ? 12 : C == 2048 ? 11 : 10);  // C * 2^FXSHIFT = 2^31
-  constexpr int KH = 4;                   // slots whose phases a lane holds at once
-  constexpr int NHALF = J / KH;
-  static_assert(ROW == (1 << ROWSH) && C <= 4096, "shape");
+  static_assert(C <= 4096, "shape");
 
   extern __shared__ uint4 fsm[];
   char* lds = reinterpret_cast<char*>(fsm);
-  float2* ehi = reinterpret_cast<float2*>(lds + Cfg::TAB);  // [64][HI_N] e^{i (m0 + 16 u) theta_p}
-  float2* elo = ehi + FPR * HI_N;                            // [64][16] e^{i u theta_p}
-  float2* stp = elo + FPR * 16;                              // [64] e^{i 512 theta_p}
-  float2* qz = stp + FPR;                                    // [4][64] rotated query
-  float* red = reinterpret_cast<float*>(qz + FNH * FPR);     // [64] reductions
-  float* stage = red + 64;                                   // [2][64][4] MFMA partials
+  uint32_t* pht = reinterpret_cast<uint32_t*>(lds + Cfg::MAIN);       // [64][64] fp16 (cos, sin)
+  float2* qz = reinterpret_cast<float2*>(lds + Cfg::MAIN + PHT_BYTES);  // [4][64] rotated query
+  float* red = reinterpret_cast<float*>(qz + FNH * FPR);               // [64] reductions
+  float* stage = red + 64;                                             // [2][64][4] MFMA partials
   uint32_t* flag = reinterpret_cast<uint32_t*>(stage + 2 * 64 * 4);
   uint8_t* new_codes = reinterpret_cast<uint8_t*>(flag + 4);         // [2][R][16]
   float* new_s = reinterpret_cast<float*>(new_codes + 64);           // [4] scaled scores
@@ -142,51 +163,42 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
       const int hh = i / (FD + 2), k = i % (FD + 2);
       part[hh * pstride + k] = (k == 0) ? -INFINITY : 0.f;
     }
-    merge_if_last<FT>(a, b, h, FNH, FD, flag, reinterpret_cast<float*>(lds), Cfg::TAB / 4);
+    merge_if_last<FT>(a, b, h, FNH, FD, flag, reinterpret_cast<float*>(lds), Cfg::MAIN / 4);
     return;
   }
 
-  const int gr = tid & (J - 1);                 // group rotation of this lane
   const uint8_t* kb = a.kcodes + ((size_t)b * a.k.Hkv + h) * (size_t)a.cache_len * BPT;
-
-  // ---- scores -------------------------------------------------------------
-  // A slice's code bytes of every owned position, rotated so that byte kj belongs
-  // to group pass*J + ((kj + gr) & (J-1)).
-  auto load_codes = [&](int pass, uint32_t (&cw)[TL][R][J / 4]) {
+  // record of the lane's position in block t (clamped into the sequence)
+  auto load_rec = [&](int t, uint32_t (&cw)[R][4]) {
+    const int mm = min(m0 + tid + FT * t, L - 1);
+    const u32x4* rec = reinterpret_cast<const u32x4*>(kb + (size_t)mm * BPT);
 #pragma unroll
-    for (int t = 0; t < TL; ++t) {
-      const int mm = min(m0 + tid + FT * t, L - 1);
-      const uint8_t* rec = kb + (size_t)mm * BPT + pass * J;
+    for (int r = 0; r < R; ++r) {
+      const u32x4 v = rec[r];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        if constexpr (J == 8) {
-          const int q = (gr >> 2) & 1, sh = gr & 3;
-          const uint32_t e0 = *reinterpret_cast<const uint32_t*>(rec + r * 16 + 4 * q);
-          const uint32_t e1 = *reinterpret_cast<const uint32_t*>(rec + r * 16 + 4 * (1 - q));
-          cw[t][r][0] = __builtin_amdgcn_alignbyte(e1, e0, sh);
-          cw[t][r][1] = __builtin_amdgcn_alignbyte(e0, e1, sh);
-        } else {
-          const uint32_t d = *reinterpret_cast<const uint32_t*>(rec + r * 16);
-          cw[t][r][0] = __builtin_amdgcn_alignbyte(d, d, gr);
-        }
-      }
+      for (int k = 0; k < 4; ++k) cw[r][k] = v[k];
     }
   };
-  uint32_t cw[TL][R][J / 4];
-  load_codes(0, cw);
+  constexpr int NB = (R == 1) ? TL : 2;  // records in flight
+  uint32_t cw[NB][R][4];
+#pragma unroll
+  for (int t = 0; t < NB - (NB < TL ? 1 : 0); ++t) load_rec(t, cw[t]);
 
   // ---- per-workgroup constants ------------------------------------------
-  // exact phases of a lane's first position m0 + tid = m0 + 16 (tid >> 4) + (tid & 15)
-  for (int i = tid; i < FPR * (HI_N + 16); i += FT) {
-    if (i < FPR * HI_N) {
-      const int p = i / HI_N, u = i % HI_N;
-      ehi[i] = phase_exact((uint32_t)(m0 + 16 * u), ph.lo[p], ph.hi[p]);
-    } else {
-      const int k = i - FPR * HI_N, p = k >> 4, u = k & 15;
-      elo[k] = phase_exact((uint32_t)u, ph.lo[p], ph.hi[p]);
-    }
+  {
+    // the head's key codebook, [G][R][Nc'][8] fp16 as in HBM
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.kcb + (size_t)h * FG * R * FNC * 8);
+    u32x4* dst = reinterpret_cast<u32x4*>(lds);
+#pragma unroll 4
+    for (int i = tid; i < Cfg::KCB / 16; i += FT) dst[i] = src[i];
   }
-  if (tid < FPR) stp[tid] = make_float2(fp.step_c[tid], fp.step_s[tid]);
+  // lane phases e^{i d theta_p}, d < 64: 16-byte chunk c (pairs 4c..4c+3) of row d
+  // at slot (c + d) & 15, so the 64 lanes reading chunk c hit 16 different slots
+  for (int i = tid; i < 64 * FPR; i += FT) {
+    const int d = i >> 6, p = i & 63;
+    const float2 e = phase_exact((uint32_t)d, ph.lo[p], ph.hi[p]);
+    pht[d * 64 + (((p >> 2) + d) & 15) * 4 + (p & 3)] = pack_h2(e.x, e.y);
+  }
   if (tid < FNH * FPR) {
     const int hh = tid >> 6, p = tid & 63;
     const float* qrow = a.q + ((size_t)b * a.Hq + h * FNH + hh) * FD;
@@ -224,120 +236,74 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
       new_v[d] = v;
     }
   }
+  __syncthreads();  // codebook, lane phases and rotated query visible
 
+  // lane constants: e^{i lane theta_p} for the 64 pairs (packed fp16)
+  uint32_t el[FPR];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(pht + lane * 64 + ((c + lane) & 15) * 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) el[4 * c + k] = v[k];
+  }
+
+  // ---- scores -------------------------------------------------------------
+  // MFMA A operand (q'): instruction k (K-step k = pairs 2k, 2k+1) broadcasts
+  // block k % 16's A to all 16 blocks (CBSZ = 4, ABID = k % 16), so lane
+  // (block bq, row qi) only holds head qi's q' for K-steps bq and bq + 16: pairs
+  // 2 bq, 2 bq + 1, 2 bq + 32, 2 bq + 33. Their block phases e^{i m_b theta_p}
+  // advance by e^{i 512 theta_p} per block from an exact start (fp32).
+  const int qi = lane & 3, bq = lane >> 2;
+  float2 qv[4], eb[4], stp[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int p = 2 * bq + (u & 1) + 32 * (u >> 1);
+    qv[u] = qz[qi * FPR + p];
+    eb[u] = phase_exact((uint32_t)(m0 + 64 * wave), ph.lo[p], ph.hi[p]);
+    stp[u] = phase_exact((uint32_t)FT, ph.lo[p], ph.hi[p]);
+  }
   float s[TL][FNH];
 #pragma unroll
-  for (int t = 0; t < TL; ++t)
+  for (int t = 0; t < TL; ++t) {
+    if constexpr (NB < TL) {
+      if (t + 1 < TL) load_rec(t + 1, cw[(t + 1) % NB]);
+    }
+    if (t > 0) {
 #pragma unroll
-    for (int k = 0; k < FNH; ++k) s[t][k] = 0.f;
-
-  const int hr = HROT ? ((tid / J) & 3) : 0;    // head rotation of this lane
-  uint32_t hoff[FNH];
+      for (int u = 0; u < 4; ++u)
+        eb[u] = make_float2(fmaf(eb[u].x, stp[u].x, -eb[u].y * stp[u].y), fmaf(eb[u].x, stp[u].y, eb[u].y * stp[u].x));
+    }
+    // q' = q~ conj(e_b) as fp16 (re, im); qa[0..1]: K-step bq, qa[2..3]: K-step bq + 16
+    uint32_t qa[4];
 #pragma unroll
-  for (int k = 0; k < FNH; ++k) hoff[k] = (uint32_t)(((k + hr) & 3) * J * 16);
-
-#pragma unroll 1
-  for (int pass = 0; pass < NPASS; ++pass) {
-    if (pass > 0) load_codes(pass, cw);  // in flight during the table build
-    __syncthreads();  // previous slice fully consumed; constants visible
-    {
-      // table slice: this lane builds every (round, code) row of group pass*J + (tid % J)
-      // for its four query heads; the codebook rows are loaded before any is used
-      constexpr int NE = R * FNC * J / FT;
-      const int jp = tid & (J - 1), j = pass * J + jp;
-      float2 qv[FNH][4];
+    for (int u = 0; u < 4; ++u)
+      qa[u] = pack_h2(fmaf(qv[u].x, eb[u].x, qv[u].y * eb[u].y), fmaf(qv[u].y, eb[u].x, -qv[u].x * eb[u].y));
+    const half4_t a_lo = as_h4(qa[0], qa[1]), a_hi = as_h4(qa[2], qa[3]);
+    const uint32_t (&cr)[R][4] = cw[t % NB];
+    float4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    static_for<FG>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      u32x4 z;
 #pragma unroll
-      for (int ah = 0; ah < FNH; ++ah)
+      for (int r = 0; r < R; ++r) {
+        const uint32_t code = (cr[r][j >> 2] >> (8 * (j & 3))) & 0xffu;
+        const u32x4 zr = *reinterpret_cast<const u32x4*>(lds + ((size_t)(j * R + r) * FNC + code) * 16);
+        if (r == 0) {
+          z = zr;
+        } else {
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) qv[ah][pp] = qz[ah * FPR + 4 * j + pp];
-      u32x4 zr[NE];
-      const _Float16* cbj = a.kcb + ((size_t)h * FG + j) * R * FNC * 8;
-#pragma unroll
-      for (int k = 0; k < NE; ++k) zr[k] = *reinterpret_cast<const u32x4*>(cbj + (size_t)((tid + FT * k) / J) * 8);
-#pragma unroll
-      for (int k = 0; k < NE; ++k) {
-        const int rl = (tid + FT * k) / J;  // r * 256 + l
-#pragma unroll
-        for (int ah = 0; ah < FNH; ++ah) {
-          u32x4 o;
-#pragma unroll
-          for (int pp = 0; pp < 4; ++pp) {
-            const half2_t z = as_h2(zr[k][pp]);
-            const float x = (float)z.x, y = (float)z.y;
-            o[pp] = pack_h2(fmaf(qv[ah][pp].x, x, qv[ah][pp].y * y), fmaf(qv[ah][pp].y, x, -qv[ah][pp].x * y));
-          }
-          *reinterpret_cast<u32x4*>(lds + (size_t)((rl * FNH + ah) * J + jp) * 16) = o;
+          for (int k = 0; k < 4; ++k) z[k] = add_h2(z[k], zr[k]);
         }
       }
-    }
-    __syncthreads();  // slice built
-
+      const uint32_t k0 = rotate_h2(z[0], el[4 * j]), k1 = rotate_h2(z[1], el[4 * j + 1]);
+      const uint32_t k2 = rotate_h2(z[2], el[4 * j + 2]), k3 = rotate_h2(z[3], el[4 * j + 3]);
+      // K-steps 2j (pairs 4j, 4j+1) and 2j + 1 (pairs 4j+2, 4j+3)
+      const half4_t aop = j < 8 ? a_lo : a_hi;
+      acc0 = __builtin_amdgcn_mfma_f32_4x4x4f16(aop, as_h4(k0, k1), acc0, 4, (2 * j) & 15, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_4x4x4f16(aop, as_h4(k2, k3), acc1, 4, (2 * j + 1) & 15, 0);
+    });
 #pragma unroll
-    for (int hf = 0; hf < NHALF; ++hf) {
-      // phase state of slots KH*hf .. KH*hf + KH - 1 at the lane's first position
-      float2 om[KH][4], w[KH][4];
-#pragma unroll
-      for (int ks = 0; ks < KH; ++ks)
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          const int p = 4 * (pass * J + ((KH * hf + ks + gr) & (J - 1))) + pp;
-          w[ks][pp] = stp[p];
-          const float2 A = ehi[p * HI_N + (tid >> 4)], B = elo[p * 16 + (tid & 15)];
-          om[ks][pp] = make_float2(A.x * B.x - A.y * B.y, A.x * B.y + A.y * B.x);
-        }
-      // gathers run one (position, slot) step ahead of their use
-      auto gather = [&](int t, int ks, u32x4 (&T)[R][FNH]) {
-        const int kj = KH * hf + ks;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const uint32_t code = (cw[t][r][kj >> 2] >> (8 * (kj & 3))) & 0xffu;
-          const uint32_t row = (code << ROWSH) + (uint32_t)(r * FNC * ROW + ((kj + gr) & (J - 1)) * 16);
-#pragma unroll
-          for (int k = 0; k < FNH; ++k) T[r][k] = *reinterpret_cast<const u32x4*>(lds + row + hoff[k]);
-        }
-      };
-      // R = 1: gathers run one (position, slot) step ahead of their use; R = 2
-      // already has eight independent gathers per slot.
-      constexpr int NB = (R == 1) ? 2 : 1;
-      u32x4 T[NB][R][FNH];
-      if constexpr (R == 1) gather(0, 0, T[0]);
-#pragma unroll
-      for (int t = 0; t < TL; ++t) {
-        if (t > 0) {
-#pragma unroll
-          for (int ks = 0; ks < KH; ++ks)
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-              const float2 o = om[ks][pp], ww = w[ks][pp];
-              om[ks][pp] = make_float2(fmaf(o.x, ww.x, -o.y * ww.y), fmaf(o.x, ww.y, o.y * ww.x));
-            }
-        }
-#pragma unroll
-        for (int ks = 0; ks < KH; ++ks) {
-          const int step = t * KH + ks, cur = (R == 1) ? (step & 1) : 0;
-          if constexpr (R == 1) {
-            if (ks + 1 < KH) gather(t, ks + 1, T[cur ^ 1]);
-            else if (t + 1 < TL) gather(t + 1, 0, T[cur ^ 1]);
-          } else {
-            gather(t, ks, T[0]);
-          }
-          half2_t phs[4];
-#pragma unroll
-          for (int pp = 0; pp < 4; ++pp) phs[pp] = as_h2(pack_h2(om[ks][pp].x, om[ks][pp].y));
-#pragma unroll
-          for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int k = 0; k < FNH; ++k) {
-              float acc = s[t][k];
-              acc = __builtin_amdgcn_fdot2(as_h2(T[cur][r][k][0]), phs[0], acc, false);
-              acc = __builtin_amdgcn_fdot2(as_h2(T[cur][r][k][1]), phs[1], acc, false);
-              acc = __builtin_amdgcn_fdot2(as_h2(T[cur][r][k][2]), phs[2], acc, false);
-              acc = __builtin_amdgcn_fdot2(as_h2(T[cur][r][k][3]), phs[3], acc, false);
-              s[t][k] = acc;
-            }
-        }
-      }
-    }
+    for (int k = 0; k < FNH; ++k) s[t][k] = acc0[k] + acc1[k];
   }
 
   // ---- softmax over the chunk ---------------------------------------------
@@ -346,14 +312,8 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   for (int t = 0; t < TL; ++t) {
     const int mt = m0 + tid + FT * t;
     const bool ok = mt < L && mt != skip_pos;
-    float v[FNH];
 #pragma unroll
-    for (int k = 0; k < FNH; ++k) {
-      const int src = HROT ? ((k - hr) & 3) : k;
-      v[k] = HROT ? sel4(s[t][0], s[t][1], s[t][2], s[t][3], src) : s[t][k];
-    }
-#pragma unroll
-    for (int k = 0; k < FNH; ++k) s[t][k] = ok ? v[k] * a.sm_scale : -INFINITY;
+    for (int k = 0; k < FNH; ++k) s[t][k] = ok ? s[t][k] * a.sm_scale : -INFINITY;
   }
 #pragma unroll
   for (int k = 0; k < FNH; ++k) {
@@ -363,7 +323,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     mx = wave_max(mx);
     if (lane == 0) red[k * FW + wave] = mx;
   }
-  __syncthreads();  // also: every lane is done with the last table slice
+  __syncthreads();  // also: every lane is done with the key codebook
 #pragma unroll
   for (int k = 0; k < FNH; ++k) {
     float mx = red[k * FW];
@@ -415,14 +375,14 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   if (mf_active) load_slab(0, cvn);
 
   // ---- value histograms (LDS integer atomics) -----------------------------
+  // One 64-bit add carries two query heads' weights: a (round, code, group) bin
+  // row holds heads 0..3 as consecutive dwords, and no 32-bit half can carry into
+  // its neighbour since a chunk's weights sum to at most C * 2^FXSHIFT = 2^31.
   {
-    const int g16 = tid & 15, h16 = (tid >> 4) & 3;
+    const int g16 = tid & 15, h16 = (tid >> 4) & 1;
     uint32_t gb[FG];
 #pragma unroll
     for (int kj = 0; kj < FG; ++kj) gb[kj] = (uint32_t)(((kj + g16) & 15) * 16);
-    uint32_t hb[FNH];
-#pragma unroll
-    for (int k = 0; k < FNH; ++k) hb[k] = (uint32_t)(((k + h16) & 3) * 4);
     const uint8_t* vb = a.vcodes + ((size_t)b * a.v.Hkv + h) * (size_t)a.cache_len * BPT;
     const float fxs = (float)(1u << FXSHIFT);
     const int q4 = (g16 >> 2) & 3, sh4 = g16 & 3;
@@ -436,10 +396,13 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
         for (int r = 0; r < R; ++r)
 #pragma unroll
           for (int k = 0; k < 4; ++k) e[r][k] = *reinterpret_cast<const uint32_t*>(rec + r * 16 + 4 * ((k + q4) & 3));
-        uint32_t pf[FNH];
-#pragma unroll
-        for (int k = 0; k < FNH; ++k)
-          pf[k] = (uint32_t)fmaf(sel4(s[t][0], s[t][1], s[t][2], s[t][3], (k + h16) & 3), fxs, 0.5f);
+        // pair word 0 goes to heads 2 h16, 2 h16 + 1; word 1 to the other pair
+        const uint64_t p01 = (uint64_t)(uint32_t)fmaf(s[t][0], fxs, 0.5f) |
+                             ((uint64_t)(uint32_t)fmaf(s[t][1], fxs, 0.5f) << 32);
+        const uint64_t p23 = (uint64_t)(uint32_t)fmaf(s[t][2], fxs, 0.5f) |
+                             ((uint64_t)(uint32_t)fmaf(s[t][3], fxs, 0.5f) << 32);
+        const uint64_t pw[2] = {h16 ? p23 : p01, h16 ? p01 : p23};
+        const uint32_t hoff0 = (uint32_t)(h16 * 8), hoff1 = (uint32_t)((1 - h16) * 8);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           uint32_t x[4];
@@ -449,10 +412,10 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
           for (int kj = 0; kj < FG; ++kj) {
             const uint32_t code = (x[kj >> 2] >> (8 * (kj & 3))) & 0xffu;
             const uint32_t row = ((uint32_t)(r * FNC) + code) * 256u + gb[kj];
-#pragma unroll
-            for (int k = 0; k < FNH; ++k)
-              __hip_atomic_fetch_add(reinterpret_cast<uint32_t*>(lds + row + hb[k]), pf[k], __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(lds + row + hoff0), pw[0], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(lds + row + hoff1), pw[1], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
           }
         }
       }
@@ -466,7 +429,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   // covers group j = 8 sI + (bk >> 1), dims 4 (bk & 1) .. +3; within a block lane
   // i = lane & 3 supplies A row (head i) and B column (dim 4 (bk & 1) + i). The
   // value-codebook rows a wave needs are staged, 32 bins of its 8 groups at a
-  // time, in its own 4 KiB of the (now unused) phase table.
+  // time, in its own 4 KiB of the (now unused) lane phase table.
   {
     const bool active = mf_active;
     const int sI = mf_sI, kh = mf_kh;
@@ -474,7 +437,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     const int g8 = bk >> 1, j = 8 * sI + g8;
     const int e = 4 * (bk & 1) + i4;
     const float inv = 1.0f / (float)(1u << FXSHIFT);
-    _Float16* slab = reinterpret_cast<_Float16*>(ehi) + (wave & 3) * 2048;  // [8 groups][32 bins][8 dims]
+    _Float16* slab = reinterpret_cast<_Float16*>(pht) + (wave & 3) * 2048;  // [8 groups][32 bins][8 dims]
     float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
     for (int sl = 0; sl < NSLAB; ++sl) {
@@ -539,37 +502,34 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
       part[tid * pstride + 1] = lsum[tid] * al[tid] + be[tid];
     }
   }
-  merge_if_last<FT>(a, b, h, FNH, FD, flag, reinterpret_cast<float*>(lds), Cfg::TAB / 4);
+  merge_if_last<FT>(a, b, h, FNH, FD, flag, reinterpret_cast<float*>(lds), Cfg::MAIN / 4);
 }
 
-template <int R, int TL, bool HROT>
-hipError_t launch_fast_t(const DecodeArgs& a, const PhaseTable& ph, const FastPhase& fp, hipStream_t stream) {
-  const size_t smem = FastCfg<R>::TAB + AUX_BYTES;
+template <int R, int TL>
+hipError_t launch_fast_t(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
+  const size_t smem = FastCfg<R>::MAIN + AUX_BYTES;
   static std::atomic<uint64_t> configured{0};
-  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&decode_fast_kernel<R, TL, HROT>), configured);
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&decode_fast_kernel<R, TL>), configured);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_fast_kernel<R, TL, HROT>), dim3(a.n_chunks * a.k.Hkv, a.B), dim3(FT), smem, stream, a,
-                     ph, fp);
+  hipLaunchKernelGGL((decode_fast_kernel<R, TL>), dim3(a.n_chunks * a.k.Hkv, a.B), dim3(FT), smem, stream, a, ph);
   return hipGetLastError();
 }
 
-template <int R, bool HROT>
-hipError_t launch_fast_r(const DecodeArgs& a, const PhaseTable& ph, const FastPhase& fp, hipStream_t stream) {
+template <int R>
+hipError_t launch_fast_r(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
   switch (a.chunk) {
-    case 4096: return launch_fast_t<R, 8, HROT>(a, ph, fp, stream);
-    case 2048: return launch_fast_t<R, 4, HROT>(a, ph, fp, stream);
-    case 1024: return launch_fast_t<R, 2, HROT>(a, ph, fp, stream);
+    case 4096: return launch_fast_t<R, 8>(a, ph, stream);
+    case 2048: return launch_fast_t<R, 4>(a, ph, stream);
+    case 1024: return launch_fast_t<R, 2>(a, ph, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_fast(const DecodeArgs& a, const PhaseTable& ph, const FastPhase& fp, hipStream_t stream) {
-  // Head rotation costs an address add per gather; it pays when a slice has too
-  // few groups (J = 4 at R = 2) to spread 16 lanes over distinct bank groups.
-  if (a.k.R == 1) return launch_fast_r<1, false>(a, ph, fp, stream);
-  if (a.k.R == 2) return launch_fast_r<2, true>(a, ph, fp, stream);
+hipError_t launch_decode_fast(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
+  if (a.k.R == 1) return launch_fast_r<1>(a, ph, stream);
+  if (a.k.R == 2) return launch_fast_r<2>(a, ph, stream);
   return hipErrorInvalidValue;
 }
 
