@@ -287,8 +287,10 @@ def main():
     t_wall = time.perf_counter() - t_wall
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
-    # one step is exactly one kernel launch on `stream` (the fused append +
-    # attention kernel), so the launch average is the timed region over K
+    # one step is one commvq_decode_step call on `stream`: the fused append +
+    # attention kernel, then the chunk-merge kernel. HIP events cannot split the
+    # two inside one call, so the roofline is taken over the whole call (the
+    # merge kernel adds ~10 %; the rocprofv3 trace gives the split).
     dec_avg_ms = ms_step
     # cached tokens per step and packed-code bytes per decode launch
     toks, code_bytes = 0, 0
@@ -300,7 +302,7 @@ def main():
     toks_per_step = toks / args.steps
     bytes_per_launch = code_bytes / args.steps
     achieved = bytes_per_launch / (dec_avg_ms * 1e-3) / 1e9
-    print(f"[bench] step {ms_step * 1e3:.1f} us (one launch each), host issue {t_wall / args.steps * 1e6:.1f} us/step",
+    print(f"[bench] step {ms_step * 1e3:.1f} us (decode + merge kernels), host issue {t_wall / args.steps * 1e6:.1f} us/step",
           file=sys.stderr, flush=True)
 
     cpu = None
@@ -327,7 +329,7 @@ def main():
                    "layer_slices": NL, "step": "commvq_decode_step: encode+append K and V of 1 token (8 KV heads), then attention"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(), "traffic_unit": "bytes per launch",
-                     "kernel": "decode step (fused append + attention)", "bytes_per_launch": bytes_per_launch,
+                     "kernel": "commvq_decode_step call: fused append + attention kernel, then chunk-merge kernel", "bytes_per_launch": bytes_per_launch,
                      "avg_launch_us": dec_avg_ms * 1e3},
         "cpu_baseline": cpu,
     }

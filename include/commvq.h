@@ -102,8 +102,9 @@ double commvq_bits_per_scalar(const commvq_codebook* cb);
  * negative commvq_status if the descriptor is invalid. */
 int64_t commvq_code_bytes_per_token(const commvq_codebook* cb);
 
-/* Workspace bytes that commvq_decode_attention needs for this shape (arrival
- * counters and split-context partials, enough for every flags value); negative
+/* Workspace bytes that commvq_decode_attention / commvq_decode_step need for
+ * this shape: the split-context partials, (max, sum, o[D]) fp32 per (sequence,
+ * query head, chunk of positions), sized for every flags value; negative
  * commvq_status on invalid arguments. */
 int64_t commvq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
                                       const commvq_codebook* kcb, const commvq_codebook* vcb);
@@ -146,9 +147,9 @@ int32_t commvq_append(const commvq_codebook* cb, const void* x, int32_t batch,
  *   sm_scale multiplies q.k (normally 1/sqrt(D)).
  *   out      device fp32 [batch][n_q_heads][D]
  *   workspace device, >= commvq_decode_workspace_bytes(batch, n_q_heads,
- *            max_seq_len, kcb, vcb) bytes, 256-byte aligned, zero-filled
- *            before its first use; every call leaves it ready for the next.
- *            Calls sharing one workspace must not overlap in time.
+ *            max_seq_len, kcb, vcb) bytes, 256-byte aligned; its contents
+ *            need no initialisation and are scratch after the call. Calls
+ *            sharing one workspace must not overlap in time.
  *   flags    0 or COMMVQ_DECODE_EXACT.
  * Pages: "What carries the argument" (query-codebook factors computed once and
  * reused over cached positions); "If this is right", fourth bullet (weights
@@ -168,8 +169,10 @@ int32_t commvq_decode_attention(const commvq_codebook* kcb, const commvq_codeboo
  *   positions    device int32 [batch]; a position outside [0, cache_len) skips
  *                the append for that sequence (attention still runs)
  *   kcodes, vcodes are written (the new records) and read.
- * Other arguments as commvq_decode_attention. For the fp16-table shapes the new
- * token is encoded inside the attention kernel, so the whole step is one launch.
+ * Other arguments as commvq_decode_attention. For the shapes of the fast kernel
+ * (D 128, g 8, Nc' 256, four query heads per KV head, R 1 or 2) the new token is
+ * encoded inside the attention kernel: the step is that kernel plus the chunk
+ * merge, as for commvq_decode_attention.
  * Pages: abstract (each new K/V vector is encoded to a low-bit code); "What
  * carries the argument" (shared index per group, R residual rounds, codebook
  * factors reused over cached positions). */

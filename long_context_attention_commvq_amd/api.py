@@ -70,8 +70,8 @@ class DecodeWorkspace:
         if n < 0:
             raise _lib.CommvqError(int(n), _lib.commvq_last_error())
         self.nbytes = int(n)
-        # zero-filled once: the arrival counters at its start must read zero on first use
-        self.buf = torch.zeros(max(self.nbytes, 256), dtype=torch.uint8, device=device)
+        # chunk partials only: no initialisation needed
+        self.buf = torch.empty(max(self.nbytes, 256), dtype=torch.uint8, device=device)
 
 
 def decode_attention(kq: Quantizer, vq: Quantizer, q: torch.Tensor, q_pos: torch.Tensor, kcache: torch.Tensor,

@@ -296,8 +296,7 @@ int32_t decode_impl(const commvq_codebook* kcb, const commvq_codebook* vcb, cons
   a.seq_lens = seq_lens;
   a.kcb = static_cast<const _Float16*>(kcb->entries);
   a.vcb = static_cast<const _Float16*>(vcb->entries);
-  a.counters = static_cast<uint32_t*>(workspace);
-  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + commvq::counter_bytes(batch, k.Hkv));
+  a.part = static_cast<float*>(workspace);
   a.out = out;
   a.B = batch;
   a.Hq = n_q_heads;
@@ -344,6 +343,7 @@ int32_t decode_impl(const commvq_codebook* kcb, const commvq_codebook* vcb, cons
       e = commvq::launch_decode_generic(a, pc.ph, s);
     }
   }
+  if (e == hipSuccess) e = commvq::launch_decode_merge(a, s);
   return hip_status(e, step ? "commvq_decode_step launch" : "commvq_decode_attention launch");
 }
 

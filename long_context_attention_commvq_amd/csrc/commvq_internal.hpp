@@ -51,7 +51,6 @@ struct DecodeArgs {
   const int32_t* positions;
   uint8_t* kcodes_w;
   uint8_t* vcodes_w;
-  uint32_t* counters;  // [B][Hkv] arrival counters (zero between calls)
   float* part;         // [B][Hq][n_chunks][D + 2]: (max, sum, o[D]) per chunk
   float* out;          // [B][Hq][D]
   int B, Hq, NH, cache_len, max_len, n_chunks, chunk;
@@ -84,5 +83,6 @@ hipError_t launch_decode_fast(const DecodeArgs& a, const PhaseTable& ph, hipStre
 
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_generic(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace commvq

@@ -61,8 +61,6 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, 
       const int hh = i / (D + 2), k = i % (D + 2);
       part[hh * pstride + k] = (k == 0) ? -INFINITY : 0.f;
     }
-    merge_if_last<kThreads>(a, b, h, NH, D, reinterpret_cast<uint32_t*>(sm), sm + 4,
-                            2 * NH * P + NH * D + red_floats + uni_floats - 4);
     return;
   }
   float2* qz = reinterpret_cast<float2*>(sm);  // [NH][P]
@@ -205,7 +203,6 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, 
     const int hh = i / (D + 2), k = i % (D + 2);
     part[hh * pstride + k] = k < 2 ? red[2 * hh + k] : oacc[hh * D + k - 2];
   }
-  merge_if_last<kThreads>(a, b, h, NH, D, reinterpret_cast<uint32_t*>(red + 2 * NH), uni, uni_floats);
 }
 
 template <int NH, int GS>
@@ -254,8 +251,9 @@ int decode_chunk_len(const CbShape& k, const CbShape& v, int B, int Hq, int max_
 }
 
 size_t decode_workspace_bytes(const CbShape& k, int B, int Hq, int max_len, int chunk) {
+  // chunk partials [B][Hq][n_chunks][D + 2]: (max, sum, o[D]) of one chunk
   const size_t n_chunks = (size_t)(max_len + chunk - 1) / chunk;
-  return counter_bytes(B, k.Hkv) + (size_t)B * Hq * n_chunks * (k.D + 2) * sizeof(float);
+  return (size_t)B * Hq * n_chunks * (k.D + 2) * sizeof(float);
 }
 
 hipError_t launch_decode_generic(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {

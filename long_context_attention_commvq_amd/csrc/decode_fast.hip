@@ -29,8 +29,8 @@
 //   histogram is contracted with the value codebook on MFMA
 //   (v_mfma_f32_4x4x4f16, 16 blocks = 8 groups x 2 dim quads, weights split into
 //   fp16 hi + lo parts).
-// The chunk's (max, sum, o) go to the workspace and the last workgroup of the
-// (sequence, KV head) merges the chunks.
+// The chunk's (max, sum, o) go to the workspace; a second kernel merges the
+// chunks of each (sequence, query head).
 
 #include <type_traits>
 #include <utility>
@@ -59,11 +59,11 @@ struct FastCfg {
 };
 
 // aux LDS: lane phases [64 offsets][64 pairs] fp16 (16-byte chunks swizzled),
-// rotated query [4][64], reductions [64], MFMA staging [2][64][4], flag, and a
-// decode step's new token: codes [2][2][16], scores [4], value [128]
+// rotated query [4][64], reductions [64], and a decode step's new token:
+// codes [2][2][16], scores [4], value [128]
 constexpr int PHT_BYTES = 64 * FPR * 4;
 constexpr int NEW_BYTES = 64 + FNH * 4 + FD * 4;
-constexpr int AUX_BYTES = PHT_BYTES + FNH * FPR * 8 + 64 * 4 + 2 * 64 * 4 * 4 + 16 + NEW_BYTES;
+constexpr int AUX_BYTES = PHT_BYTES + FNH * FPR * 8 + 64 * 4 + NEW_BYTES;
 static_assert(131072 + AUX_BYTES <= 160 * 1024, "LDS budget");
 static_assert(PHT_BYTES >= 4 * 4096, "value-codebook slabs reuse the lane phase table");
 
@@ -76,13 +76,17 @@ __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
 }
 
 // (x + iy)(c + is) on packed fp16 pairs z = (x, y), e = (c, s): t = (x c, y c),
-// then (x c - y s, y c + x s); the compiler folds the swaps and the negation into
-// operand selects of one v_pk_mul_f16 and one v_pk_fma_f16.
+// then (y, x) (-s, s) + t = (x c - y s, y c + x s); the compiler folds the swap,
+// the broadcasts and the negation into operand selects of one v_pk_mul_f16 and
+// one v_pk_fma_f16. The empty asm makes z an opaque register value: without it
+// the swap of a vector's first element was materialised by a separate
+// instruction.
 __device__ __forceinline__ uint32_t rotate_h2(uint32_t z, uint32_t e) {
+  asm("" : "+v"(z));
   const half2_t zz = __builtin_bit_cast(half2_t, z), ee = __builtin_bit_cast(half2_t, e);
   const half2_t t = zz * (half2_t){ee.x, ee.x};
-  const half2_t zs = {-zz.y, zz.x};
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(zs, (half2_t){ee.y, ee.y}, t));
+  const half2_t zs = {zz.y, zz.x};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(zs, (half2_t){-ee.y, ee.y}, t));
 }
 
 // Packed fp16 sum of two (x, y) pairs. Elements of a 32-bit vector are passed
@@ -120,9 +124,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   uint32_t* pht = reinterpret_cast<uint32_t*>(lds + Cfg::MAIN);       // [64][64] fp16 (cos, sin)
   float2* qz = reinterpret_cast<float2*>(lds + Cfg::MAIN + PHT_BYTES);  // [4][64] rotated query
   float* red = reinterpret_cast<float*>(qz + FNH * FPR);               // [64] reductions
-  float* stage = red + 64;                                             // [2][64][4] MFMA partials
-  uint32_t* flag = reinterpret_cast<uint32_t*>(stage + 2 * 64 * 4);
-  uint8_t* new_codes = reinterpret_cast<uint8_t*>(flag + 4);         // [2][R][16]
+  uint8_t* new_codes = reinterpret_cast<uint8_t*>(red + 64);         // [2][R][16]
   float* new_s = reinterpret_cast<float*>(new_codes + 64);           // [4] scaled scores
   float* new_v = new_s + FNH;                                        // [128]
 
@@ -163,7 +165,6 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
       const int hh = i / (FD + 2), k = i % (FD + 2);
       part[hh * pstride + k] = (k == 0) ? -INFINITY : 0.f;
     }
-    merge_if_last<FT>(a, b, h, FNH, FD, flag, reinterpret_cast<float*>(lds), Cfg::MAIN / 4);
     return;
   }
 
@@ -185,12 +186,14 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   for (int t = 0; t < NB - (NB < TL ? 1 : 0); ++t) load_rec(t, cw[t]);
 
   // ---- per-workgroup constants ------------------------------------------
+  // the head's key codebook, [G][R][Nc'][8] fp16 as in HBM: all loads are issued
+  // before the lane phases are computed and stored to LDS after
+  constexpr int NKCB = Cfg::KCB / 16 / FT;
+  u32x4 kcv[NKCB];
   {
-    // the head's key codebook, [G][R][Nc'][8] fp16 as in HBM
     const u32x4* src = reinterpret_cast<const u32x4*>(a.kcb + (size_t)h * FG * R * FNC * 8);
-    u32x4* dst = reinterpret_cast<u32x4*>(lds);
-#pragma unroll 4
-    for (int i = tid; i < Cfg::KCB / 16; i += FT) dst[i] = src[i];
+#pragma unroll
+    for (int k = 0; k < NKCB; ++k) kcv[k] = src[tid + FT * k];
   }
   // lane phases e^{i d theta_p}, d < 64: 16-byte chunk c (pairs 4c..4c+3) of row d
   // at slot (c + d) & 15, so the 64 lanes reading chunk c hit 16 different slots
@@ -199,6 +202,8 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     const float2 e = phase_exact((uint32_t)d, ph.lo[p], ph.hi[p]);
     pht[d * 64 + (((p >> 2) + d) & 15) * 4 + (p & 3)] = pack_h2(e.x, e.y);
   }
+#pragma unroll
+  for (int k = 0; k < NKCB; ++k) reinterpret_cast<u32x4*>(lds)[tid + FT * k] = kcv[k];
   if (tid < FNH * FPR) {
     const int hh = tid >> 6, p = tid & 63;
     const float* qrow = a.q + ((size_t)b * a.Hq + h * FNH + hh) * FD;
@@ -244,7 +249,10 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   for (int c = 0; c < 16; ++c) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(pht + lane * 64 + ((c + lane) & 15) * 4);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) el[4 * c + k] = v[k];
+    for (int k = 0; k < 4; ++k) {
+      el[4 * c + k] = v[k];
+      asm("" : "+v"(el[4 * c + k]));  // kept in registers, not re-read from LDS in the loop
+    }
   }
 
   // ---- scores -------------------------------------------------------------
@@ -355,25 +363,6 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     lsum[k] = acc;
   }
 
-  // Value-codebook slab loader for the MFMA contraction below (waves 0..3): the
-  // first slab is requested now so it arrives while the histograms fill.
-  const bool mf_active = wave < 4;
-  const int mf_sI = wave & 1, mf_kh = (wave >> 1) & 1;
-  constexpr int NSLAB = R * FNC / 2 / 32;
-  auto load_slab = [&](int sl, u32x4 (&cv)[4]) {
-    const int rl0 = mf_kh * (R * FNC / 2) + sl * 32;
-    const int r = rl0 / FNC, l0 = rl0 % FNC;
-    const _Float16* src = a.vcb + ((((size_t)h * FG + 8 * mf_sI) * R + r) * FNC + l0) * 8;
-    // element u = lane + 64 k of the slab: group u >> 5, bin u & 31
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int u = lane + 64 * k;
-      cv[k] = *reinterpret_cast<const u32x4*>(src + ((size_t)(u >> 5) * R * FNC + (u & 31)) * 8);
-    }
-  };
-  u32x4 cvn[4] = {};
-  if (mf_active) load_slab(0, cvn);
-
   // ---- value histograms (LDS integer atomics) -----------------------------
   // One 64-bit add carries two query heads' weights: a (round, code, group) bin
   // row holds heads 0..3 as consecutive dwords, and no 32-bit half can carry into
@@ -421,60 +410,57 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
       }
     }
   }
+  // Value-codebook operands of the MFMA contraction below, requested as soon as
+  // this lane's atomics are issued (the barrier wait hides part of their
+  // latency; one head's codebook is shared by all its chunks, so these mostly
+  // hit L2). Wavefront w contracts groups 2w, 2w+1; its
+  // 16 MFMA blocks are 4 bin quarters x (2 groups x 2 dimension quads): lane
+  // (block mb = 4 mq + mg, column mi) takes bin quarter mq, group 2w + (mg >> 1),
+  // dimension me = 4 (mg & 1) + mi, and step st covers bins 4 st .. 4 st + 3 of
+  // its quarter (a bin is a (round, code) pair, r * 256 + code).
+  constexpr int NBIN = R * FNC, QBIN = NBIN / 4, NSTEP = QBIN / 4;
+  const int mbk = lane >> 2, mi = lane & 3, mq = mbk >> 2, mg = mbk & 3;
+  const int mgrp = 2 * wave + (mg >> 1), me = 4 * (mg & 1) + mi;
+  half4_t cvb[NSTEP];
+  {
+    const _Float16* cvg = a.vcb + ((size_t)h * FG + mgrp) * R * FNC * 8 + me;
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) cvb[st][u] = cvg[(size_t)(mq * QBIN + 4 * st + u) * 8];
+  }
+
   __syncthreads();
 
   // ---- histogram x value codebook on MFMA ---------------------------------
-  // Waves 0..3 contract: wave w takes instruction set sI = w & 1 (groups 8 sI ..
-  // 8 sI + 7) and half kh = w >> 1 of the (round, bin) range. Block bk = lane >> 2
-  // covers group j = 8 sI + (bk >> 1), dims 4 (bk & 1) .. +3; within a block lane
-  // i = lane & 3 supplies A row (head i) and B column (dim 4 (bk & 1) + i). The
-  // value-codebook rows a wave needs are staged, 32 bins of its 8 groups at a
-  // time, in its own 4 KiB of the (now unused) lane phase table.
+  // Per group: o[head][dim] = sum_bin H[head][bin] CV[bin][dim], the fixed-point
+  // bins split into fp16 hi + lo parts (v_mfma_f32_4x4x4f16: A = H rows = heads,
+  // B = CV columns = dims, K = 4 bins per step). The four bin quarters' partial
+  // sums are then added across lanes 16 apart.
   {
-    const bool active = mf_active;
-    const int sI = mf_sI, kh = mf_kh;
-    const int bk = lane >> 2, i4 = lane & 3;
-    const int g8 = bk >> 1, j = 8 * sI + g8;
-    const int e = 4 * (bk & 1) + i4;
     const float inv = 1.0f / (float)(1u << FXSHIFT);
-    _Float16* slab = reinterpret_cast<_Float16*>(pht) + (wave & 3) * 2048;  // [8 groups][32 bins][8 dims]
     float4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-    for (int sl = 0; sl < NSLAB; ++sl) {
-      const int rl0 = kh * (R * FNC / 2) + sl * 32;  // first (round, bin) of the slab
-      const int r = rl0 / FNC, l0 = rl0 % FNC;
-      __syncthreads();  // previous slab consumed (and, first time, phase tables dead)
-      if (active) {
+    const char* hrow = lds + mgrp * 16 + mi * 4;  // bin rl of (group, head mi) at rl * 256
 #pragma unroll
-        for (int k = 0; k < 4; ++k) reinterpret_cast<u32x4*>(slab)[lane + 64 * k] = cvn[k];
-        if (sl + 1 < NSLAB) load_slab(sl + 1, cvn);
+    for (int st = 0; st < NSTEP; ++st) {
+      half4_t ahi, alo;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t hv = *reinterpret_cast<const uint32_t*>(hrow + (size_t)(mq * QBIN + 4 * st + u) * 256);
+        const float x = (float)hv * inv;
+        const _Float16 hi = (_Float16)x;
+        ahi[u] = hi;
+        alo[u] = (_Float16)(x - (float)hi);
       }
-      __syncthreads();
-      if (active) {
-#pragma unroll
-        for (int st = 0; st < 8; ++st) {
-          half4_t ahi, alo, bv;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int l = l0 + 4 * st + u;
-            const uint32_t hv = *reinterpret_cast<const uint32_t*>(lds + ((r * FNC + l) * 256 + j * 16 + i4 * 4));
-            const float x = (float)hv * inv;
-            const _Float16 hi = (_Float16)x;
-            ahi[u] = hi;
-            alo[u] = (_Float16)(x - (float)hi);
-            bv[u] = slab[(g8 * 32 + 4 * st + u) * 8 + e];
-          }
-          acc = __builtin_amdgcn_mfma_f32_4x4x4f16(ahi, bv, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_4x4x4f16(alo, bv, acc, 0, 0, 0);
-        }
-      }
+      acc = __builtin_amdgcn_mfma_f32_4x4x4f16(ahi, cvb[st], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_4x4x4f16(alo, cvb[st], acc, 0, 0, 0);
     }
-    // acc[k] = partial o[head k][8 j + e]
-    if (active && kh == 1) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) stage[(sI * 64 + lane) * 4 + k] = acc[k];
+    for (int k = 0; k < 4; ++k) {
+      acc[k] += __shfl_xor(acc[k], 16, 64);
+      acc[k] += __shfl_xor(acc[k], 32, 64);
     }
-    __syncthreads();
+    // acc[k] = o[head k][8 mgrp + me] (lanes 0..15)
     // with the new token folded in (decode step owner): M' = max(M, s_new),
     // o' = o e^{M - M'} + v_new e^{s_new - M'}, l' = l e^{M - M'} + e^{s_new - M'}
     float al[FNH], be[FNH], Mf[FNH];
@@ -491,18 +477,16 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
         be[k] = 0.f;
       }
     }
-    if (active && kh == 0) {
-      const float vn = fold ? new_v[8 * j + e] : 0.f;
+    if (lane < 16) {
+      const float vn = fold ? new_v[8 * mgrp + me] : 0.f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        part[k * pstride + 2 + 8 * j + e] = (acc[k] + stage[(sI * 64 + lane) * 4 + k]) * al[k] + vn * be[k];
+      for (int k = 0; k < 4; ++k) part[k * pstride + 2 + 8 * mgrp + me] = acc[k] * al[k] + vn * be[k];
     }
     if (tid < FNH) {
       part[tid * pstride + 0] = Mf[tid];
       part[tid * pstride + 1] = lsum[tid] * al[tid] + be[tid];
     }
   }
-  merge_if_last<FT>(a, b, h, FNH, FD, flag, reinterpret_cast<float*>(lds), Cfg::MAIN / 4);
 }
 
 template <int R, int TL>

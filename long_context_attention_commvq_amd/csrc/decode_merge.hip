@@ -1,0 +1,90 @@
+// Split-context combine: the decode kernels leave, per (sequence, query head,
+// chunk of positions), the chunk's running max m_c, its sum of exponentials
+// l_c and its unnormalised output o_c. The merged output is
+//   o = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c,  M = max_c m_c,
+// the standard combination of softmax partials over disjoint position ranges.
+// Running it as its own kernel (ordered after the decode kernel on the stream)
+// publishes the partials at the kernel boundary, instead of one release per
+// workgroup across the XCDs' separate L2 caches.
+
+#include "decode_common.hpp"
+
+namespace commvq {
+namespace {
+
+constexpr int kMergeThreads = 256;
+
+// One workgroup per (sequence, query head). Lane t takes dimension t % D and the
+// chunks c = t / D (mod 256 / D), loading 16 of them at a time before using
+// any (one memory round trip per batch; batches are combined with a running max
+// and rescaling). The lanes sharing a dimension are combined the same way
+// through LDS.
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float* __restrict__ part,
+                                                                     float* __restrict__ out, int n_chunks, int D,
+                                                                     int Hq) {
+  __shared__ float sm[3][kMergeThreads];
+  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const size_t cs = (size_t)D + 2;
+  const float* pr = part + ((size_t)b * Hq + hq) * (size_t)n_chunks * cs;
+  const int lpd = kMergeThreads / D;  // lanes per dimension (D <= 256)
+  const int d = tid % D, sub = tid / D;
+  const bool active = sub < lpd;
+  float M = -INFINITY, l = 0.f, acc = 0.f;
+  if (active) {
+    constexpr int KB = 16;  // chunks loaded per batch, all before any is used
+    for (int c0 = sub; c0 < n_chunks; c0 += KB * lpd) {
+      float mc[KB], lc[KB], oc[KB];
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int c = c0 + k * lpd;
+        const float* p = pr + (size_t)(c < n_chunks ? c : 0) * cs;
+        mc[k] = c < n_chunks ? p[0] : -INFINITY;
+        lc[k] = p[1];
+        oc[k] = p[2 + d];
+      }
+      float Mb = M;
+#pragma unroll
+      for (int k = 0; k < KB; ++k) Mb = fmaxf(Mb, mc[k]);
+      if (Mb > -INFINITY) {
+        const float a = M > -INFINITY ? __expf(M - Mb) : 0.f;
+        l *= a;
+        acc *= a;
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+          const float w = mc[k] > -INFINITY ? __expf(mc[k] - Mb) : 0.f;
+          l = fmaf(w, lc[k], l);
+          acc = fmaf(w, oc[k], acc);
+        }
+        M = Mb;
+      }
+    }
+  }
+  sm[0][tid] = M;
+  sm[1][tid] = l;
+  sm[2][tid] = acc;
+  __syncthreads();
+  if (active && sub == 0) {
+    for (int k = 1; k < lpd; ++k) {
+      const float mk = sm[0][tid + k * D];
+      if (mk > -INFINITY) {
+        const float Mn = fmaxf(M, mk);
+        const float a = M > -INFINITY ? __expf(M - Mn) : 0.f, w = __expf(mk - Mn);
+        l = fmaf(l, a, w * sm[1][tid + k * D]);
+        acc = fmaf(acc, a, w * sm[2][tid + k * D]);
+        M = Mn;
+      }
+    }
+    out[((size_t)b * Hq + hq) * D + d] = l > 0.f ? acc / l : 0.f;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
+  if (a.k.D > kMergeThreads) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.Hq, a.B), dim3(kMergeThreads), 0, stream, a.part, a.out,
+                     a.n_chunks, a.k.D, a.Hq);
+  return hipGetLastError();
+}
+
+}  // namespace commvq
