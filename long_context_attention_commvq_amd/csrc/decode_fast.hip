@@ -107,6 +107,26 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// 16 * byte B of w in one instruction (a byte-select operand); used for LDS
+// gather offsets of 16-byte codebook entries.
+template <int B>
+__device__ __forceinline__ uint32_t byte_x16(uint32_t w) {
+  uint32_t r;
+  if constexpr (B == 0)
+    asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+        : "=v"(r) : "v"(w));
+  if constexpr (B == 1)
+    asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+        : "=v"(r) : "v"(w));
+  if constexpr (B == 2)
+    asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
+        : "=v"(r) : "v"(w));
+  if constexpr (B == 3)
+    asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+        : "=v"(r) : "v"(w));
+  return r;
+}
+
 __device__ __forceinline__ half4_t as_h4(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(half4_t, (u32x2){lo, hi});
 }
@@ -160,18 +180,13 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
       cache[(((size_t)b * a.k.Hkv + h) * a.cache_len + pb) * BPT + k] = new_codes[kv2 * BPT + k];
     }
   }
-  if (m0 >= L) {
-    for (int i = tid; i < FNH * (FD + 2); i += FT) {
-      const int hh = i / (FD + 2), k = i % (FD + 2);
-      part[hh * pstride + k] = (k == 0) ? -INFINITY : 0.f;
-    }
-    return;
-  }
 
   const uint8_t* kb = a.kcodes + ((size_t)b * a.k.Hkv + h) * (size_t)a.cache_len * BPT;
-  // record of the lane's position in block t (clamped into the sequence)
+  // record of the lane's position in block t, clamped into the cache (not the
+  // sequence, so the loads need not wait for seq_lens; positions past the
+  // sequence are masked after the scores)
   auto load_rec = [&](int t, uint32_t (&cw)[R][4]) {
-    const int mm = min(m0 + tid + FT * t, L - 1);
+    const int mm = min(m0 + tid + FT * t, a.cache_len - 1);
     const u32x4* rec = reinterpret_cast<const u32x4*>(kb + (size_t)mm * BPT);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -195,11 +210,20 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
 #pragma unroll
     for (int k = 0; k < NKCB; ++k) kcv[k] = src[tid + FT * k];
   }
+  // a chunk wholly past the sequence contributes an empty partial (its loads were
+  // issued before the length was known; they stay unused)
+  if (m0 >= L) {
+    for (int i = tid; i < FNH * (FD + 2); i += FT) {
+      const int hh = i / (FD + 2), k = i % (FD + 2);
+      part[hh * pstride + k] = (k == 0) ? -INFINITY : 0.f;
+    }
+    return;
+  }
   // lane phases e^{i d theta_p}, d < 64: 16-byte chunk c (pairs 4c..4c+3) of row d
   // at slot (c + d) & 15, so the 64 lanes reading chunk c hit 16 different slots
   for (int i = tid; i < 64 * FPR; i += FT) {
     const int d = i >> 6, p = i & 63;
-    const float2 e = phase_exact((uint32_t)d, ph.lo[p], ph.hi[p]);
+    const float2 e = phase_hw((uint32_t)d, ph.lo[p], ph.hi[p]);
     pht[d * 64 + (((p >> 2) + d) & 15) * 4 + (p & 3)] = pack_h2(e.x, e.y);
   }
 #pragma unroll
@@ -208,7 +232,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     const int hh = tid >> 6, p = tid & 63;
     const float* qrow = a.q + ((size_t)b * a.Hq + h * FNH + hh) * FD;
     const float x = qrow[2 * p], y = qrow[2 * p + 1];
-    const float2 w = phase_exact((uint32_t)max(a.q_pos[b], 0), ph.lo[p], ph.hi[p]);
+    const float2 w = phase_hw((uint32_t)max(a.q_pos[b], 0), ph.lo[p], ph.hi[p]);
     qz[tid] = make_float2(x * w.x - y * w.y, x * w.y + y * w.x);
   }
 
@@ -224,7 +248,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
         kx += (float)ce[0];
         ky += (float)ce[1];
       }
-      const float2 wk = phase_exact((uint32_t)pb, ph.lo[p], ph.hi[p]);
+      const float2 wk = phase_hw((uint32_t)pb, ph.lo[p], ph.hi[p]);
       const float krx = kx * wk.x - ky * wk.y, kry = kx * wk.y + ky * wk.x;
 #pragma unroll
       for (int k = 0; k < FNH; ++k) {
@@ -267,8 +291,8 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   for (int u = 0; u < 4; ++u) {
     const int p = 2 * bq + (u & 1) + 32 * (u >> 1);
     qv[u] = qz[qi * FPR + p];
-    eb[u] = phase_exact((uint32_t)(m0 + 64 * wave), ph.lo[p], ph.hi[p]);
-    stp[u] = phase_exact((uint32_t)FT, ph.lo[p], ph.hi[p]);
+    eb[u] = phase_hw((uint32_t)(m0 + 64 * wave), ph.lo[p], ph.hi[p]);
+    stp[u] = phase_hw((uint32_t)FT, ph.lo[p], ph.hi[p]);
   }
   float s[TL][FNH];
 #pragma unroll
@@ -294,8 +318,8 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
       u32x4 z;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const uint32_t code = (cr[r][j >> 2] >> (8 * (j & 3))) & 0xffu;
-        const u32x4 zr = *reinterpret_cast<const u32x4*>(lds + ((size_t)(j * R + r) * FNC + code) * 16);
+        const uint32_t off = byte_x16<j & 3>(cr[r][j >> 2]);  // code * 16
+        const u32x4 zr = *reinterpret_cast<const u32x4*>(lds + (size_t)(j * R + r) * FNC * 16 + off);
         if (r == 0) {
           z = zr;
         } else {
@@ -312,6 +336,24 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     });
 #pragma unroll
     for (int k = 0; k < FNH; ++k) s[t][k] = acc0[k] + acc1[k];
+  }
+
+  // value records of the lane's positions, requested now so they arrive during
+  // the softmax; dword k of round r is taken from slot (k + q4) & 3 (the lane's
+  // rotation over groups in the histogram stage)
+  const int g16 = tid & 15, h16 = (tid >> 4) & 1;
+  const int q4 = (g16 >> 2) & 3, sh4 = g16 & 3;
+  uint32_t ve[TL][R][4];
+  {
+    const uint8_t* vb = a.vcodes + ((size_t)b * a.v.Hkv + h) * (size_t)a.cache_len * BPT;
+#pragma unroll
+    for (int t = 0; t < TL; ++t) {
+      const uint8_t* rec = vb + (size_t)min(m0 + tid + FT * t, a.cache_len - 1) * BPT;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ve[t][r][k] = *reinterpret_cast<const uint32_t*>(rec + r * 16 + 4 * ((k + q4) & 3));
+    }
   }
 
   // ---- softmax over the chunk ---------------------------------------------
@@ -368,23 +410,15 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   // row holds heads 0..3 as consecutive dwords, and no 32-bit half can carry into
   // its neighbour since a chunk's weights sum to at most C * 2^FXSHIFT = 2^31.
   {
-    const int g16 = tid & 15, h16 = (tid >> 4) & 1;
     uint32_t gb[FG];
 #pragma unroll
     for (int kj = 0; kj < FG; ++kj) gb[kj] = (uint32_t)(((kj + g16) & 15) * 16);
-    const uint8_t* vb = a.vcodes + ((size_t)b * a.v.Hkv + h) * (size_t)a.cache_len * BPT;
     const float fxs = (float)(1u << FXSHIFT);
-    const int q4 = (g16 >> 2) & 3, sh4 = g16 & 3;
 #pragma unroll
     for (int t = 0; t < TL; ++t) {
       const int m = m0 + tid + FT * t;
       if (m < L && m != skip_pos) {
-        const uint8_t* rec = vb + (size_t)m * BPT;
-        uint32_t e[R][4];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) e[r][k] = *reinterpret_cast<const uint32_t*>(rec + r * 16 + 4 * ((k + q4) & 3));
+        const uint32_t (&e)[R][4] = ve[t];
         // pair word 0 goes to heads 2 h16, 2 h16 + 1; word 1 to the other pair
         const uint64_t p01 = (uint64_t)(uint32_t)fmaf(s[t][0], fxs, 0.5f) |
                              ((uint64_t)(uint32_t)fmaf(s[t][1], fxs, 0.5f) << 32);
