@@ -35,13 +35,14 @@ WORKLOAD = "llama8b_ctx128k_1bit_64steps"
 PREFILL = 131008
 N_POSITIONS = 64
 
-# HBM bytes per launch of the decode kernel from rocprofv3 counters (FETCH_SIZE
-# and WRITE_SIZE, each scaled by what the counter reads on a plain streaming
-# kernel of known size; profiles/decode_fast_llama8b_ctx128k_1bit.md), valid for
-# the kernel sources whose SHA-256 is given: any change to them voids it.
-KERNEL_SOURCES = ['decode_fast.hip', 'decode_common.hpp', 'encode_common.hpp', 'commvq_internal.hpp']
-TRAFFIC = {"sha256": "a38feac76ef76ab5660025be26838f5419064c64d77871b94a7adf8b0a69d831",
-           "read_bytes": 36352340, "write_bytes": 601897}
+# HBM bytes per commvq_decode_step call (decode kernel + chunk-merge kernel) from
+# rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter
+# reads on a plain streaming kernel of known size; the commands and figures are
+# in the decode_fast summary under profiles/), valid for the kernel sources whose
+# SHA-256 is given: any change to them voids it.
+KERNEL_SOURCES = ['decode_fast.hip', 'decode_merge.hip', 'decode.hip', 'decode_common.hpp', 'encode_common.hpp', 'commvq_internal.hpp']
+TRAFFIC = {"sha256": "b955491c2f574e0bfd90d4f59eb92f1d48a3e3378c6a7251976745284170077f",
+           "read_bytes": 35903304, "write_bytes": 549376}
 
 
 def measured_traffic():
