@@ -157,6 +157,13 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   const int m0 = chunk * C;
   const size_t pstride = (size_t)a.n_chunks * (FD + 2);
   float* part = a.part + ((size_t)b * a.Hq + h * FNH) * pstride + (size_t)chunk * (FD + 2);
+  // the query pair this lane rotates (lanes < 256: head tid / 64, pair tid % 64),
+  // requested before anything else
+  const float2 qx = tid < FNH * FPR
+                        ? *reinterpret_cast<const float2*>(a.q + ((size_t)b * a.Hq + h * FNH + (tid >> 6)) * FD +
+                                                           2 * (tid & 63))
+                        : make_float2(0.f, 0.f);
+  const int qpos = a.q_pos[b];
   // decode step: the workgroup whose chunk holds the new position encodes the new
   // key and value of its KV head (all 32 group searches at once, 16 lanes each)
   // and writes the records; its table path leaves that position out and the
@@ -229,11 +236,9 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
 #pragma unroll
   for (int k = 0; k < NKCB; ++k) reinterpret_cast<u32x4*>(lds)[tid + FT * k] = kcv[k];
   if (tid < FNH * FPR) {
-    const int hh = tid >> 6, p = tid & 63;
-    const float* qrow = a.q + ((size_t)b * a.Hq + h * FNH + hh) * FD;
-    const float x = qrow[2 * p], y = qrow[2 * p + 1];
-    const float2 w = phase_hw((uint32_t)max(a.q_pos[b], 0), ph.lo[p], ph.hi[p]);
-    qz[tid] = make_float2(x * w.x - y * w.y, x * w.y + y * w.x);
+    const int p = tid & 63;
+    const float2 w = phase_hw((uint32_t)max(qpos, 0), ph.lo[p], ph.hi[p]);
+    qz[tid] = make_float2(qx.x * w.x - qx.y * w.y, qx.x * w.y + qx.y * w.x);
   }
 
   const bool fold = owner && pb < L;
@@ -295,8 +300,13 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     stp[u] = phase_hw((uint32_t)FT, ph.lo[p], ph.hi[p]);
   }
   float s[TL][FNH];
-#pragma unroll
-  for (int t = 0; t < TL; ++t) {
+  // Two wavefronts share each SIMD. The scheduler favours the older one, which
+  // would race ahead and leave the other to run alone (no latency hiding) at
+  // the end; a wavefront's issue priority instead falls as it advances through
+  // its blocks, so the pair stays interleaved.
+  static_for<TL>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    __builtin_amdgcn_s_setprio(3 - (4 * t) / TL);
     if constexpr (NB < TL) {
       if (t + 1 < TL) load_rec(t + 1, cw[(t + 1) % NB]);
     }
@@ -336,7 +346,8 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     });
 #pragma unroll
     for (int k = 0; k < FNH; ++k) s[t][k] = acc0[k] + acc1[k];
-  }
+  });
+  __builtin_amdgcn_s_setprio(0);
 
   // value records of the lane's positions, requested now so they arrive during
   // the softmax; dword k of round r is taken from slot (k + q4) & 3 (the lane's
