@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=16, help="layer slices rotated over (caches > MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    help="decode workload to time (default: the 128K 1-bit decode-step workload)")
     ap.add_argument("--encode", action="store_true",
                     help="time the prefill encoder instead (131072 tokens x 8 KV heads of K and V, 2-bit)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -197,6 +199,76 @@ def bench_encode(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_decode_workload(args):
+    """One commvq_decode_attention call per step over a whole decode workload
+    (every sequence and head), caches of seeded random records rotated over
+    layer slices whose total exceeds the Infinity Cache."""
+    import torch
+
+    from long_context_attention_commvq_amd import _lib, api, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    B, Hq, H, D, Lmax = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.context
+    kq = api.Quantizer(torch.from_numpy(synth.codebook(w.seed + 1, H, D, w.group_size, w.n_entries, w.n_rounds)).to(dev),
+                       w.group_size)
+    vq = api.Quantizer(torch.from_numpy(synth.codebook(w.seed + 2, H, D, w.group_size, w.n_entries, w.n_rounds)).to(dev),
+                       w.group_size)
+    bpt = kq.bytes_per_token
+    lens = (synth.ragged_lengths(w.seed + 5, B, *w.ragged) if w.ragged else np.full(B, Lmax)).astype(np.int32)
+    layer_bytes = 2 * B * H * Lmax * bpt
+    NL = max(1, min(args.layers, -(-(512 << 20) // layer_bytes)))
+    print(f"[bench] {args.workload}: {NL} layer slices of {layer_bytes / 2**20:.0f} MiB", file=sys.stderr, flush=True)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 40)
+    caches = [(torch.randint(0, 256, (B, H, Lmax, bpt), dtype=torch.uint8, device=dev, generator=g),
+               torch.randint(0, 256, (B, H, Lmax, bpt), dtype=torch.uint8, device=dev, generator=g)) for _ in range(NL)]
+    q = torch.from_numpy(synth.queries(w.seed + 42, B, Hq, D)).to(dev)
+    lens_d = torch.from_numpy(lens).to(dev)
+    qpos = lens_d - 1
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ws = api.DecodeWorkspace(kq, vq, B, Hq, Lmax, dev)
+    rope = _lib.make_rope(w.theta_base)
+    stream = torch.cuda.current_stream()
+    sid = stream.cuda_stream
+    sm = 1.0 / math.sqrt(D)
+
+    def call(i):
+        kc, vc = caches[i % NL]
+        _lib.commvq_decode_attention(kq.desc, vq.desc, rope, q.data_ptr(), qpos.data_ptr(), kc.data_ptr(),
+                                     vc.data_ptr(), lens_d.data_ptr(), B, Hq, Lmax, Lmax, sm, out.data_ptr(),
+                                     ws.buf.data_ptr(), ws.nbytes, 0, sid)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        call(args.warmup + i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    toks = int(lens.sum())
+    code_bytes = toks * H * 2 * bpt
+    achieved = code_bytes / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC, "value": toks / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "n_q_heads": Hq, "n_kv_heads": H, "head_dim": D,
+                   "context": Lmax, "sum_len": toks, "n_rounds": w.n_rounds, "layer_slices": NL,
+                   "step": "commvq_decode_attention over every sequence and head"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": code_bytes,
+                     "avg_launch_us": ms * 1e3,
+                     "kernel": "commvq_decode_attention call: decode kernel, then chunk-merge kernel"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -208,6 +280,9 @@ def main():
         return
     if args.encode:
         bench_encode(args)
+        return
+    if args.workload != WORKLOAD:
+        bench_decode_workload(args)
         return
     import torch
 
