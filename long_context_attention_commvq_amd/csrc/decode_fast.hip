@@ -164,6 +164,17 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
                                                            2 * (tid & 63))
                         : make_float2(0.f, 0.f);
   const int qpos = a.q_pos[b];
+  // turn counts of this lane's RoPE pair (pair = lane in the phase table and the
+  // query rotation) and of the four pairs whose block phases it carries; loaded
+  // first, the kernel-argument table being indexed per lane
+  const uint32_t flo = ph.lo[lane], fhi = ph.hi[lane];
+  uint32_t bflo[4], bfhi[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int p = 2 * (lane >> 2) + (u & 1) + 32 * (u >> 1);
+    bflo[u] = ph.lo[p];
+    bfhi[u] = ph.hi[p];
+  }
   // decode step: the workgroup whose chunk holds the new position encodes the new
   // key and value of its KV head (all 32 group searches at once, 16 lanes each)
   // and writes the records; its table path leaves that position out and the
@@ -228,16 +239,16 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   }
   // lane phases e^{i d theta_p}, d < 64: 16-byte chunk c (pairs 4c..4c+3) of row d
   // at slot (c + d) & 15, so the 64 lanes reading chunk c hit 16 different slots
+  // (i = tid + 512 k, so the pair i & 63 is the lane's own)
   for (int i = tid; i < 64 * FPR; i += FT) {
-    const int d = i >> 6, p = i & 63;
-    const float2 e = phase_hw((uint32_t)d, ph.lo[p], ph.hi[p]);
+    const int d = i >> 6, p = lane;
+    const float2 e = phase_hw((uint32_t)d, flo, fhi);
     pht[d * 64 + (((p >> 2) + d) & 15) * 4 + (p & 3)] = pack_h2(e.x, e.y);
   }
 #pragma unroll
   for (int k = 0; k < NKCB; ++k) reinterpret_cast<u32x4*>(lds)[tid + FT * k] = kcv[k];
   if (tid < FNH * FPR) {
-    const int p = tid & 63;
-    const float2 w = phase_hw((uint32_t)max(qpos, 0), ph.lo[p], ph.hi[p]);
+    const float2 w = phase_hw((uint32_t)max(qpos, 0), flo, fhi);  // pair tid & 63 = lane
     qz[tid] = make_float2(qx.x * w.x - qx.y * w.y, qx.x * w.y + qx.y * w.x);
   }
 
@@ -253,7 +264,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
         kx += (float)ce[0];
         ky += (float)ce[1];
       }
-      const float2 wk = phase_hw((uint32_t)pb, ph.lo[p], ph.hi[p]);
+      const float2 wk = phase_hw((uint32_t)pb, flo, fhi);  // p = lane
       const float krx = kx * wk.x - ky * wk.y, kry = kx * wk.y + ky * wk.x;
 #pragma unroll
       for (int k = 0; k < FNH; ++k) {
@@ -296,8 +307,8 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   for (int u = 0; u < 4; ++u) {
     const int p = 2 * bq + (u & 1) + 32 * (u >> 1);
     qv[u] = qz[qi * FPR + p];
-    eb[u] = phase_hw((uint32_t)(m0 + 64 * wave), ph.lo[p], ph.hi[p]);
-    stp[u] = phase_hw((uint32_t)FT, ph.lo[p], ph.hi[p]);
+    eb[u] = phase_hw((uint32_t)(m0 + 64 * wave), bflo[u], bfhi[u]);
+    stp[u] = phase_hw((uint32_t)FT, bflo[u], bfhi[u]);
   }
   float s[TL][FNH];
   // Two wavefronts share each SIMD. The scheduler favours the older one, which
