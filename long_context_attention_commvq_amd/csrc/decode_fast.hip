@@ -139,7 +139,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   constexpr int FXSHIFT = 31 - (C == 4096 ? 12 : C == 2048 ? 11 : 10);  // C * 2^FXSHIFT = 2^31
   static_assert(C <= 4096, "shape");
 
-  extern __shared__ uint4 fsm[];
+  __shared__ uint4 fsm[(131072 + AUX_BYTES) / 16];  // static: its LDS address (0) folds into offsets
   char* lds = reinterpret_cast<char*>(fsm);
   uint32_t* pht = reinterpret_cast<uint32_t*>(lds + Cfg::MAIN);       // [64][64] fp16 (cos, sin)
   float2* qz = reinterpret_cast<float2*>(lds + Cfg::MAIN + PHT_BYTES);  // [4][64] rotated query
@@ -214,6 +214,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     }
   };
   constexpr int NB = (R == 1) ? TL : 2;  // records in flight
+  constexpr int PD = (R == 1) ? 4 : 2;   // codebook gathers in flight (groups)
   uint32_t cw[NB][R][4];
 #pragma unroll
   for (int t = 0; t < NB - (NB < TL ? 1 : 0); ++t) load_rec(t, cw[t]);
@@ -321,6 +322,19 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     if constexpr (NB < TL) {
       if (t + 1 < TL) load_rec(t + 1, cw[(t + 1) % NB]);
     }
+    const uint32_t (&cr)[R][4] = cw[t % NB];
+    // codebook gathers run PD groups ahead of their use (rolling buffer), the
+    // first PD issued before the block's q' is formed
+    u32x4 zb[PD][R];
+    auto gather = [&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t off = byte_x16<j & 3>(cr[r][j >> 2]);  // code * 16
+        zb[j % PD][r] = *reinterpret_cast<const u32x4*>(lds + (size_t)(j * R + r) * FNC * 16 + off);
+      }
+    };
+    static_for<PD>(gather);
     if (t > 0) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -332,22 +346,15 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     for (int u = 0; u < 4; ++u)
       qa[u] = pack_h2(fmaf(qv[u].x, eb[u].x, qv[u].y * eb[u].y), fmaf(qv[u].y, eb[u].x, -qv[u].x * eb[u].y));
     const half4_t a_lo = as_h4(qa[0], qa[1]), a_hi = as_h4(qa[2], qa[3]);
-    const uint32_t (&cr)[R][4] = cw[t % NB];
     float4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     static_for<FG>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
-      u32x4 z;
+      u32x4 z = zb[j % PD][0];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const uint32_t off = byte_x16<j & 3>(cr[r][j >> 2]);  // code * 16
-        const u32x4 zr = *reinterpret_cast<const u32x4*>(lds + (size_t)(j * R + r) * FNC * 16 + off);
-        if (r == 0) {
-          z = zr;
-        } else {
+      for (int r = 1; r < R; ++r)
 #pragma unroll
-          for (int k = 0; k < 4; ++k) z[k] = add_h2(z[k], zr[k]);
-        }
-      }
+        for (int k = 0; k < 4; ++k) z[k] = add_h2(z[k], zb[j % PD][r][k]);
+      if constexpr (j + PD < FG) gather(std::integral_constant<int, j + PD>{});
       const uint32_t k0 = rotate_h2(z[0], el[4 * j]), k1 = rotate_h2(z[1], el[4 * j + 1]);
       const uint32_t k2 = rotate_h2(z[2], el[4 * j + 2]), k3 = rotate_h2(z[3], el[4 * j + 3]);
       // K-steps 2j (pairs 4j, 4j+1) and 2j + 1 (pairs 4j+2, 4j+3)
@@ -547,11 +554,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
 
 template <int R, int TL>
 hipError_t launch_fast_t(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
-  const size_t smem = FastCfg<R>::MAIN + AUX_BYTES;
-  static std::atomic<uint64_t> configured{0};
-  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&decode_fast_kernel<R, TL>), configured);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_fast_kernel<R, TL>), dim3(a.n_chunks * a.k.Hkv, a.B), dim3(FT), smem, stream, a, ph);
+  hipLaunchKernelGGL((decode_fast_kernel<R, TL>), dim3(a.n_chunks * a.k.Hkv, a.B), dim3(FT), 0, stream, a, ph);
   return hipGetLastError();
 }
 
