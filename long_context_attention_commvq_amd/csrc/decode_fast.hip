@@ -27,8 +27,8 @@
 //   histograms with 64-bit LDS integer atomics (two heads per add); lanes
 //   rotate over (group, head pair) to spread the adds over the banks. The
 //   histogram is contracted with the value codebook on MFMA
-//   (v_mfma_f32_4x4x4f16, 16 blocks = 8 groups x 2 dim quads, weights split into
-//   fp16 hi + lo parts).
+//   (v_mfma_f32_4x4x4f16; per wavefront, 16 blocks = 2 groups x 8 bin segments
+//   with two dimensions per lane; weights split into fp16 hi + lo parts).
 // The chunk's (max, sum, o) go to the workspace; a second kernel merges the
 // chunks of each (sequence, query head).
 
@@ -476,21 +476,22 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   // Value-codebook operands of the MFMA contraction below, requested as soon as
   // this lane's atomics are issued (the barrier wait hides part of their
   // latency; one head's codebook is shared by all its chunks, so these mostly
-  // hit L2). Wavefront w contracts groups 2w, 2w+1; its
-  // 16 MFMA blocks are 4 bin quarters x (2 groups x 2 dimension quads): lane
-  // (block mb = 4 mq + mg, column mi) takes bin quarter mq, group 2w + (mg >> 1),
-  // dimension me = 4 (mg & 1) + mi, and step st covers bins 4 st .. 4 st + 3 of
-  // its quarter (a bin is a (round, code) pair, r * 256 + code).
-  constexpr int NBIN = R * FNC, QBIN = NBIN / 4, NSTEP = QBIN / 4;
-  const int mbk = lane >> 2, mi = lane & 3, mq = mbk >> 2, mg = mbk & 3;
-  const int mgrp = 2 * wave + (mg >> 1), me = 4 * (mg & 1) + mi;
-  half4_t cvb[NSTEP];
+  // hit L2). Wavefront w contracts groups 2w, 2w+1; its 16 MFMA blocks are
+  // 2 groups x 8 bin segments: lane (block mb = 8 gsel + sg, column mi) takes
+  // group 2w + gsel, dimensions 2 mi and 2 mi + 1 (one dword per bin), and
+  // step st covers bins sg * SEG + 4 st .. + 3 (a bin is a (round, code) pair,
+  // r * 256 + code).
+  constexpr int NBIN = R * FNC, SEG = NBIN / 8, NSTEP = SEG / 4;
+  const int mbk = lane >> 2, mi = lane & 3, gsel = mbk >> 3, sg = mbk & 7;
+  const int mgrp = 2 * wave + gsel;
+  uint32_t cvw[NSTEP][4];
   {
-    const _Float16* cvg = a.vcb + ((size_t)h * FG + mgrp) * R * FNC * 8 + me;
+    const uint32_t* cvg =
+        reinterpret_cast<const uint32_t*>(a.vcb + ((size_t)h * FG + mgrp) * R * FNC * 8) + (sg * SEG) * 4 + mi;
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) cvb[st][u] = cvg[(size_t)(mq * QBIN + 4 * st + u) * 8];
+      for (int u = 0; u < 4; ++u) cvw[st][u] = cvg[(4 * st + u) * 4];
   }
 
   __syncthreads();
@@ -498,32 +499,41 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   // ---- histogram x value codebook on MFMA ---------------------------------
   // Per group: o[head][dim] = sum_bin H[head][bin] CV[bin][dim], the fixed-point
   // bins split into fp16 hi + lo parts (v_mfma_f32_4x4x4f16: A = H rows = heads,
-  // B = CV columns = dims, K = 4 bins per step). The four bin quarters' partial
-  // sums are then added across lanes 16 apart.
+  // B = CV columns = dims, K = 4 bins per step; the dword of a bin holds the
+  // lane's two dims, regrouped per dim with byte permutes). The eight segments'
+  // partial sums are then added across lanes 4, 8 and 16 apart.
   {
     const float inv = 1.0f / (float)(1u << FXSHIFT);
-    float4_t acc = {0.f, 0.f, 0.f, 0.f};
-    const char* hrow = lds + mgrp * 16 + mi * 4;  // bin rl of (group, head mi) at rl * 256
+    float4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    const char* hrow = lds + mgrp * 16 + mi * 4 + (size_t)(sg * SEG) * 256;  // bin rl at rl * 256
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
       half4_t ahi, alo;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint32_t hv = *reinterpret_cast<const uint32_t*>(hrow + (size_t)(mq * QBIN + 4 * st + u) * 256);
+        const uint32_t hv = *reinterpret_cast<const uint32_t*>(hrow + (size_t)(4 * st + u) * 256);
         const float x = (float)hv * inv;
         const _Float16 hi = (_Float16)x;
         ahi[u] = hi;
         alo[u] = (_Float16)(x - (float)hi);
       }
-      acc = __builtin_amdgcn_mfma_f32_4x4x4f16(ahi, cvb[st], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_4x4x4f16(alo, cvb[st], acc, 0, 0, 0);
+      const uint32_t(&w)[4] = cvw[st];
+      const half4_t b0 = as_h4(__builtin_amdgcn_perm(w[1], w[0], 0x05040100u), __builtin_amdgcn_perm(w[3], w[2], 0x05040100u));
+      const half4_t b1 = as_h4(__builtin_amdgcn_perm(w[1], w[0], 0x07060302u), __builtin_amdgcn_perm(w[3], w[2], 0x07060302u));
+      acc0 = __builtin_amdgcn_mfma_f32_4x4x4f16(ahi, b0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_4x4x4f16(ahi, b1, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_4x4x4f16(alo, b0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_4x4x4f16(alo, b1, acc1, 0, 0, 0);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      acc[k] += __shfl_xor(acc[k], 16, 64);
-      acc[k] += __shfl_xor(acc[k], 32, 64);
+#pragma unroll
+      for (int x = 4; x <= 16; x *= 2) {
+        acc0[k] += __shfl_xor(acc0[k], x, 64);
+        acc1[k] += __shfl_xor(acc1[k], x, 64);
+      }
     }
-    // acc[k] = o[head k][8 mgrp + me] (lanes 0..15)
+    // acc0[k], acc1[k] = o[head k][8 mgrp + 2 mi], o[head k][8 mgrp + 2 mi + 1] (lanes with sg = 0)
     // with the new token folded in (decode step owner): M' = max(M, s_new),
     // o' = o e^{M - M'} + v_new e^{s_new - M'}, l' = l e^{M - M'} + e^{s_new - M'}
     float al[FNH], be[FNH], Mf[FNH];
@@ -540,10 +550,14 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
         be[k] = 0.f;
       }
     }
-    if (lane < 16) {
-      const float vn = fold ? new_v[8 * mgrp + me] : 0.f;
+    if (sg == 0) {
+      const int dd = 8 * mgrp + 2 * mi;
+      const float vn0 = fold ? new_v[dd] : 0.f, vn1 = fold ? new_v[dd + 1] : 0.f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) part[k * pstride + 2 + 8 * mgrp + me] = acc[k] * al[k] + vn * be[k];
+      for (int k = 0; k < 4; ++k) {
+        part[k * pstride + 2 + dd] = acc0[k] * al[k] + vn0 * be[k];
+        part[k * pstride + 3 + dd] = acc1[k] * al[k] + vn1 * be[k];
+      }
     }
     if (tid < FNH) {
       part[tid * pstride + 0] = Mf[tid];
