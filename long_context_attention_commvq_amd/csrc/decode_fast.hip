@@ -65,6 +65,7 @@ constexpr int PHT_BYTES = 64 * FPR * 4;
 constexpr int NEW_BYTES = 64 + FNH * 4 + FD * 4;
 constexpr int AUX_BYTES = PHT_BYTES + FNH * FPR * 8 + 64 * 4 + NEW_BYTES;
 static_assert(131072 + AUX_BYTES <= 160 * 1024, "LDS budget");
+static_assert(FT == FNH * FD && PHT_BYTES >= FW * FNH * FD * 4, "contraction: one output per lane, wavefront partials in the phase table's space");
 static_assert(PHT_BYTES >= 4 * 4096, "value-codebook slabs reuse the lane phase table");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -434,6 +435,20 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     lsum[k] = acc;
   }
 
+  // Value-codebook operands of the MFMA contraction at the end, requested a
+  // slice per block of the histogram stage below, as that block's value records
+  // free their registers (one head's codebook is shared by all its chunks, so
+  // these mostly hit L2). Wavefront w contracts bins w * BPW .. + BPW - 1 (a bin
+  // is a (round, code) pair, r * 256 + code) of all 16 groups: MFMA block grp
+  // (lanes 4 grp .. 4 grp + 3) is group grp, its column mi two dimensions
+  // (2 mi, 2 mi + 1; one dword per bin), and step st covers 4 bins.
+  constexpr int NBIN = R * FNC, BPW = NBIN / FW, NSTEP = BPW / 4;
+  static_assert(NSTEP % TL == 0, "codebook slices per block");
+  const int mgrp = lane >> 2, mi = lane & 3;
+  uint32_t cvw[NSTEP][4];
+  const uint32_t* cvg =
+      reinterpret_cast<const uint32_t*>(a.vcb + ((size_t)h * FG + mgrp) * R * FNC * 8) + (wave * BPW) * 4 + mi;
+
   // ---- value histograms (LDS integer atomics) -----------------------------
   // One 64-bit add carries two query heads' weights: a (round, code, group) bin
   // row holds heads 0..3 as consecutive dwords, and no 32-bit half can carry into
@@ -471,41 +486,26 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
           }
         }
       }
+#pragma unroll
+      for (int st = t * (NSTEP / TL); st < (t + 1) * (NSTEP / TL); ++st)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) cvw[st][u] = cvg[(4 * st + u) * 4];
     }
   }
-  // Value-codebook operands of the MFMA contraction below, requested as soon as
-  // this lane's atomics are issued (the barrier wait hides part of their
-  // latency; one head's codebook is shared by all its chunks, so these mostly
-  // hit L2). Wavefront w contracts groups 2w, 2w+1; its 16 MFMA blocks are
-  // 2 groups x 8 bin segments: lane (block mb = 8 gsel + sg, column mi) takes
-  // group 2w + gsel, dimensions 2 mi and 2 mi + 1 (one dword per bin), and
-  // step st covers bins sg * SEG + 4 st .. + 3 (a bin is a (round, code) pair,
-  // r * 256 + code).
-  constexpr int NBIN = R * FNC, SEG = NBIN / 8, NSTEP = SEG / 4;
-  const int mbk = lane >> 2, mi = lane & 3, gsel = mbk >> 3, sg = mbk & 7;
-  const int mgrp = 2 * wave + gsel;
-  uint32_t cvw[NSTEP][4];
-  {
-    const uint32_t* cvg =
-        reinterpret_cast<const uint32_t*>(a.vcb + ((size_t)h * FG + mgrp) * R * FNC * 8) + (sg * SEG) * 4 + mi;
-#pragma unroll
-    for (int st = 0; st < NSTEP; ++st)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) cvw[st][u] = cvg[(4 * st + u) * 4];
-  }
-
   __syncthreads();
 
   // ---- histogram x value codebook on MFMA ---------------------------------
   // Per group: o[head][dim] = sum_bin H[head][bin] CV[bin][dim], the fixed-point
   // bins split into fp16 hi + lo parts (v_mfma_f32_4x4x4f16: A = H rows = heads,
   // B = CV columns = dims, K = 4 bins per step; the dword of a bin holds the
-  // lane's two dims, regrouped per dim with byte permutes). The eight segments'
-  // partial sums are then added across lanes 4, 8 and 16 apart.
+  // lane's two dims, regrouped per dim with byte permutes). The 64 lanes of a
+  // histogram read hit 16 groups x 4 heads, 64 distinct banks. The eight
+  // wavefronts' partial sums are added through LDS (the lane phase table's
+  // space, unused since the set-up).
   {
     const float inv = 1.0f / (float)(1u << FXSHIFT);
     float4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    const char* hrow = lds + mgrp * 16 + mi * 4 + (size_t)(sg * SEG) * 256;  // bin rl at rl * 256
+    const char* hrow = lds + mgrp * 16 + mi * 4 + (size_t)(wave * BPW) * 256;  // bin rl at rl * 256
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
       half4_t ahi, alo;
@@ -525,17 +525,19 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
       acc0 = __builtin_amdgcn_mfma_f32_4x4x4f16(alo, b0, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_4x4x4f16(alo, b1, acc1, 0, 0, 0);
     }
+    // acc0[k], acc1[k] = this wavefront's part of o[head k][8 mgrp + 2 mi], o[head k][8 mgrp + 2 mi + 1]
+    float* osum = reinterpret_cast<float*>(pht);  // [wavefront][head][dim]
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-#pragma unroll
-      for (int x = 4; x <= 16; x *= 2) {
-        acc0[k] += __shfl_xor(acc0[k], x, 64);
-        acc1[k] += __shfl_xor(acc1[k], x, 64);
-      }
-    }
-    // acc0[k], acc1[k] = o[head k][8 mgrp + 2 mi], o[head k][8 mgrp + 2 mi + 1] (lanes with sg = 0)
+    for (int k = 0; k < FNH; ++k)
+      *reinterpret_cast<float2*>(osum + (wave * FNH + k) * FD + 8 * mgrp + 2 * mi) = make_float2(acc0[k], acc1[k]);
+    __syncthreads();
+    // lane tid: head tid / 128, dimension tid % 128, summed over the wavefronts;
     // with the new token folded in (decode step owner): M' = max(M, s_new),
     // o' = o e^{M - M'} + v_new e^{s_new - M'}, l' = l e^{M - M'} + e^{s_new - M'}
+    const int ok_ = tid >> 7, od = tid & (FD - 1);
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < FW; ++w) o += osum[(w * FNH + ok_) * FD + od];
     float al[FNH], be[FNH], Mf[FNH];
 #pragma unroll
     for (int k = 0; k < FNH; ++k) {
@@ -550,14 +552,16 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
         be[k] = 0.f;
       }
     }
-    if (sg == 0) {
-      const int dd = 8 * mgrp + 2 * mi;
-      const float vn0 = fold ? new_v[dd] : 0.f, vn1 = fold ? new_v[dd + 1] : 0.f;
+    {
+      const float vn = fold ? new_v[od] : 0.f;
+      float alk = al[0], bek = be[0];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        part[k * pstride + 2 + dd] = acc0[k] * al[k] + vn0 * be[k];
-        part[k * pstride + 3 + dd] = acc1[k] * al[k] + vn1 * be[k];
-      }
+      for (int k = 1; k < FNH; ++k)
+        if (ok_ == k) {
+          alk = al[k];
+          bek = be[k];
+        }
+      part[ok_ * pstride + 2 + od] = o * alk + vn * bek;
     }
     if (tid < FNH) {
       part[tid * pstride + 0] = Mf[tid];
