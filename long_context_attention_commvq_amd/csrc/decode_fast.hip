@@ -54,8 +54,12 @@ struct FastCfg {
   static constexpr int BPT = 16 * R;                   // bytes per packed record
   static constexpr int KCB = R * FG * FNC * 16;        // key codebook bytes (64 KiB per round)
   static constexpr int HIST = R * FNC * FG * FNH * 4;  // histogram bytes (64 KiB per round)
-  static constexpr int MAIN = 131072;                  // LDS region holding one, then the other
-  static_assert(KCB <= MAIN && HIST <= MAIN, "layout");
+  static constexpr int MAIN = 131072;                  // LDS region for both
+  // R = 1: the histogram sits beside the key codebook, each wavefront clearing
+  // its slice as it leaves the score loop; R = 2: it replaces the codebook once
+  // all scores are done
+  static constexpr int HOFF = R == 1 ? KCB : 0;
+  static_assert(HOFF + HIST <= MAIN && KCB <= MAIN && (R == 2 || HOFF >= KCB), "layout");
 };
 
 // aux LDS: lane phases [64 offsets][64 pairs] fp16 (16-byte chunks swizzled),
@@ -387,7 +391,16 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   }
 
   // ---- softmax over the chunk ---------------------------------------------
-  float M[FNH], lsum[FNH];
+  // Each wavefront exponentiates against its own maximum M_w before the
+  // workgroup's M is known (while slower wavefronts finish their scores); the
+  // factor e^{M_w - M} then enters the fixed-point scale of the histogram stage,
+  // and the wavefront sums are combined with it at the end.
+  float M[FNH], fw[FNH], lsum[FNH];
+  if constexpr (Cfg::HOFF >= Cfg::KCB) {
+    uint4* hs = reinterpret_cast<uint4*>(lds + Cfg::HOFF) + wave * (Cfg::HIST / 16 / FW);
+#pragma unroll
+    for (int i = 0; i < Cfg::HIST / 16 / FT; ++i) hs[lane + 64 * i] = make_uint4(0, 0, 0, 0);
+  }
 #pragma unroll
   for (int t = 0; t < TL; ++t) {
     const int mt = m0 + tid + FT * t;
@@ -401,7 +414,20 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
 #pragma unroll
     for (int t = 0; t < TL; ++t) mx = fmaxf(mx, s[t][k]);
     mx = wave_max(mx);
-    if (lane == 0) red[k * FW + wave] = mx;
+    fw[k] = mx;
+    const float ref = mx == -INFINITY ? 0.f : mx;  // a wavefront may hold only masked positions
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < TL; ++t) {
+      const float pw = __expf(s[t][k] - ref);  // exp(-inf) = 0 for masked positions
+      s[t][k] = pw;
+      acc += pw;
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      red[k * FW + wave] = mx;
+      red[32 + k * FW + wave] = acc;
+    }
   }
   __syncthreads();  // also: every lane is done with the key codebook
 #pragma unroll
@@ -410,29 +436,28 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
 #pragma unroll
     for (int w = 1; w < FW; ++w) mx = fmaxf(mx, red[k * FW + w]);
     M[k] = mx;
+    fw[k] = fw[k] == -INFINITY ? 0.f : __expf(fw[k] - mx);
   }
-  // zero the histograms while the weights are formed
-  for (int i = tid; i < Cfg::HIST / 16; i += FT) reinterpret_cast<uint4*>(lds)[i] = make_uint4(0, 0, 0, 0);
+  // the chunk's sums: lane l < 32 scales wavefront l % 8's sum of head l / 8
+  // from its own maximum, and the eight terms of a head are added in a row
+  {
+    const int kk = (lane >> 3) & 3, ww = lane & 7;
+    const float mw = red[kk * FW + ww], mk = red[kk * FW];
+    float mkx = mk;
 #pragma unroll
-  for (int k = 0; k < FNH; ++k) {
-    float acc = 0.f;
-    const float ref = M[k] == -INFINITY ? 0.f : M[k];  // a chunk may hold only the skipped new position
+    for (int w = 1; w < FW; ++w) mkx = fmaxf(mkx, red[kk * FW + w]);
+    float term = (lane < 32 && mw != -INFINITY) ? red[32 + kk * FW + ww] * __expf(mw - mkx) : 0.f;
+    term += dpp_f<0xb1>(term);   // quad_perm [1,0,3,2]
+    term += dpp_f<0x4e>(term);   // quad_perm [2,3,0,1]
+    term += __shfl_xor(term, 4, 64);
 #pragma unroll
-    for (int t = 0; t < TL; ++t) {
-      const float pw = __expf(s[t][k] - ref);  // exp(-inf) = 0 for masked positions
-      s[t][k] = pw;
-      acc += pw;
-    }
-    acc = wave_sum(acc);
-    if (lane == 0) red[32 + k * FW + wave] = acc;
+    for (int k = 0; k < FNH; ++k)
+      lsum[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, term), 8 * k));
   }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < FNH; ++k) {
-    float acc = 0.f;
-#pragma unroll
-    for (int w = 0; w < FW; ++w) acc += red[32 + k * FW + w];
-    lsum[k] = acc;
+  if constexpr (Cfg::HOFF < Cfg::KCB) {
+    // the histograms replace the key codebook
+    for (int i = tid; i < Cfg::HIST / 16; i += FT) reinterpret_cast<uint4*>(lds + Cfg::HOFF)[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
   }
 
   // Value-codebook operands of the MFMA contraction at the end, requested a
@@ -457,17 +482,19 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     uint32_t gb[FG];
 #pragma unroll
     for (int kj = 0; kj < FG; ++kj) gb[kj] = (uint32_t)(((kj + g16) & 15) * 16);
-    const float fxs = (float)(1u << FXSHIFT);
+    float fxk[FNH];  // fixed-point scale with the wavefront's factor e^{M_w - M}
+#pragma unroll
+    for (int k = 0; k < FNH; ++k) fxk[k] = (float)(1u << FXSHIFT) * fw[k];
 #pragma unroll
     for (int t = 0; t < TL; ++t) {
       const int m = m0 + tid + FT * t;
       if (m < L && m != skip_pos) {
         const uint32_t (&e)[R][4] = ve[t];
         // pair word 0 goes to heads 2 h16, 2 h16 + 1; word 1 to the other pair
-        const uint64_t p01 = (uint64_t)(uint32_t)fmaf(s[t][0], fxs, 0.5f) |
-                             ((uint64_t)(uint32_t)fmaf(s[t][1], fxs, 0.5f) << 32);
-        const uint64_t p23 = (uint64_t)(uint32_t)fmaf(s[t][2], fxs, 0.5f) |
-                             ((uint64_t)(uint32_t)fmaf(s[t][3], fxs, 0.5f) << 32);
+        const uint64_t p01 = (uint64_t)(uint32_t)fmaf(s[t][0], fxk[0], 0.5f) |
+                             ((uint64_t)(uint32_t)fmaf(s[t][1], fxk[1], 0.5f) << 32);
+        const uint64_t p23 = (uint64_t)(uint32_t)fmaf(s[t][2], fxk[2], 0.5f) |
+                             ((uint64_t)(uint32_t)fmaf(s[t][3], fxk[3], 0.5f) << 32);
         const uint64_t pw[2] = {h16 ? p23 : p01, h16 ? p01 : p23};
         const uint32_t hoff0 = (uint32_t)(h16 * 8), hoff1 = (uint32_t)((1 - h16) * 8);
 #pragma unroll
@@ -479,10 +506,10 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
           for (int kj = 0; kj < FG; ++kj) {
             const uint32_t code = (x[kj >> 2] >> (8 * (kj & 3))) & 0xffu;
             const uint32_t row = ((uint32_t)(r * FNC) + code) * 256u + gb[kj];
-            __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(lds + row + hoff0), pw[0], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
-            __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(lds + row + hoff1), pw[1], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(lds + Cfg::HOFF + row + hoff0), pw[0],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(lds + Cfg::HOFF + row + hoff1), pw[1],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
           }
         }
       }
@@ -505,7 +532,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   {
     const float inv = 1.0f / (float)(1u << FXSHIFT);
     float4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    const char* hrow = lds + mgrp * 16 + mi * 4 + (size_t)(wave * BPW) * 256;  // bin rl at rl * 256
+    const char* hrow = lds + Cfg::HOFF + mgrp * 16 + mi * 4 + (size_t)(wave * BPW) * 256;  // bin rl at rl * 256
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
       half4_t ahi, alo;
