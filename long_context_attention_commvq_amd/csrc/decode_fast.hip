@@ -305,15 +305,16 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   // MFMA A operand (q'): instruction k (K-step k = pairs 2k, 2k+1) broadcasts
   // block k % 16's A to all 16 blocks (CBSZ = 4, ABID = k % 16), so lane
   // (block bq, row qi) only holds head qi's q' for K-steps bq and bq + 16: pairs
-  // 2 bq, 2 bq + 1, 2 bq + 32, 2 bq + 33. Their block phases e^{i m_b theta_p}
-  // advance by e^{i 512 theta_p} per block from an exact start (fp32).
+  // 2 bq, 2 bq + 1, 2 bq + 32, 2 bq + 33. They start from an exact block phase
+  // and advance as q' <- q' conj(e^{i 512 theta_p}) per block (fp32).
   const int qi = lane & 3, bq = lane >> 2;
-  float2 qv[4], eb[4], stp[4];
+  float2 qf[4], stp[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int p = 2 * bq + (u & 1) + 32 * (u >> 1);
-    qv[u] = qz[qi * FPR + p];
-    eb[u] = phase_hw((uint32_t)(m0 + 64 * wave), bflo[u], bfhi[u]);
+    const float2 qv = qz[qi * FPR + p];
+    const float2 eb = phase_hw((uint32_t)(m0 + 64 * wave), bflo[u], bfhi[u]);
+    qf[u] = make_float2(fmaf(qv.x, eb.x, qv.y * eb.y), fmaf(qv.y, eb.x, -qv.x * eb.y));
     stp[u] = phase_hw((uint32_t)FT, bflo[u], bfhi[u]);
   }
   float s[TL][FNH];
@@ -343,13 +344,12 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     if (t > 0) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        eb[u] = make_float2(fmaf(eb[u].x, stp[u].x, -eb[u].y * stp[u].y), fmaf(eb[u].x, stp[u].y, eb[u].y * stp[u].x));
+        qf[u] = make_float2(fmaf(qf[u].x, stp[u].x, qf[u].y * stp[u].y), fmaf(qf[u].y, stp[u].x, -qf[u].x * stp[u].y));
     }
     // q' = q~ conj(e_b) as fp16 (re, im); qa[0..1]: K-step bq, qa[2..3]: K-step bq + 16
     uint32_t qa[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      qa[u] = pack_h2(fmaf(qv[u].x, eb[u].x, qv[u].y * eb[u].y), fmaf(qv[u].y, eb[u].x, -qv[u].x * eb[u].y));
+    for (int u = 0; u < 4; ++u) qa[u] = pack_h2(qf[u].x, qf[u].y);
     const half4_t a_lo = as_h4(qa[0], qa[1]), a_hi = as_h4(qa[2], qa[3]);
     float4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     static_for<FG>([&](auto jc) {
