@@ -104,7 +104,8 @@ int64_t commvq_code_bytes_per_token(const commvq_codebook* cb);
 
 /* Workspace bytes that commvq_decode_attention / commvq_decode_step need for
  * this shape: the split-context partials, (max, sum, o[D]) fp32 per (sequence,
- * query head, chunk of positions), sized for every flags value; negative
+ * query head, chunk of positions), then a decode step's new-token terms (192
+ * fp32 per (sequence, KV head)), sized for every flags value; negative
  * commvq_status on invalid arguments. */
 int64_t commvq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
                                       const commvq_codebook* kcb, const commvq_codebook* vcb);
@@ -171,8 +172,10 @@ int32_t commvq_decode_attention(const commvq_codebook* kcb, const commvq_codeboo
  *   kcodes, vcodes are written (the new records) and read.
  * Other arguments as commvq_decode_attention. For the shapes of the fast kernel
  * (D 128, g 8, Nc' 256, four query heads per KV head, R 1 or 2) the new token is
- * encoded inside the attention kernel: the step is that kernel plus the chunk
- * merge, as for commvq_decode_attention.
+ * encoded inside the attention kernel (R = 1: its 32 group searches spread over
+ * the KV head's workgroups, the token joining in the chunk merge; R = 2: by the
+ * workgroup whose chunk holds the position): the step is that kernel plus the
+ * chunk merge, as for commvq_decode_attention.
  * Pages: abstract (each new K/V vector is encoded to a low-bit code); "What
  * carries the argument" (shared index per group, R residual rounds, codebook
  * factors reused over cached positions). */

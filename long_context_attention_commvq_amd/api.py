@@ -70,7 +70,7 @@ class DecodeWorkspace:
         if n < 0:
             raise _lib.CommvqError(int(n), _lib.commvq_last_error())
         self.nbytes = int(n)
-        # chunk partials only: no initialisation needed
+        # chunk partials and new-token terms: no initialisation needed
         self.buf = torch.empty(max(self.nbytes, 256), dtype=torch.uint8, device=device)
 
 

@@ -297,6 +297,8 @@ int32_t decode_impl(const commvq_codebook* kcb, const commvq_codebook* vcb, cons
   a.kcb = static_cast<const _Float16*>(kcb->entries);
   a.vcb = static_cast<const _Float16*>(vcb->entries);
   a.part = static_cast<float*>(workspace);
+  a.newtok = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      commvq::decode_newtok_offset(k, batch, n_q_heads, max_seq_len, 1024));
   a.out = out;
   a.B = batch;
   a.Hq = n_q_heads;
@@ -319,6 +321,7 @@ int32_t decode_impl(const commvq_codebook* kcb, const commvq_codebook* vcb, cons
     a.positions = step->positions;
     a.kcodes_w = const_cast<uint8_t*>(kcodes);
     a.vcodes_w = const_cast<uint8_t*>(vcodes);
+    a.fold_new = k.R == 1 ? 1 : 0;  // R = 1: the merge kernel adds the new token
   } else if (step) {
     for (int kv = 0; kv < 2 && e == hipSuccess; ++kv) {
       const commvq::CbShape& sh = kv ? v : k;

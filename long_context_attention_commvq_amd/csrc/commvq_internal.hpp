@@ -36,6 +36,8 @@ struct PhaseTable {
   uint32_t hi[kMaxPairs];
 };
 
+constexpr int kFastNewTokFloats = 16 * 4 + 128;
+
 struct DecodeArgs {
   const float* q;
   const int32_t* q_pos;
@@ -52,14 +54,16 @@ struct DecodeArgs {
   uint8_t* kcodes_w;
   uint8_t* vcodes_w;
   float* part;         // [B][Hq][n_chunks][D + 2]: (max, sum, o[D]) per chunk
+  // decode step on the fast R = 1 kernel: [B][Hkv][kFastNewTokFloats], the new
+  // key's per-group products q~.k~ [16][4] and its value [128], which the merge
+  // kernel adds as one more chunk (fold_new set)
+  float* newtok;
+  int fold_new;
   float* out;          // [B][Hq][D]
   int B, Hq, NH, cache_len, max_len, n_chunks, chunk;
   float sm_scale;
   CbShape k, v;
 };
-
-// Step multipliers of the fast decode kernel: a lane advances by 512 positions
-// per owned position, so its phase is multiplied by e^{i 512 theta_p}.
 
 // Chunk length (tokens per workgroup) chosen for a decode shape; the workspace
 // query and the launch use the same rule.
@@ -79,6 +83,8 @@ inline hipError_t allow_full_lds(const void* kernel, std::atomic<uint64_t>& done
 int decode_chunk_len(const CbShape& k, const CbShape& v, int B, int Hq, int max_len, int flags);
 bool decode_fast_path(const CbShape& k, const CbShape& v, int NH, int flags);
 size_t decode_workspace_bytes(const CbShape& k, int B, int Hq, int max_len, int chunk);
+// Byte offset of the new-token area in the workspace (after the partials, 256-aligned).
+size_t decode_newtok_offset(const CbShape& k, int B, int Hq, int max_len, int chunk);
 hipError_t launch_decode_fast(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream);
 
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t stream);

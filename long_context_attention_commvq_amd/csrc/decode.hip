@@ -250,10 +250,16 @@ int decode_chunk_len(const CbShape& k, const CbShape& v, int B, int Hq, int max_
   return 1024;
 }
 
-size_t decode_workspace_bytes(const CbShape& k, int B, int Hq, int max_len, int chunk) {
+size_t decode_newtok_offset(const CbShape& k, int B, int Hq, int max_len, int chunk) {
   // chunk partials [B][Hq][n_chunks][D + 2]: (max, sum, o[D]) of one chunk
   const size_t n_chunks = (size_t)(max_len + chunk - 1) / chunk;
-  return (size_t)B * Hq * n_chunks * (k.D + 2) * sizeof(float);
+  return ((size_t)B * Hq * n_chunks * (k.D + 2) * sizeof(float) + 255) / 256 * 256;
+}
+
+size_t decode_workspace_bytes(const CbShape& k, int B, int Hq, int max_len, int chunk) {
+  // the partials, then a decode step's new-token area [B][Hkv][kFastNewTokFloats]
+  return decode_newtok_offset(k, B, Hq, max_len, chunk) +
+         ((size_t)B * k.Hkv * kFastNewTokFloats * sizeof(float) + 255) / 256 * 256;
 }
 
 hipError_t launch_decode_generic(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {

@@ -66,6 +66,10 @@ struct FastCfg {
 // rotated query [4][64], reductions [64], and a decode step's new token:
 // codes [2][2][16], scores [4], value [128]
 constexpr int PHT_BYTES = 64 * FPR * 4;
+// decode step, R = 1: per (sequence, KV head) the new key's group products
+// q~.k~ [16 groups][4 heads], then its value [128]
+constexpr int NEWTOK_FLOATS = kFastNewTokFloats;
+static_assert(NEWTOK_FLOATS == FG * FNH + FD, "new-token record");
 constexpr int NEW_BYTES = 64 + FNH * 4 + FD * 4;
 constexpr int AUX_BYTES = PHT_BYTES + FNH * FPR * 8 + 64 * 4 + NEW_BYTES;
 static_assert(131072 + AUX_BYTES <= 160 * 1024, "LDS budget");
@@ -136,6 +140,52 @@ __device__ __forceinline__ half4_t as_h4(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(half4_t, (u32x2){lo, hi});
 }
 
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+
+// Decode step, R = 1: one group of the new token's key or value searched by a
+// wavefront over entries l = lane + 64 k held in ent[k]. The input is fp16, so
+// e.c and |c|^2 are fp32 sums of exact fp16 products (v_dot2_f32_f16), and
+// score(c) = |c|^2 / 2 - e.c orders the entries as |e - c|^2; lowest index on
+// ties. Returns the chosen entry and leaves its eight values in win (every lane).
+__device__ __forceinline__ int search_row64_dot(const half2_t (&e2)[4], const h8_t (&ent)[4], int lane, u32x4& win) {
+  float best = INFINITY;
+  int bi = 0x7fffffff;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float ec = 0.f, cc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const half2_t c2 = {ent[k][2 * i], ent[k][2 * i + 1]};
+      ec = __builtin_amdgcn_fdot2(e2[i], c2, ec, false);
+      cc = __builtin_amdgcn_fdot2(c2, c2, cc, false);
+    }
+    const float sc = fmaf(cc, 0.5f, -ec);
+    if (sc < best) {
+      best = sc;
+      bi = lane + 64 * k;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float od = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (od < best || (od == best && oi < bi)) {
+      best = od;
+      bi = oi;
+    }
+  }
+  if (bi == 0x7fffffff) bi = 0;  // (no score below +inf: non-finite input)
+  // the winner's entry sits in lane bi % 64, slot bi / 64
+  const int ks = bi >> 6;
+  const u32x4 mine = __builtin_bit_cast(u32x4, ks == 0 ? ent[0] : ks == 1 ? ent[1] : ks == 2 ? ent[2] : ent[3]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t mi = mine[i];
+    win[i] = (uint32_t)__shfl((int)mi, bi & 63, 64);
+  }
+  return bi;
+}
+
 template <int R, int TL>
 __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseTable ph) {
   using Cfg = FastCfg<R>;
@@ -180,14 +230,77 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     bflo[u] = ph.lo[p];
     bfhi[u] = ph.hi[p];
   }
-  // decode step: the workgroup whose chunk holds the new position encodes the new
-  // key and value of its KV head (all 32 group searches at once, 16 lanes each)
-  // and writes the records; its table path leaves that position out and the
-  // token joins the chunk's partial with an exact fp32 score at the end
+  // decode step: the workgroup whose chunk holds the new position leaves that
+  // position out of its table path (its record is being written). R = 2: that
+  // workgroup encodes the new key and value of its KV head (all 32 group
+  // searches at once, 16 lanes each), writes the records, and the token joins
+  // the chunk's partial with an exact fp32 score at the end.
   const int pb = a.k_new ? a.positions[b] : -1;
   const bool appended = a.k_new && pb >= 0 && pb < a.cache_len;
   const int skip_pos = appended ? pb : -1;
-  const bool owner = appended && chunk == min(pb / C, a.n_chunks - 1);
+  const bool owner = R != 1 && appended && chunk == min(pb / C, a.n_chunks - 1);
+  // R = 1: the 32 searches (K, then V, of the 16 groups) are spread over the
+  // head's workgroups: slot i of the workgroup of chunk c takes search
+  // c + i * n_chunks, and wavefront w the slots w, w + 8, ... The first slot's
+  // inputs are loaded here, the search runs after the set-up, and the results
+  // go to the record and to the workspace, where the merge kernel adds the new
+  // token as one more chunk (its score from the 16 group products, its value).
+  auto row_of = [&](int it) { return chunk + (wave + FW * it) * a.n_chunks; };
+  half2_t rx[4];
+  h8_t rent[4];
+  float2 rq = make_float2(0.f, 0.f);
+  uint32_t rlo = 0, rhi = 0;
+  auto row_load = [&](int rho) {
+    const int rkv = rho >= FG ? 1 : 0, rj = rho & (FG - 1);
+    const half2_t* x = reinterpret_cast<const half2_t*>((rkv ? a.v_new : a.k_new) + ((size_t)b * a.k.Hkv + h) * FD + rj * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rx[i] = x[i];
+    const _Float16* cbg = (rkv ? a.vcb : a.kcb) + ((size_t)h * FG + rj) * FNC * 8;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) rent[k] = *reinterpret_cast<const h8_t*>(cbg + (size_t)(lane + 64 * k) * 8);
+    if (!rkv && lane < 16) {  // lane (head lane / 4, pair 4 rj + lane % 4): the query pair and its turn counts
+      const int p = 4 * rj + (lane & 3);
+      rq = *reinterpret_cast<const float2*>(a.q + ((size_t)b * a.Hq + h * FNH + (lane >> 2)) * FD + 2 * p);
+      rlo = ph.lo[p];
+      rhi = ph.hi[p];
+    }
+  };
+  const bool rowjob = R == 1 && appended && row_of(0) < 2 * FG;
+  if (rowjob) row_load(row_of(0));
+  auto row_job = [&]() {
+    if (!(R == 1 && appended)) return;
+    for (int it = 0; it < 4; ++it) {
+      const int rho = row_of(it);
+      if (rho >= 2 * FG) break;
+      if (it > 0) row_load(rho);
+      const int rkv = rho >= FG ? 1 : 0, rj = rho & (FG - 1);
+      u32x4 win;
+      const int code = search_row64_dot(rx, rent, lane, win);
+      if (lane == 0) (rkv ? a.vcodes_w : a.kcodes_w)[(((size_t)b * a.k.Hkv + h) * a.cache_len + pb) * BPT + rj] = (uint8_t)code;
+      float* nt = a.newtok + ((size_t)b * a.k.Hkv + h) * NEWTOK_FLOATS;
+      if (rkv) {
+        if (lane < 8) {
+          const int u = lane >> 1;
+          const uint32_t w2 = u == 0 ? win[0] : u == 1 ? win[1] : u == 2 ? win[2] : win[3];
+          const half2_t vh = __builtin_bit_cast(half2_t, w2);  // (a scalar copy: bit_cast of a vector element misreads)
+          nt[FG * FNH + 8 * rj + lane] = (float)((lane & 1) ? vh.y : vh.x);
+        }
+      } else {
+        // q~_p k~_p for lane (head lane / 4, pair lane % 4), both rotations in fp32
+        const int u = lane & 3;
+        const uint32_t kw = u == 0 ? win[0] : u == 1 ? win[1] : u == 2 ? win[2] : win[3];
+        const half2_t kp = __builtin_bit_cast(half2_t, kw);
+        const float2 wq = phase_hw((uint32_t)max(qpos, 0), rlo, rhi), wk = phase_hw((uint32_t)pb, rlo, rhi);
+        const float qx2 = rq.x * wq.x - rq.y * wq.y, qy2 = rq.x * wq.y + rq.y * wq.x;
+        const float kx = (float)kp.x, ky = (float)kp.y;
+        const float kx2 = kx * wk.x - ky * wk.y, ky2 = kx * wk.y + ky * wk.x;
+        float c = qx2 * kx2 + qy2 * ky2;
+        c += __shfl_xor(c, 1, 64);
+        c += __shfl_xor(c, 2, 64);
+        if (lane < 16 && u == 0) nt[rj * FNH + (lane >> 2)] = c;
+      }
+    }
+  };
   if (owner) {
     const int row = tid >> 4, kv = row / FG, j = row % FG;
     const _Float16* x = (kv ? a.v_new : a.k_new) + ((size_t)b * a.k.Hkv + h) * FD + j * 8;
@@ -241,6 +354,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
       const int hh = i / (FD + 2), k = i % (FD + 2);
       part[hh * pstride + k] = (k == 0) ? -INFINITY : 0.f;
     }
+    row_job();
     return;
   }
   // lane phases e^{i d theta_p}, d < 64: 16-byte chunk c (pairs 4c..4c+3) of row d
@@ -288,6 +402,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     }
   }
   __syncthreads();  // codebook, lane phases and rotated query visible
+  row_job();
 
   // lane constants: e^{i lane theta_p} for the 64 pairs (packed fp16)
   uint32_t el[FPR];

@@ -5,7 +5,9 @@
 // the standard combination of softmax partials over disjoint position ranges.
 // Running it as its own kernel (ordered after the decode kernel on the stream)
 // publishes the partials at the kernel boundary, instead of one release per
-// workgroup across the XCDs' separate L2 caches.
+// workgroup across the XCDs' separate L2 caches. In a decode step on the fast
+// 1-bit kernel the new token enters here as one more chunk: m = its scaled
+// score (the sum of its 16 group products), l = 1, o = its value.
 
 #include "decode_common.hpp"
 
@@ -19,10 +21,10 @@ constexpr int kMergeThreads = 256;
 // any (one memory round trip per batch; batches are combined with a running max
 // and rescaling). The lanes sharing a dimension are combined the same way
 // through LDS.
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float* __restrict__ part,
-                                                                     float* __restrict__ out, int n_chunks, int D,
-                                                                     int Hq) {
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
   __shared__ float sm[3][kMergeThreads];
+  const float* __restrict__ part = a.part;
+  const int n_chunks = a.n_chunks, D = a.k.D, Hq = a.Hq;
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const size_t cs = (size_t)D + 2;
   const float* pr = part + ((size_t)b * Hq + hq) * (size_t)n_chunks * cs;
@@ -64,17 +66,27 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
   sm[2][tid] = acc;
   __syncthreads();
   if (active && sub == 0) {
-    for (int k = 1; k < lpd; ++k) {
-      const float mk = sm[0][tid + k * D];
+    auto add = [&](float mk, float lk, float ok) {
       if (mk > -INFINITY) {
         const float Mn = fmaxf(M, mk);
-        const float a = M > -INFINITY ? __expf(M - Mn) : 0.f, w = __expf(mk - Mn);
-        l = fmaf(l, a, w * sm[1][tid + k * D]);
-        acc = fmaf(acc, a, w * sm[2][tid + k * D]);
+        const float sa = M > -INFINITY ? __expf(M - Mn) : 0.f, w = __expf(mk - Mn);
+        l = fmaf(l, sa, w * lk);
+        acc = fmaf(acc, sa, w * ok);
         M = Mn;
       }
+    };
+    for (int k = 1; k < lpd; ++k) add(sm[0][tid + k * D], sm[1][tid + k * D], sm[2][tid + k * D]);
+    if (a.fold_new) {
+      const int pb = a.positions[b], L = min(max(a.seq_lens[b], 0), a.max_len);
+      if (pb >= 0 && pb < a.cache_len && pb < L) {
+        const int h = hq / a.NH, kk = hq % a.NH;
+        const float* nt = a.newtok + ((size_t)b * a.k.Hkv + h) * kFastNewTokFloats;
+        float sc = 0.f;
+        for (int j = 0; j < 16; ++j) sc += nt[j * 4 + kk];
+        add(sc * a.sm_scale, 1.f, nt[64 + d]);
+      }
     }
-    out[((size_t)b * Hq + hq) * D + d] = l > 0.f ? acc / l : 0.f;
+    a.out[((size_t)b * Hq + hq) * D + d] = l > 0.f ? acc / l : 0.f;
   }
 }
 
@@ -82,8 +94,8 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
   if (a.k.D > kMergeThreads) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.Hq, a.B), dim3(kMergeThreads), 0, stream, a.part, a.out,
-                     a.n_chunks, a.k.D, a.Hq);
+  if (a.fold_new && (a.k.D != 128 || a.NH != 4)) return hipErrorInvalidValue;  // the fast kernel's shape
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.Hq, a.B), dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }
 
