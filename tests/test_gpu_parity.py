@@ -365,3 +365,50 @@ def test_decode_step_appends_then_attends(R, exact):
     err = row_errors(out.cpu().numpy().reshape(-1, D), ref.reshape(-1, D))
     print(f"[decode step R{R} exact={exact}] max row rel err {err.max():.3e}", flush=True)
     assert err.max() <= ATTN_TOL
+
+
+@pytest.mark.parametrize("Lmax", [600, 1500, 4100])
+def test_decode_step_search_spread_over_few_chunks(Lmax):
+    """The 1-bit decode step spreads the new token's 32 group searches over the
+    KV head's chunk workgroups (search c + i * n_chunks in chunk c): with one,
+    two and five chunks a workgroup takes up to 32, 16 and 7 searches, some in
+    chunks that lie past a short sequence. Records and outputs against the oracle."""
+    B, Hq, Hkv, D, g, Nc, R = 3, 8, 2, 128, 8, 256, 1
+    G = D // g
+    lens = np.array([1, Lmax // 2 + 1, Lmax], dtype=np.int32)
+    positions = lens - 1
+    rng = np.random.default_rng(700 + Lmax)
+    kcb = synth.codebook(701, Hkv, D, g, Nc, R)
+    vcb = synth.codebook(702, Hkv, D, g, Nc, R)
+    kc = rng.integers(0, Nc, size=(B, Lmax, Hkv, R, G))
+    vc = rng.integers(0, Nc, size=(B, Lmax, Hkv, R, G))
+    kp, vp = _pack_cache(kc, Nc), _pack_cache(vc, Nc)
+    k_new = synth.kv(703, B, Hkv, D)
+    v_new = synth.kv(704, B, Hkv, D)
+    q = synth.queries(705, B, Hq, D)
+    kexp, vexp = kp.copy(), vp.copy()
+    kn_codes, _ = O.encode(k_new, kcb)
+    vn_codes, _ = O.encode(v_new, vcb)
+    for b in range(B):
+        kexp[b, :, positions[b]] = O.pack_codes(kn_codes[b], Nc)
+        vexp[b, :, positions[b]] = O.pack_codes(vn_codes[b], Nc)
+    ref = O.decode_attention_from_packed(q, positions, kexp, vexp, lens, kcb, vcb, 500000.0)
+    kq, vq = api.Quantizer(dev(kcb), g), api.Quantizer(dev(vcb), g)
+    kd, vd = dev(kp), dev(vp)
+    print(f"[decode step spread] Lmax={Lmax}", flush=True)
+    out = api.decode_step(kq, vq, dev(k_new), dev(v_new), dev(positions), dev(q), dev(positions), kd, vd, dev(lens),
+                          Lmax, 500000.0)
+    torch.cuda.synchronize()
+    kgot, vgot = kd.cpu().numpy(), vd.cpu().numpy()
+    for b in range(B):
+        p = positions[b]
+        hard, _ = check_encoding(k_new[b][None], kcb, kgot[b, :, p][None], Nc)
+        assert not hard, (b, hard)
+        hard, _ = check_encoding(v_new[b][None], vcb, vgot[b, :, p][None], Nc)
+        assert not hard, (b, hard)
+        kgot[b, :, p] = kexp[b, :, p]
+        vgot[b, :, p] = vexp[b, :, p]
+    assert np.array_equal(kgot, kexp) and np.array_equal(vgot, vexp)  # nothing else written
+    err = row_errors(out.cpu().numpy().reshape(-1, D), ref.reshape(-1, D))
+    print(f"[decode step spread] Lmax={Lmax} max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= ATTN_TOL
