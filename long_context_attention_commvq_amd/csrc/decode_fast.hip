@@ -331,7 +331,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
       for (int k = 0; k < 4; ++k) cw[r][k] = v[k];
     }
   };
-  constexpr int NB = (R == 1) ? TL : 2;  // records in flight
+  constexpr int NB = (R == 1) ? (TL < 3 ? TL : 3) : 2;  // records in flight
   constexpr int PD = (R == 1) ? 4 : 2;   // codebook gathers in flight (groups)
   uint32_t cw[NB][R][4];
 #pragma unroll
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     constexpr int t = decltype(tc)::value;
     __builtin_amdgcn_s_setprio(3 - (4 * t) / TL);
     if constexpr (NB < TL) {
-      if (t + 1 < TL) load_rec(t + 1, cw[(t + 1) % NB]);
+      if (t + NB - 1 < TL) load_rec(t + NB - 1, cw[(t + NB - 1) % NB]);
     }
     const uint32_t (&cr)[R][4] = cw[t % NB];
     // codebook gathers run PD groups ahead of their use (rolling buffer), the
