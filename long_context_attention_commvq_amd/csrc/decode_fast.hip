@@ -230,6 +230,36 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     bflo[u] = ph.lo[p];
     bfhi[u] = ph.hi[p];
   }
+  const uint8_t* kb = a.kcodes + ((size_t)b * a.k.Hkv + h) * (size_t)a.cache_len * BPT;
+  // record of the lane's position in block t, clamped into the cache (not the
+  // sequence, so the loads need not wait for seq_lens; positions past the
+  // sequence are masked after the scores)
+  auto load_rec = [&](int t, uint32_t (&cw)[R][4]) {
+    const int mm = min(m0 + tid + FT * t, a.cache_len - 1);
+    const u32x4* rec = reinterpret_cast<const u32x4*>(kb + (size_t)mm * BPT);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const u32x4 v = rec[r];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) cw[r][k] = v[k];
+    }
+  };
+  constexpr int NB = (R == 1) ? (TL < 3 ? TL : 3) : 2;  // records in flight
+  constexpr int PD = (R == 1) ? 4 : 2;   // codebook gathers in flight (groups)
+  uint32_t cw[NB][R][4];
+#pragma unroll
+  for (int t = 0; t < NB - (NB < TL ? 1 : 0); ++t) load_rec(t, cw[t]);
+
+  // ---- per-workgroup constants ------------------------------------------
+  // the head's key codebook, [G][R][Nc'][8] fp16 as in HBM: all loads are issued
+  // before the lane phases are computed and stored to LDS after
+  constexpr int NKCB = Cfg::KCB / 16 / FT;
+  u32x4 kcv[NKCB];
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.kcb + (size_t)h * FG * R * FNC * 8);
+#pragma unroll
+    for (int k = 0; k < NKCB; ++k) kcv[k] = src[tid + FT * k];
+  }
   // decode step: the workgroup whose chunk holds the new position leaves that
   // position out of its table path (its record is being written). R = 2: that
   // workgroup encodes the new key and value of its KV head (all 32 group
@@ -265,8 +295,6 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
       rhi = ph.hi[p];
     }
   };
-  const bool rowjob = R == 1 && appended && row_of(0) < 2 * FG;
-  if (rowjob) row_load(row_of(0));
   auto row_job = [&]() {
     if (!(R == 1 && appended)) return;
     for (int it = 0; it < 4; ++it) {
@@ -317,39 +345,21 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     }
   }
 
-  const uint8_t* kb = a.kcodes + ((size_t)b * a.k.Hkv + h) * (size_t)a.cache_len * BPT;
-  // record of the lane's position in block t, clamped into the cache (not the
-  // sequence, so the loads need not wait for seq_lens; positions past the
-  // sequence are masked after the scores)
-  auto load_rec = [&](int t, uint32_t (&cw)[R][4]) {
-    const int mm = min(m0 + tid + FT * t, a.cache_len - 1);
-    const u32x4* rec = reinterpret_cast<const u32x4*>(kb + (size_t)mm * BPT);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const u32x4 v = rec[r];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) cw[r][k] = v[k];
-    }
-  };
-  constexpr int NB = (R == 1) ? (TL < 3 ? TL : 3) : 2;  // records in flight
-  constexpr int PD = (R == 1) ? 4 : 2;   // codebook gathers in flight (groups)
-  uint32_t cw[NB][R][4];
-#pragma unroll
-  for (int t = 0; t < NB - (NB < TL ? 1 : 0); ++t) load_rec(t, cw[t]);
-
-  // ---- per-workgroup constants ------------------------------------------
-  // the head's key codebook, [G][R][Nc'][8] fp16 as in HBM: all loads are issued
-  // before the lane phases are computed and stored to LDS after
-  constexpr int NKCB = Cfg::KCB / 16 / FT;
-  u32x4 kcv[NKCB];
-  {
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.kcb + (size_t)h * FG * R * FNC * 8);
-#pragma unroll
-    for (int k = 0; k < NKCB; ++k) kcv[k] = src[tid + FT * k];
-  }
+  // the decode step's first search inputs (after the loads that do not wait on
+  // the step's positions)
+  const bool rowjob = R == 1 && appended && row_of(0) < 2 * FG;
+  if (rowjob) row_load(row_of(0));
   // a chunk wholly past the sequence contributes an empty partial (its loads were
   // issued before the length was known; they stay unused)
   if (m0 >= L) {
+    // (uses of the set-up's loads on this path too, so that the compiler keeps
+    // them ahead of the length test instead of sinking them past it)
+#pragma unroll
+    for (int k = 0; k < NKCB; ++k) asm volatile("" ::"v"(kcv[k]));
+#pragma unroll
+    for (int t = 0; t < NB - (NB < TL ? 1 : 0); ++t)
+#pragma unroll
+      for (int r = 0; r < R; ++r) asm volatile("" ::"v"(cw[t][r][0]), "v"(cw[t][r][1]), "v"(cw[t][r][2]), "v"(cw[t][r][3]));
     for (int i = tid; i < FNH * (FD + 2); i += FT) {
       const int hh = i / (FD + 2), k = i % (FD + 2);
       part[hh * pstride + k] = (k == 0) ? -INFINITY : 0.f;
