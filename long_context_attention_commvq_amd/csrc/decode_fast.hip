@@ -368,12 +368,19 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     return;
   }
   // lane phases e^{i d theta_p}, d < 64: 16-byte chunk c (pairs 4c..4c+3) of row d
-  // at slot (c + d) & 15, so the 64 lanes reading chunk c hit 16 different slots
-  // (i = tid + 512 k, so the pair i & 63 is the lane's own)
-  for (int i = tid; i < 64 * FPR; i += FT) {
-    const int d = i >> 6, p = lane;
-    const float2 e = phase_hw((uint32_t)d, flo, fhi);
-    pht[d * 64 + (((p >> 2) + d) & 15) * 4 + (p & 3)] = pack_h2(e.x, e.y);
+  // at slot (c + d) & 15, so the 64 lanes reading chunk c hit 16 different slots.
+  // Lane p (the pair) of wavefront w takes offsets d = w + 8 k: e^{i w theta}
+  // from the hardware sine and cosine, then seven steps of e^{i 8 theta} in fp32.
+  {
+    static_assert(FT / 64 == 8, "eight offsets per lane");
+    const float2 st = phase_hw(8u, flo, fhi);
+    float2 e = phase_hw((uint32_t)wave, flo, fhi);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int d = wave + 8 * k, p = lane;
+      pht[d * 64 + (((p >> 2) + d) & 15) * 4 + (p & 3)] = pack_h2(e.x, e.y);
+      e = make_float2(e.x * st.x - e.y * st.y, e.x * st.y + e.y * st.x);
+    }
   }
 #pragma unroll
   for (int k = 0; k < NKCB; ++k) reinterpret_cast<u32x4*>(lds)[tid + FT * k] = kcv[k];
