@@ -23,6 +23,7 @@ constexpr int kMergeThreads = 256;
 // through LDS.
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
   __shared__ float sm[3][kMergeThreads];
+  __shared__ float sc_new;
   const float* __restrict__ part = a.part;
   const int n_chunks = a.n_chunks, D = a.k.D, Hq = a.Hq;
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
@@ -32,6 +33,23 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   const int d = tid % D, sub = tid / D;
   const bool active = sub < lpd;
   float M = -INFINITY, l = 0.f, acc = 0.f;
+  // the decode step's new token (fast 1-bit kernel): its terms are requested
+  // with the partials (lanes 0..15 one group product each, lane d its value
+  // dimension) and used after them, so its fold costs no second round trip
+  float v_new = 0.f, scj = 0.f;
+  int pbv = -1, Lv = 0;
+  if (a.fold_new) {
+    const int h = hq / a.NH, kk = hq % a.NH;
+    const float* nt = a.newtok + ((size_t)b * a.k.Hkv + h) * kFastNewTokFloats;
+    if (active && sub == 0) v_new = nt[64 + d];
+    if (tid < 16) scj = nt[tid * 4 + kk];
+    // vector loads (an opaque zero index), so that no scalar wait for them
+    // stands before the partials' loads
+    int z = 0;
+    asm volatile("" : "+v"(z));
+    pbv = a.positions[b + z];
+    Lv = a.seq_lens[b + z];
+  }
   if (active) {
     constexpr int KB = 16;  // chunks loaded per batch, all before any is used
     for (int c0 = sub; c0 < n_chunks; c0 += KB * lpd) {
@@ -64,6 +82,12 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   sm[0][tid] = M;
   sm[1][tid] = l;
   sm[2][tid] = acc;
+  if (a.fold_new && tid < 64) {
+    // sum of the 16 group products (lanes 0..15; the other lanes hold 0)
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) scj += __shfl_xor(scj, o, 64);
+    if (tid == 0) sc_new = scj;
+  }
   __syncthreads();
   if (active && sub == 0) {
     auto add = [&](float mk, float lk, float ok) {
@@ -77,14 +101,9 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
     };
     for (int k = 1; k < lpd; ++k) add(sm[0][tid + k * D], sm[1][tid + k * D], sm[2][tid + k * D]);
     if (a.fold_new) {
-      const int pb = a.positions[b], L = min(max(a.seq_lens[b], 0), a.max_len);
-      if (pb >= 0 && pb < a.cache_len && pb < L) {
-        const int h = hq / a.NH, kk = hq % a.NH;
-        const float* nt = a.newtok + ((size_t)b * a.k.Hkv + h) * kFastNewTokFloats;
-        float sc = 0.f;
-        for (int j = 0; j < 16; ++j) sc += nt[j * 4 + kk];
-        add(sc * a.sm_scale, 1.f, nt[64 + d]);
-      }
+      asm volatile("" : "+v"(Lv), "+v"(pbv));  // (used here, not where loaded)
+      const int L = min(max(Lv, 0), a.max_len);
+      if (pbv >= 0 && pbv < a.cache_len && pbv < L) add(sc_new * a.sm_scale, 1.f, v_new);
     }
     a.out[((size_t)b * Hq + hq) * D + d] = l > 0.f ? acc / l : 0.f;
   }
