@@ -665,13 +665,23 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     const float inv = 1.0f / (float)(1u << FXSHIFT);
     float4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     const char* hrow = lds + Cfg::HOFF + mgrp * 16 + mi * 4 + (size_t)(wave * BPW) * 256;  // bin rl at rl * 256
+    // all of the lane's bins read before the first is used (one LDS latency,
+    // not one per step)
+    uint32_t hvs[NSTEP][4];
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) hvs[st][u] = *reinterpret_cast<const uint32_t*>(hrow + (size_t)(4 * st + u) * 256);
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) asm volatile("" : "+v"(hvs[st][u]));  // (keeps the reads together, ahead of the loop)
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
       half4_t ahi, alo;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint32_t hv = *reinterpret_cast<const uint32_t*>(hrow + (size_t)(4 * st + u) * 256);
-        const float x = (float)hv * inv;
+        const float x = (float)hvs[st][u] * inv;
         const _Float16 hi = (_Float16)x;
         ahi[u] = hi;
         alo[u] = (_Float16)(x - (float)hi);
