@@ -187,6 +187,59 @@ int32_t commvq_decode_step(const commvq_codebook* kcb, const commvq_codebook* vc
                            int32_t max_seq_len, float sm_scale, float* out, void* workspace,
                            size_t workspace_bytes, uint32_t flags, void* stream);
 
+/* ---- comparison path: the "naive" decode of the same codes ----------------
+ * The review ("Pith review of CommVQ", "The pith") compares the method's decode
+ * latency with a naive implementation of the same quantization. These two calls
+ * are that baseline, read plainly: rebuild fp16 keys and values from the codes
+ * in HBM, then run dense attention over them. Same synchronisation, ownership
+ * and error conventions as above. */
+
+/* Dequantise the cached records of positions [0, min(seq_lens[b], max_seq_len))
+ * into fp16 vectors:
+ *   k_out[b][h][t][:] = RoPE_t( sum_r key entries selected by record (b, h, t) )
+ *   v_out[b][h][t][:] = sum_r value entries selected by record (b, h, t)
+ * (sums and rotation in fp32, rounded to fp16 once; the rotation angle of
+ * pair p is t * theta_p, from the position's exact fraction of a turn and the
+ * hardware sine and cosine, within 2e-7 of the exact values).
+ *   kcodes, vcodes  device bytes [batch][Hkv][cache_len][bytes_per_token]
+ *   seq_lens        device int32 [batch], clamped to [0, max_seq_len]
+ *   k_out, v_out    device fp16 [batch][Hkv][cache_len][D], 16-byte aligned;
+ *                   positions at or past the length are left untouched.
+ * Codebooks as for commvq_decode_attention (same D, g and Hkv for K and V);
+ * max_seq_len <= cache_len. Pages: "What carries the argument" (a vector is the
+ * sum of its R rounds' entries; RoPE as 2x2 rotations of pairs). */
+int32_t commvq_dequantize_kv(const commvq_codebook* kcb, const commvq_codebook* vcb,
+                             const commvq_rope* rope, const uint8_t* kcodes, const uint8_t* vcodes,
+                             const int32_t* seq_lens, int32_t batch, int32_t cache_len,
+                             int32_t max_seq_len, void* k_out, void* v_out, void* stream);
+
+/* Workspace bytes for commvq_dense_decode_attention: (max, sum, o[D]) fp32 per
+ * (sequence, query head, chunk of 1024 positions); negative commvq_status on
+ * invalid arguments (head_dim other than 128: COMMVQ_ERR_UNSUPPORTED). */
+int64_t commvq_dense_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                     int32_t head_dim, int32_t max_seq_len);
+
+/* Dense grouped-query decode attention over fp16 keys that already carry their
+ * rotation and fp16 values:
+ *   out[b][hq] = sum_t softmax_t(sm_scale * qr . k[b][h][t]) v[b][h][t],
+ *   t < min(seq_lens[b], max_seq_len), h = hq / (n_q_heads / n_kv_heads),
+ *   qr = q[b][hq] rotated to position q_pos[b] (exact phase) in fp32, carried
+ *   as two fp16 parts so that its products with the fp16 keys are exact; the
+ *   products are summed in fp32 and the weighted value sum is fp32.
+ *   q        device fp32 [batch][n_q_heads][head_dim]
+ *   k, v     device fp16 [batch][n_kv_heads][cache_len][head_dim]
+ *   out      device fp32 [batch][n_q_heads][head_dim]; a length of 0 gives zeros
+ *   workspace >= commvq_dense_workspace_bytes(...), 256-byte aligned, no
+ *            initialisation needed; calls sharing it must not overlap.
+ * head_dim must be 128 and n_q_heads / n_kv_heads 1, 2, 4 or 8 (otherwise
+ * COMMVQ_ERR_UNSUPPORTED); q, out, k and v 16-byte aligned. */
+int32_t commvq_dense_decode_attention(const commvq_rope* rope, const float* q, const int32_t* q_pos,
+                                      const void* k, const void* v, const int32_t* seq_lens,
+                                      int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                      int32_t head_dim, int32_t cache_len, int32_t max_seq_len,
+                                      float sm_scale, float* out, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,7 +34,8 @@ STATUS_NAMES = {
 EXPORTED = [
     "commvq_abi_version", "commvq_last_error", "commvq_validate_codebook", "commvq_bits_per_scalar",
     "commvq_code_bytes_per_token", "commvq_decode_workspace_bytes", "commvq_encode", "commvq_append",
-    "commvq_decode_attention", "commvq_decode_step",
+    "commvq_decode_attention", "commvq_decode_step", "commvq_dequantize_kv", "commvq_dense_workspace_bytes",
+    "commvq_dense_decode_attention",
 ]
 
 
@@ -89,6 +90,15 @@ def lib():
         L.commvq_decode_step.argtypes = [CB, CB, POINTER(commvq_rope), c_void_p, c_void_p, c_void_p, c_void_p,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                          c_float, c_void_p, c_void_p, c_size_t, ctypes.c_uint32, c_void_p]
+        L.commvq_dequantize_kv.restype = c_int32
+        L.commvq_dequantize_kv.argtypes = [CB, CB, POINTER(commvq_rope), c_void_p, c_void_p, c_void_p, c_int32,
+                                           c_int32, c_int32, c_void_p, c_void_p, c_void_p]
+        L.commvq_dense_workspace_bytes.restype = c_int64
+        L.commvq_dense_workspace_bytes.argtypes = [c_int32, c_int32, c_int32, c_int32, c_int32]
+        L.commvq_dense_decode_attention.restype = c_int32
+        L.commvq_dense_decode_attention.argtypes = [POINTER(commvq_rope), c_void_p, c_void_p, c_void_p, c_void_p,
+                                                    c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                                    c_float, c_void_p, c_void_p, c_size_t, c_void_p]
         _lib = L
     return _lib
 
@@ -184,3 +194,24 @@ def commvq_decode_step(kcb: commvq_codebook, vcb: commvq_codebook, rope: commvq_
         ctypes.byref(kcb), ctypes.byref(vcb), ctypes.byref(rope), _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(q),
         _ptr(q_pos), _ptr(kcodes), _ptr(vcodes), _ptr(seq_lens), batch, n_q_heads, cache_len, max_seq_len,
         float(sm_scale), _ptr(out), _ptr(workspace), int(workspace_bytes), int(flags), _stream(stream, q, out)))
+
+
+def commvq_dequantize_kv(kcb: commvq_codebook, vcb: commvq_codebook, rope: commvq_rope, kcodes, vcodes, seq_lens,
+                         batch: int, cache_len: int, max_seq_len: int, k_out, v_out, stream=None) -> int:
+    return _check(lib().commvq_dequantize_kv(
+        ctypes.byref(kcb), ctypes.byref(vcb), ctypes.byref(rope), _ptr(kcodes), _ptr(vcodes), _ptr(seq_lens), batch,
+        cache_len, max_seq_len, _ptr(k_out), _ptr(v_out), _stream(stream, k_out, kcodes)))
+
+
+def commvq_dense_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                                 max_seq_len: int) -> int:
+    return lib().commvq_dense_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, max_seq_len)
+
+
+def commvq_dense_decode_attention(rope: commvq_rope, q, q_pos, k, v, seq_lens, batch: int, n_q_heads: int,
+                                  n_kv_heads: int, head_dim: int, cache_len: int, max_seq_len: int, sm_scale: float,
+                                  out, workspace, workspace_bytes: int, stream=None) -> int:
+    return _check(lib().commvq_dense_decode_attention(
+        ctypes.byref(rope), _ptr(q), _ptr(q_pos), _ptr(k), _ptr(v), _ptr(seq_lens), batch, n_q_heads, n_kv_heads,
+        head_dim, cache_len, max_seq_len, float(sm_scale), _ptr(out), _ptr(workspace), int(workspace_bytes),
+        _stream(stream, q, out)))

@@ -111,3 +111,52 @@ def decode_step(kq: Quantizer, vq: Quantizer, k_new: torch.Tensor, v_new: torch.
                             kcache, vcache, seq_lens, B, Hq, kcache.shape[2], max_seq_len, sm_scale, out,
                             workspace.buf, workspace.nbytes, _lib.COMMVQ_DECODE_EXACT if exact else 0)
     return out
+
+
+# ---- comparison path: dequantise to fp16, then dense attention ---------------
+
+def dequantize_kv(kq: Quantizer, vq: Quantizer, kcache: torch.Tensor, vcache: torch.Tensor, seq_lens: torch.Tensor,
+                  max_seq_len: int, theta_base: float, k_out: torch.Tensor | None = None,
+                  v_out: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Packed caches [B, Hkv, Lmax, bpt] -> fp16 keys (rotated to their positions)
+    and values [B, Hkv, Lmax, D]; positions at or past seq_lens[b] are left as
+    they were in k_out / v_out."""
+    B, H, Lmax, _ = kcache.shape
+    D = kq.head_dim
+    if k_out is None:
+        k_out = torch.zeros((B, H, Lmax, D), dtype=torch.float16, device=kcache.device)
+    if v_out is None:
+        v_out = torch.zeros((B, H, Lmax, D), dtype=torch.float16, device=kcache.device)
+    rope = _lib.make_rope(theta_base)
+    _lib.commvq_dequantize_kv(kq.desc, vq.desc, rope, kcache, vcache, seq_lens, B, Lmax, max_seq_len, k_out, v_out)
+    return k_out, v_out
+
+
+class DenseWorkspace:
+    """Workspace of commvq_dense_decode_attention for one shape."""
+
+    def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, max_seq_len: int, device):
+        n = _lib.commvq_dense_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, max_seq_len)
+        if n < 0:
+            raise _lib.CommvqError(int(n), _lib.commvq_last_error())
+        self.nbytes = int(n)
+        self.buf = torch.empty(max(self.nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def dense_decode_attention(q: torch.Tensor, q_pos: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                           seq_lens: torch.Tensor, max_seq_len: int, theta_base: float,
+                           sm_scale: float | None = None, out: torch.Tensor | None = None,
+                           workspace: DenseWorkspace | None = None) -> torch.Tensor:
+    """q fp32 [B, Hq, D] (not rotated) over fp16 k (rotated), v [B, Hkv, Lmax, D]."""
+    B, Hq, D = q.shape
+    Hkv, Lmax = k.shape[1], k.shape[2]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = DenseWorkspace(B, Hq, Hkv, D, max_seq_len, q.device)
+    rope = _lib.make_rope(theta_base)
+    _lib.commvq_dense_decode_attention(rope, q, q_pos, k, v, seq_lens, B, Hq, Hkv, D, Lmax, max_seq_len, sm_scale,
+                                       out, workspace.buf, workspace.nbytes)
+    return out

@@ -374,3 +374,137 @@ int32_t commvq_decode_step(const commvq_codebook* kcb, const commvq_codebook* vc
 }
 
 }  // extern "C"
+
+// ---- comparison path: dequantise, then dense attention ---------------------
+
+namespace {
+
+int32_t check_rope(const commvq_rope* rope) {
+  if (!rope) return fail(COMMVQ_ERR_INVALID_ARG, "null rope descriptor");
+  if (!(rope->theta_base > 1.0) || !std::isfinite(rope->theta_base))
+    return fail(COMMVQ_ERR_INVALID_ARG, "rope theta_base must be finite and > 1");
+  if (rope->pairing != 0 || rope->reserved != 0)
+    return fail(COMMVQ_ERR_UNSUPPORTED, "rope pairing %d: only interleaved pairs (0) are supported", rope->pairing);
+  return COMMVQ_OK;
+}
+
+int32_t dense_shapes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t max_seq_len) {
+  if (batch < 1) return fail(COMMVQ_ERR_INVALID_ARG, "batch %d < 1", batch);
+  if (n_kv_heads < 1) return fail(COMMVQ_ERR_INVALID_ARG, "n_kv_heads %d < 1", n_kv_heads);
+  if (n_q_heads < 1 || n_q_heads % n_kv_heads)
+    return fail(COMMVQ_ERR_INVALID_ARG, "n_q_heads %d must be a positive multiple of n_kv_heads %d", n_q_heads,
+                n_kv_heads);
+  if (max_seq_len < 1) return fail(COMMVQ_ERR_INVALID_ARG, "max_seq_len %d < 1", max_seq_len);
+  if (head_dim < 2 || (head_dim & 1)) return fail(COMMVQ_ERR_INVALID_ARG, "head_dim %d must be even and >= 2", head_dim);
+  if (head_dim != 128) return fail(COMMVQ_ERR_UNSUPPORTED, "dense attention supports head_dim 128, not %d", head_dim);
+  const int NH = n_q_heads / n_kv_heads;
+  if (NH != 1 && NH != 2 && NH != 4 && NH != 8)
+    return fail(COMMVQ_ERR_UNSUPPORTED, "query heads per KV head %d not in {1, 2, 4, 8}", NH);
+  if (batch > 65535 || n_kv_heads > 65535)
+    return fail(COMMVQ_ERR_UNSUPPORTED, "batch %d or n_kv_heads %d > 65535", batch, n_kv_heads);
+  return COMMVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t commvq_dequantize_kv(const commvq_codebook* kcb, const commvq_codebook* vcb, const commvq_rope* rope,
+                             const uint8_t* kcodes, const uint8_t* vcodes, const int32_t* seq_lens, int32_t batch,
+                             int32_t cache_len, int32_t max_seq_len, void* k_out, void* v_out, void* stream) {
+  g_err[0] = 0;
+  commvq::CbShape k, v;
+  int32_t st = check_shape(kcb, "key codebook", &k);
+  if (st) return st;
+  st = check_shape(vcb, "value codebook", &v);
+  if (st) return st;
+  if (k.D != v.D || k.g != v.g || k.Hkv != v.Hkv)
+    return fail(COMMVQ_ERR_INVALID_ARG, "key and value codebooks disagree on head_dim, group_size or n_kv_heads");
+  st = check_rope(rope);
+  if (st) return st;
+  if (batch < 1) return fail(COMMVQ_ERR_INVALID_ARG, "batch %d < 1", batch);
+  if (max_seq_len < 1) return fail(COMMVQ_ERR_INVALID_ARG, "max_seq_len %d < 1", max_seq_len);
+  if (cache_len < max_seq_len)
+    return fail(COMMVQ_ERR_INVALID_ARG, "max_seq_len %d exceeds cache_len %d", max_seq_len, cache_len);
+  if (batch > 65535) return fail(COMMVQ_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  st = check_entries(kcb, "key codebook");
+  if (st) return st;
+  st = check_entries(vcb, "value codebook");
+  if (st) return st;
+  if (!kcodes || !vcodes || !seq_lens || !k_out || !v_out)
+    return fail(COMMVQ_ERR_INVALID_ARG, "null codes, seq_lens or output pointer");
+  if ((reinterpret_cast<uintptr_t>(k_out) | reinterpret_cast<uintptr_t>(v_out)) & 15)
+    return fail(COMMVQ_ERR_INVALID_ARG, "k_out and v_out must be 16-byte aligned");
+  commvq::DequantArgs a{};
+  a.kcodes = kcodes;
+  a.vcodes = vcodes;
+  a.seq_lens = seq_lens;
+  a.kcb = static_cast<const _Float16*>(kcb->entries);
+  a.vcb = static_cast<const _Float16*>(vcb->entries);
+  a.kout = static_cast<_Float16*>(k_out);
+  a.vout = static_cast<_Float16*>(v_out);
+  a.B = batch;
+  a.cache_len = cache_len;
+  a.max_len = max_seq_len;
+  a.k = k;
+  a.v = v;
+  const PhaseConsts& pc = phase_consts(rope->theta_base, k.D);
+  return hip_status(commvq::launch_dequant_kv(a, pc.ph, static_cast<hipStream_t>(stream)),
+                    "commvq_dequantize_kv launch");
+}
+
+int64_t commvq_dense_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                     int32_t max_seq_len) {
+  g_err[0] = 0;
+  const int32_t st = dense_shapes(batch, n_q_heads, n_kv_heads, head_dim, max_seq_len);
+  if (st) return st;
+  return (int64_t)commvq::dense_workspace_bytes(batch, n_q_heads, max_seq_len);
+}
+
+int32_t commvq_dense_decode_attention(const commvq_rope* rope, const float* q, const int32_t* q_pos, const void* k,
+                                      const void* v, const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
+                                      int32_t n_kv_heads, int32_t head_dim, int32_t cache_len, int32_t max_seq_len,
+                                      float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  g_err[0] = 0;
+  int32_t st = dense_shapes(batch, n_q_heads, n_kv_heads, head_dim, max_seq_len);
+  if (st) return st;
+  st = check_rope(rope);
+  if (st) return st;
+  if (cache_len < max_seq_len)
+    return fail(COMMVQ_ERR_INVALID_ARG, "max_seq_len %d exceeds cache_len %d", max_seq_len, cache_len);
+  if (!std::isfinite(sm_scale)) return fail(COMMVQ_ERR_INVALID_ARG, "sm_scale is not finite");
+  if (!q || !q_pos || !k || !v || !seq_lens || !out)
+    return fail(COMMVQ_ERR_INVALID_ARG, "null q, q_pos, k, v, seq_lens or out pointer");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(k) |
+       reinterpret_cast<uintptr_t>(v)) & 15)
+    return fail(COMMVQ_ERR_INVALID_ARG, "q, out, k and v must be 16-byte aligned");
+  const int64_t need = commvq_dense_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, max_seq_len);
+  if (need < 0) return (int32_t)need;
+  if (!workspace || workspace_bytes < (size_t)need)
+    return fail(COMMVQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %lld required", workspace_bytes,
+                (long long)need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(COMMVQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  commvq::DenseArgs a{};
+  a.q = q;
+  a.q_pos = q_pos;
+  a.k = static_cast<const _Float16*>(k);
+  a.v = static_cast<const _Float16*>(v);
+  a.seq_lens = seq_lens;
+  a.part = static_cast<float*>(workspace);
+  a.out = out;
+  a.B = batch;
+  a.Hq = n_q_heads;
+  a.Hkv = n_kv_heads;
+  a.NH = n_q_heads / n_kv_heads;
+  a.cache_len = cache_len;
+  a.max_len = max_seq_len;
+  a.n_chunks = (max_seq_len + commvq::kDenseChunk - 1) / commvq::kDenseChunk;
+  a.sm_scale = sm_scale;
+  const PhaseConsts& pc = phase_consts(rope->theta_base, head_dim);
+  return hip_status(commvq::launch_dense_decode(a, pc.ph, static_cast<hipStream_t>(stream)),
+                    "commvq_dense_decode_attention launch");
+}
+
+}  // extern "C"

@@ -65,8 +65,35 @@ struct DecodeArgs {
   CbShape k, v;
 };
 
-// Chunk length (tokens per workgroup) chosen for a decode shape; the workspace
-// query and the launch use the same rule.
+// Comparison path: packed records -> fp16 keys (rotated to their positions) and
+// values, [B][Hkv][cache_len][D], for positions below the sequence length.
+struct DequantArgs {
+  const uint8_t* kcodes;
+  const uint8_t* vcodes;
+  const int32_t* seq_lens;
+  const _Float16* kcb;
+  const _Float16* vcb;
+  _Float16* kout;
+  _Float16* vout;
+  int B, cache_len, max_len;
+  CbShape k, v;
+};
+
+// Comparison path: dense decode attention over fp16 keys (already rotated) and
+// values [B][Hkv][cache_len][128], chunks of kDenseChunk positions.
+constexpr int kDenseChunk = 1024;
+struct DenseArgs {
+  const float* q;
+  const int32_t* q_pos;
+  const _Float16* k;
+  const _Float16* v;
+  const int32_t* seq_lens;
+  float* part;  // [B][Hq][n_chunks][D + 2]
+  float* out;   // [B][Hq][D]
+  int B, Hq, Hkv, NH, cache_len, max_len, n_chunks;
+  float sm_scale;
+};
+
 // Raises a kernel's dynamic-LDS limit to the whole 160 KiB of a CU, once per
 // device: `done` is a per-kernel bit set of the devices already configured.
 inline hipError_t allow_full_lds(const void* kernel, std::atomic<uint64_t>& done) {
@@ -80,6 +107,8 @@ inline hipError_t allow_full_lds(const void* kernel, std::atomic<uint64_t>& done
   return e;
 }
 
+// Chunk length (tokens per workgroup) chosen for a decode shape; the workspace
+// query and the launch use the same rule.
 int decode_chunk_len(const CbShape& k, const CbShape& v, int B, int Hq, int max_len, int flags);
 bool decode_fast_path(const CbShape& k, const CbShape& v, int NH, int flags);
 size_t decode_workspace_bytes(const CbShape& k, int B, int Hq, int max_len, int chunk);
@@ -90,5 +119,9 @@ hipError_t launch_decode_fast(const DecodeArgs& a, const PhaseTable& ph, hipStre
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_generic(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_dequant_kv(const DequantArgs& a, const PhaseTable& ph, hipStream_t stream);
+size_t dense_workspace_bytes(int B, int Hq, int max_len);
+// dense_decode_kernel, then the chunk merge into a.out
+hipError_t launch_dense_decode(const DenseArgs& a, const PhaseTable& ph, hipStream_t stream);
 
 }  // namespace commvq

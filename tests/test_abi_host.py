@@ -152,3 +152,66 @@ def test_decode_step_validation_without_launch():
     assert step(positions=None) == _lib.COMMVQ_ERR_INVALID_ARG
     assert step(k_new=FAKE + 8) == _lib.COMMVQ_ERR_INVALID_ARG
     assert step(ws_bytes=16) == _lib.COMMVQ_ERR_WORKSPACE
+
+
+def test_dense_workspace_query():
+    E = _lib
+    assert E.commvq_dense_workspace_bytes(1, 32, 8, 128, 131072) == 32 * 128 * 130 * 4  # chunks of 1024 positions
+    assert E.commvq_dense_workspace_bytes(2, 4, 1, 128, 1025) == 2 * 4 * 2 * 130 * 4
+    assert E.commvq_dense_workspace_bytes(1, 32, 8, 64, 1000) == E.COMMVQ_ERR_UNSUPPORTED
+    assert E.commvq_dense_workspace_bytes(1, 32, 8, 127, 1000) == E.COMMVQ_ERR_INVALID_ARG
+    assert E.commvq_dense_workspace_bytes(1, 30, 8, 128, 1000) == E.COMMVQ_ERR_INVALID_ARG
+    assert E.commvq_dense_workspace_bytes(1, 24, 8, 128, 1000) == E.COMMVQ_ERR_UNSUPPORTED  # 3 q per kv
+    assert E.commvq_dense_workspace_bytes(0, 32, 8, 128, 1000) == E.COMMVQ_ERR_INVALID_ARG
+    assert E.commvq_dense_workspace_bytes(1, 32, 8, 128, 0) == E.COMMVQ_ERR_INVALID_ARG
+    assert E.commvq_dense_workspace_bytes(1, 32, 0, 128, 10) == E.COMMVQ_ERR_INVALID_ARG
+    assert E.commvq_dense_workspace_bytes(65536, 32, 8, 128, 10) == E.COMMVQ_ERR_UNSUPPORTED
+
+
+def test_dequantize_validation_without_launch():
+    k, rope = cb(R=1), _lib.make_rope(500000.0)
+    L = _lib.lib()
+
+    def deq(kc=k, vc=k, rp=rope, codes=FAKE, lens=FAKE, B=1, cache_len=1024, max_len=1024, ko=FAKE, vo=FAKE):
+        return L.commvq_dequantize_kv(ctypes.byref(kc), ctypes.byref(vc), ctypes.byref(rp) if rp else None, codes,
+                                      codes, lens, B, cache_len, max_len, ko, vo, None)
+    E = _lib
+    assert deq(rp=None) == E.COMMVQ_ERR_INVALID_ARG
+    assert deq(rp=_lib.make_rope(500000.0, pairing=1)) == E.COMMVQ_ERR_UNSUPPORTED
+    assert deq(vc=cb(D=64)) == E.COMMVQ_ERR_INVALID_ARG
+    assert deq(vc=cb(g=4)) == E.COMMVQ_ERR_INVALID_ARG
+    assert deq(B=0) == E.COMMVQ_ERR_INVALID_ARG
+    assert deq(max_len=0) == E.COMMVQ_ERR_INVALID_ARG
+    assert deq(max_len=1025) == E.COMMVQ_ERR_INVALID_ARG  # beyond the cache
+    assert deq(B=65536) == E.COMMVQ_ERR_UNSUPPORTED
+    assert deq(codes=None) == E.COMMVQ_ERR_INVALID_ARG
+    assert deq(lens=None) == E.COMMVQ_ERR_INVALID_ARG
+    assert deq(ko=None) == E.COMMVQ_ERR_INVALID_ARG
+    assert deq(vo=FAKE + 8) == E.COMMVQ_ERR_INVALID_ARG  # 16-byte alignment
+    assert deq(kc=cb(R=1, entries=None)) == E.COMMVQ_ERR_INVALID_ARG
+    assert deq(kc=cb(D=0)) == E.COMMVQ_ERR_INVALID_ARG
+
+
+def test_dense_attention_validation_without_launch():
+    rope = _lib.make_rope(500000.0)
+    L = _lib.lib()
+
+    def dense(rp=rope, q=FAKE, k=FAKE, out=FAKE, B=1, Hq=32, Hkv=8, D=128, cache_len=1024, max_len=1024,
+              scale=0.088, ws=FAKE, ws_bytes=1 << 30):
+        return L.commvq_dense_decode_attention(ctypes.byref(rp) if rp else None, q, FAKE, k, k, FAKE, B, Hq, Hkv, D,
+                                               cache_len, max_len, scale, out, ws, ws_bytes, None)
+    E = _lib
+    assert dense(rp=None) == E.COMMVQ_ERR_INVALID_ARG
+    assert dense(rp=_lib.make_rope(0.5)) == E.COMMVQ_ERR_INVALID_ARG
+    assert dense(D=64) == E.COMMVQ_ERR_UNSUPPORTED
+    assert dense(Hq=12) == E.COMMVQ_ERR_INVALID_ARG
+    assert dense(Hq=24) == E.COMMVQ_ERR_UNSUPPORTED
+    assert dense(max_len=1025) == E.COMMVQ_ERR_INVALID_ARG
+    assert dense(scale=float("nan")) == E.COMMVQ_ERR_INVALID_ARG
+    assert dense(q=None) == E.COMMVQ_ERR_INVALID_ARG
+    assert dense(k=FAKE + 2) == E.COMMVQ_ERR_INVALID_ARG
+    assert dense(out=FAKE + 4) == E.COMMVQ_ERR_INVALID_ARG
+    assert dense(ws_bytes=16) == E.COMMVQ_ERR_WORKSPACE
+    assert dense(ws=None) == E.COMMVQ_ERR_WORKSPACE
+    assert dense(ws=FAKE + 64) == E.COMMVQ_ERR_WORKSPACE
+    assert dense(B=0) == E.COMMVQ_ERR_INVALID_ARG
