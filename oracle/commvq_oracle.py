@@ -21,7 +21,10 @@ Sources (the pages this implements):
         multiply the quantized value codes before the codebook multiply.
       - "Assumptions & free parameters": RoPE is block-diagonal 2x2 rotations
         (Eqns 5-6); matrices [[x, y], [-y, x]] commute with every 2-D rotation
-        (Eqn 8, Property 1); R = residual rounds, g = group size, Nc' = entries.
+        (Eqn 8, Property 1); R = residual rounds, g = group size, Nc' = entries;
+        the codebook is fitted by alternating assignment and update (k-means
+        style) with soft assignment and annealing ("Referee Report",
+        Significance: the update has a closed form).
 
 Readings taken where the pages are silent or ambiguous (each listed in the
 repository's design notes):
@@ -37,6 +40,9 @@ repository's design notes):
   * The query arrives un-rotated and sits at position q_pos = L - 1; attention
     covers cached positions [0, L); scale 1/sqrt(D) by default.
   * Values use the same greedy residual codebook as keys, without RoPE.
+  * Codebook fitting: round r is fitted on the residuals of the earlier rounds;
+    soft assignment = softmax of -distance / temperature, temperature 0 = the
+    nearest entry; the update is the responsibility-weighted mean.
 
 Array conventions:
   codebook  [Hkv, G, R, Nc, g]   float (fp16 values are used exactly as float64)
@@ -349,3 +355,69 @@ def values_histogram_form(weights, codes, codebook):
             H = np.bincount(codes[:, r, j], weights=weights, minlength=Nc)
             out[j] += H @ codebook[j, r]
     return out.reshape(G * g)
+
+
+# ---------------------------------------------------------------------------
+# Codebook fitting: one EM iteration for one residual round. The abstract says
+# the codebook is trained with an Expectation-Maximization algorithm; the review
+# ("Assumptions & free parameters") describes it as alternating assignment and
+# update in the manner of k-means, stabilised by soft assignment and annealing,
+# and ("Referee Report", Significance) notes that the update has a closed form.
+# Reading taken: round r is fitted on the residuals the earlier rounds leave
+# (greedy, as `encode`); the objective is the squared reconstruction error of
+# each group; the annealed soft assignment is a softmax over -distance /
+# temperature, and temperature 0 is the hard (nearest-entry) assignment.
+# ---------------------------------------------------------------------------
+
+
+def em_round_residuals(x: np.ndarray, codebook: np.ndarray, round_index: int) -> np.ndarray:
+    """Residuals [N, H, G, g] that round `round_index` is fitted on: each group
+    reduced greedily by the nearest entry of every earlier round."""
+    x = np.asarray(x, dtype=np.float64)
+    cb = np.asarray(codebook, dtype=np.float64)
+    N, H, D = x.shape
+    _, G, R, Nc, g = cb.shape
+    e = x.reshape(N, H, G, g).copy()
+    for r in range(round_index):
+        entries = cb[:, :, r]  # [H, G, Nc, g]
+        best = np.argmin(sq_distances(e, entries[None]), axis=-1)  # [N, H, G], first index on ties
+        e = e - np.take_along_axis(entries[None], best[..., None, None], axis=-2)[..., 0, :]
+    return e
+
+
+def em_step(x: np.ndarray, codebook: np.ndarray, round_index: int, temperature: float, min_mass: float = 0.0):
+    """One EM iteration for round `round_index` of `codebook` [H, G, R, Nc, g].
+
+    E-step: for each residual e (see em_round_residuals) and the round's entries
+    c_l, d_l = |e - c_l|^2; responsibilities w_l = exp(-(d_l - min d) / T) / sum
+    for T > 0, one-hot on the nearest entry (lowest index on ties) for T = 0.
+    M-step: c_l = sum_n w_nl e_n / sum_n w_nl, the minimiser of
+    sum_n w_nl |e_n - c_l|^2; an entry whose mass sum_n w_nl is not above
+    min_mass keeps its value.
+    Returns (entries of the round [H, G, Nc, g], mass [H, G, Nc]), float64."""
+    cb = np.asarray(codebook, dtype=np.float64)
+    e = em_round_residuals(x, cb, round_index)  # [N, H, G, g]
+    entries = cb[:, :, round_index]  # [H, G, Nc, g]
+    d = sq_distances(e, entries[None])  # [N, H, G, Nc]
+    if temperature > 0:
+        w = np.exp(-(d - d.min(axis=-1, keepdims=True)) / temperature)
+        w = w / w.sum(axis=-1, keepdims=True)
+    else:
+        w = np.zeros_like(d)
+        np.put_along_axis(w, np.argmin(d, axis=-1)[..., None], 1.0, axis=-1)
+    mass = w.sum(axis=0)  # [H, G, Nc]
+    sums = np.einsum("nhgl,nhgi->hgli", w, e)  # [H, G, Nc, g]
+    new = entries.copy()
+    upd = mass > min_mass
+    new[upd] = sums[upd] / mass[upd][:, None]
+    return new, mass
+
+
+def reconstruction_error(x: np.ndarray, codebook: np.ndarray) -> float:
+    """Mean squared error of the greedy residual encoding: sum over rounds of the
+    chosen entries against x, averaged over every scalar."""
+    x = np.asarray(x, dtype=np.float64)
+    cb = np.asarray(codebook, dtype=np.float64)
+    codes, _ = encode(x, cb)
+    xh = dequantize(codes, cb)
+    return float(np.mean((x - xh) ** 2))

@@ -129,3 +129,34 @@ def test_mutant_table_form_conjugate(monkeypatch):
         return s * sm_scale
     monkeypatch.setattr(O, "scores_table_form", bad)
     _expect_fail(P.test_table_form_scores_equal_dense_scores)
+
+
+def test_mutant_em_unnormalised_soft_weights(monkeypatch):
+    def bad(x, codebook, round_index, temperature, min_mass=0.0):
+        cb = np.asarray(codebook, dtype=np.float64)
+        e = O.em_round_residuals(x, cb, round_index)
+        entries = cb[:, :, round_index]
+        d = O.sq_distances(e, entries[None])
+        w = np.exp(-(d - d.min(axis=-1, keepdims=True)) / temperature) if temperature > 0 else \
+            (d == d.min(axis=-1, keepdims=True)).astype(float)
+        mass = w.sum(axis=0)
+        new = np.einsum("nhgl,nhgi->hgli", w, e) / np.maximum(mass, 1e-300)[..., None]
+        return new, mass  # weights not normalised per vector
+    monkeypatch.setattr(O, "em_step", bad)
+    _expect_fail(P.test_em_infinite_temperature_gives_the_mean_of_all_residuals)
+
+
+def test_mutant_em_ignores_earlier_rounds(monkeypatch):
+    real = O.em_round_residuals
+    monkeypatch.setattr(O, "em_round_residuals", lambda x, cb, r: real(x, cb, 0))
+    _expect_fail(P.test_em_later_round_fits_what_earlier_rounds_leave)
+
+
+def test_mutant_em_update_is_not_the_mean(monkeypatch):
+    real = O.em_step
+
+    def bad(x, codebook, round_index, temperature, min_mass=0.0):
+        new, mass = real(x, codebook, round_index, temperature, min_mass)
+        return 0.5 * (new + np.asarray(codebook, dtype=np.float64)[:, :, round_index]), mass  # half step
+    monkeypatch.setattr(O, "em_step", bad)
+    _expect_fail(P.test_em_hard_step_equals_brute_force_lloyd_step)

@@ -348,3 +348,113 @@ def test_encode_then_attend_end_to_end_small():
     codes, _ = O.encode(x, cb)
     err = np.abs(O.dequantize(codes, cb) - x).max()
     assert err < 0.1
+
+
+# ---------------------------------------------------------------- codebook fitting (EM)
+
+def _em_data(seed, N, H, G, g, Nc, R):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((N, H, G * g))
+    cb = rng.standard_normal((H, G, R, Nc, g))
+    return x, cb
+
+
+def test_em_hard_step_equals_brute_force_lloyd_step():
+    """T = 0, round 0: every entry becomes the plain mean of the vectors whose
+    nearest entry it is, found here by explicit loops over every entry."""
+    x, cb = _em_data(11, 60, 2, 2, 2, 5, 1)
+    new, mass = O.em_step(x, cb, 0, 0.0)
+    N, H, D = x.shape
+    G, g, Nc = 2, 2, 5
+    for h in range(H):
+        for j in range(G):
+            members = [[] for _ in range(Nc)]
+            for n in range(N):
+                e = x[n, h, j * g:(j + 1) * g]
+                best, bd = 0, None
+                for l in range(Nc):
+                    d = sum((e[i] - cb[h, j, 0, l, i]) ** 2 for i in range(g))
+                    if bd is None or d < bd:
+                        best, bd = l, d
+                members[best].append(e)
+            for l in range(Nc):
+                assert mass[h, j, l] == len(members[l])
+                want = np.mean(members[l], axis=0) if members[l] else cb[h, j, 0, l]
+                assert np.allclose(new[h, j, l], want, rtol=0, atol=1e-12)
+
+
+def test_em_infinite_temperature_gives_the_mean_of_all_residuals():
+    """T -> infinity: uniform responsibilities, so every entry becomes the mean of
+    all residuals (round 1: x minus the nearest round-0 entry) with mass N / Nc."""
+    x, cb = _em_data(12, 80, 1, 3, 4, 6, 2)
+    new, mass = O.em_step(x, cb, 1, 1e15)
+    e = O.em_round_residuals(x, cb, 1)  # [N, 1, 3, 4]
+    # round-0 residual by explicit nearest-entry search
+    for j in range(3):
+        for n in range(80):
+            v = x[n, 0, 4 * j:4 * j + 4]
+            l = int(np.argmin([np.sum((v - cb[0, j, 0, k]) ** 2) for k in range(6)]))
+            assert np.allclose(e[n, 0, j], v - cb[0, j, 0, l], atol=1e-15)
+        assert np.allclose(mass[0, j], 80 / 6, rtol=1e-12)
+        assert np.allclose(new[0, j], e[:, 0, j].mean(axis=0)[None, :], atol=1e-9)
+
+
+def test_em_small_temperature_approaches_hard_assignment():
+    x, cb = _em_data(13, 200, 1, 2, 8, 16, 1)
+    hard, mh = O.em_step(x, cb, 0, 0.0)
+    soft, ms = O.em_step(x, cb, 0, 1e-6)
+    d = O.sq_distances(x.reshape(200, 1, 2, 8), cb[:, :, 0][None])
+    part = np.partition(d, 1, axis=-1)
+    assert (part[..., 1] - part[..., 0]).min() > 1e-3  # no near-ties: 1e-3 / 1e-6 makes the runner-up weight < e^-1000
+    assert np.allclose(soft, hard, atol=1e-12) and np.allclose(ms, mh, atol=1e-12)
+
+
+def test_em_hard_iterations_never_increase_the_reconstruction_error():
+    """Lloyd's iteration: neither the closed-form update nor the re-assignment
+    can raise the squared error of a one-round quantiser."""
+    x, cb = _em_data(14, 500, 2, 4, 4, 8, 1)
+    err = [O.reconstruction_error(x, cb)]
+    for _ in range(6):
+        new, _ = O.em_step(x, cb, 0, 0.0)
+        cb = cb.copy()
+        cb[:, :, 0] = new
+        err.append(O.reconstruction_error(x, cb))
+    assert all(b <= a + 1e-12 for a, b in zip(err, err[1:])), err
+    assert err[-1] < 0.8 * err[0]
+
+
+def test_em_fixed_point_and_unused_entries():
+    """A codebook holding the data points themselves is a fixed point of the hard
+    step; entries no vector picks keep their value, and min_mass keeps entries
+    whose mass is too small."""
+    rng = np.random.default_rng(15)
+    pts = rng.standard_normal((5, 4))
+    x = np.repeat(pts, [3, 1, 4, 2, 5], axis=0)[:, None, :]  # [15, 1, 4]: one group of g = 4
+    cb = np.zeros((1, 1, 1, 8, 4))
+    cb[0, 0, 0, :5] = pts
+    cb[0, 0, 0, 5:] = 100.0 + rng.standard_normal((3, 4))  # far away: never chosen
+    new, mass = O.em_step(x, cb, 0, 0.0)
+    assert np.allclose(new, cb[:, :, 0], rtol=0, atol=1e-14) and list(mass[0, 0]) == [3, 1, 4, 2, 5, 0, 0, 0]
+    assert np.array_equal(new[0, 0, 5:], cb[0, 0, 0, 5:])  # unused entries: bit-identical
+    moved = cb.copy()
+    moved[0, 0, 0, :5] += 0.01
+    new2, _ = O.em_step(x, moved, 0, 0.0, min_mass=2.5)
+    assert np.allclose(new2[0, 0, [0, 2, 4]], pts[[0, 2, 4]], atol=1e-14)   # mass 3, 4, 5 -> the mean
+    assert np.array_equal(new2[0, 0, [1, 3]], moved[0, 0, 0, [1, 3]])       # mass 1, 2 <= 2.5 -> kept
+
+
+def test_em_later_round_fits_what_earlier_rounds_leave():
+    """Round 1 is fitted on x minus round 0's choice: with round 0 holding the
+    exact data points the residuals are zero, so every used round-1 entry moves
+    to 0; the fitted codebook then reconstructs x exactly."""
+    rng = np.random.default_rng(16)
+    pts = rng.standard_normal((4, 6))
+    x = np.repeat(pts, 3, axis=0)[:, None, :]  # [12, 1, 6]
+    cb = np.zeros((1, 1, 2, 4, 6))
+    cb[0, 0, 0] = pts
+    cb[0, 0, 1] = rng.standard_normal((4, 6))
+    new, mass = O.em_step(x, cb, 1, 0.0)
+    used = mass[0, 0] > 0
+    assert used.any() and np.allclose(new[0, 0][used], 0.0, atol=1e-15)
+    cb[0, 0, 1] = new[0, 0]
+    assert O.reconstruction_error(x, cb) < 1e-30
