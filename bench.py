@@ -74,6 +74,8 @@ def parse():
     ap.add_argument("--naive", action="store_true",
                     help="time the comparison path (dequantise the codes to fp16, then dense attention) against "
                          "commvq_decode_attention on the same 128K 1-bit caches, instead of the headline step")
+    ap.add_argument("--em", action="store_true",
+                    help="time one EM iteration of codebook fitting (commvq_em_step) on the prefill workload's keys")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain streaming kernel (fp32 negate) over this many MiB, 5 times, and exit; "
                          "its FETCH_SIZE/WRITE_SIZE counters calibrate the decode kernel's")
@@ -373,6 +375,67 @@ def bench_naive(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_em(args):
+    """One EM iteration of codebook fitting on the prefill workload's key tensor
+    (131072 tokens x 8 KV heads, heavy-tailed channels, g = 8, Nc' = 256): round
+    0 at temperature 0 (nearest entry) and 1, and round 1 of a two-round
+    codebook at temperature 0 (which first reduces every vector by its round-0
+    choice). Each is timed over the steps with HIP events on the launch stream."""
+    import torch
+
+    from long_context_attention_commvq_amd import _lib, api, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS["llama8b_encode128k_b4_2bit"]
+    N, H, D, g, Nc = w.context, w.n_kv_heads, w.head_dim, w.group_size, w.n_entries
+    G = D // g
+    x = torch.from_numpy(synth.kv(w.seed + 10, N, H, D, heavy_tail=True)).to(dev)
+    q = api.Quantizer(torch.from_numpy(synth.codebook(w.seed + 1, H, D, g, Nc, 2)).to(dev), g)
+    work = torch.empty(int(_lib.commvq_em_work_bytes(q.desc)), dtype=torch.uint8, device=dev)
+    new = torch.empty_like(q.entries)
+    stream = torch.cuda.current_stream()
+    sid = stream.cuda_stream
+    out = {}
+    for label, r, T in [("round0_hard", 0, 0.0), ("round0_soft_T1", 0, 1.0), ("round1_hard", 1, 0.0)]:
+        def step():
+            _lib.commvq_em_step(q.desc, x.data_ptr(), N, H * D, r, T, 0.0, new.data_ptr(), None, work.data_ptr(),
+                                work.numel(), sid)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(args.steps):
+            step()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / args.steps
+        # vector-ALU work: per (vector, group, entry) of each round searched, g subtractions and g FMAs for the
+        # distance and one compare-select in the row minimum; the fitted round at temperature > 0 adds two
+        # exponentials and g + 1 FMAs of the weighted sums
+        per_entry = (r + 1) * (2 * g + 1) + (2 + g + 1 if T > 0 else 0)
+        ops = N * H * G * Nc * per_entry
+        out[label] = {"ms": ms, "vectors_per_s": N * H * G / (ms * 1e-3),
+                      "achieved_T_lane_ops": ops / (ms * 1e-3) / 1e12,
+                      "frac_valu": ops / (ms * 1e-3) / VALU_PEAK_LANE_OPS}
+        print(f"[bench] em {label}: {ms:.2f} ms", file=sys.stderr, flush=True)
+    main_rec = out["round0_hard"]
+    rec = {
+        "metric": "codebook-fitting EM iteration, (vector, group) pairs per second (131072 tokens x 8 KV heads x 16 groups)",
+        "value": main_rec["vectors_per_s"], "unit": "vector-groups/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": main_rec["ms"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": "llama8b_encode128k_b4_2bit keys", "tokens": N, "n_kv_heads": H, "head_dim": D,
+                   "group_size": g, "n_entries": Nc, "step": "commvq_em_step, round 0, temperature 0"},
+        "roofline": {"bound": "alu", "achieved": main_rec["achieved_T_lane_ops"], "peak": VALU_PEAK_LANE_OPS / 1e12,
+                     "unit": "T lane-ops/s", "frac": main_rec["frac_valu"],
+                     "work": "(2 g + 1) vector ops per (vector, group, entry, round searched)"},
+        "variants": out,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -387,6 +450,9 @@ def main():
         return
     if args.naive:
         bench_naive(args)
+        return
+    if args.em:
+        bench_em(args)
         return
     if args.workload != WORKLOAD:
         bench_decode_workload(args)

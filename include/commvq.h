@@ -240,6 +240,45 @@ int32_t commvq_dense_decode_attention(const commvq_rope* rope, const float* q, c
                                       float sm_scale, float* out, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
+/* ---- codebook fitting ------------------------------------------------------
+ * The codebook is trained with an Expectation-Maximization algorithm
+ * (abstract); the review ("Assumptions & free parameters") describes it as
+ * alternating assignment and update in the k-means manner, stabilised by soft
+ * assignment and annealing, and ("Referee Report", Significance) notes the
+ * closed-form update. One call is one iteration for one residual round; a
+ * caller anneals by lowering the temperature over iterations and fits the
+ * rounds in order. */
+
+/* Bytes of the fp32 work buffer commvq_em_step needs for this codebook:
+ * Hkv * (D/g) * Nc' * (g + 1) * 4; negative commvq_status if invalid. */
+int64_t commvq_em_work_bytes(const commvq_codebook* cb);
+
+/* One EM iteration fitting round `round` of `cb` to n_tokens vectors of every
+ * KV head and group:
+ *   E-step: each group of g scalars is reduced greedily by the nearest entry of
+ *     rounds 0 .. round-1 (fp32 squared distance, lowest index on ties, as
+ *     commvq_encode); for that residual e, d_l = |e - c_l|^2 over the round's
+ *     entries and w_l = exp((min d - d_l) / temperature) / sum over l, or, for
+ *     temperature 0, 1 on the nearest entry (lowest index on ties) and 0 else.
+ *   M-step: c_l = sum w_l e / sum w_l over the vectors (fp32 sums, written as
+ *     fp16); an entry whose mass sum w_l is not above min_mass keeps its value.
+ *   x            device fp16, token t head h scalar d at
+ *                x[t * x_token_stride + h * D + d] (stride in elements >= Hkv*D)
+ *   new_entries  device fp16 with cb->entries' layout, 16-byte aligned: the
+ *                round's entries are written, nothing else (it may be
+ *                cb->entries itself: the update runs after every read)
+ *   mass_out     NULL or device fp32 [Hkv][D/g][Nc']: sum w_l per entry
+ *   work         device, >= commvq_em_work_bytes(cb), 256-byte aligned; no
+ *                initialisation needed; calls sharing it must not overlap.
+ * Requires n_tokens >= 1, 0 <= round < n_rounds, finite temperature >= 0 and
+ * min_mass >= 0 (else COMMVQ_ERR_INVALID_ARG); the fitted round's staging
+ * (round + 1) * Nc' * g + 256 * g + 16 * Nc' floats must fit 160 KiB of LDS
+ * (else COMMVQ_ERR_HIP). */
+int32_t commvq_em_step(const commvq_codebook* cb, const void* x, int64_t n_tokens,
+                       int64_t x_token_stride, int32_t round, float temperature, float min_mass,
+                       void* new_entries, float* mass_out, void* work, size_t work_bytes,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,7 +35,7 @@ EXPORTED = [
     "commvq_abi_version", "commvq_last_error", "commvq_validate_codebook", "commvq_bits_per_scalar",
     "commvq_code_bytes_per_token", "commvq_decode_workspace_bytes", "commvq_encode", "commvq_append",
     "commvq_decode_attention", "commvq_decode_step", "commvq_dequantize_kv", "commvq_dense_workspace_bytes",
-    "commvq_dense_decode_attention",
+    "commvq_dense_decode_attention", "commvq_em_work_bytes", "commvq_em_step",
 ]
 
 
@@ -99,6 +99,11 @@ def lib():
         L.commvq_dense_decode_attention.argtypes = [POINTER(commvq_rope), c_void_p, c_void_p, c_void_p, c_void_p,
                                                     c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                                     c_float, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.commvq_em_work_bytes.restype = c_int64
+        L.commvq_em_work_bytes.argtypes = [CB]
+        L.commvq_em_step.restype = c_int32
+        L.commvq_em_step.argtypes = [CB, c_void_p, c_int64, c_int64, c_int32, c_float, c_float, c_void_p, c_void_p,
+                                     c_void_p, c_size_t, c_void_p]
         _lib = L
     return _lib
 
@@ -215,3 +220,14 @@ def commvq_dense_decode_attention(rope: commvq_rope, q, q_pos, k, v, seq_lens, b
         ctypes.byref(rope), _ptr(q), _ptr(q_pos), _ptr(k), _ptr(v), _ptr(seq_lens), batch, n_q_heads, n_kv_heads,
         head_dim, cache_len, max_seq_len, float(sm_scale), _ptr(out), _ptr(workspace), int(workspace_bytes),
         _stream(stream, q, out)))
+
+
+def commvq_em_work_bytes(cb: commvq_codebook) -> int:
+    return lib().commvq_em_work_bytes(ctypes.byref(cb))
+
+
+def commvq_em_step(cb: commvq_codebook, x, n_tokens: int, x_token_stride: int, round_index: int, temperature: float,
+                   min_mass: float, new_entries, mass_out, work, work_bytes: int, stream=None) -> int:
+    return _check(lib().commvq_em_step(
+        ctypes.byref(cb), _ptr(x), n_tokens, x_token_stride, round_index, float(temperature), float(min_mass),
+        _ptr(new_entries), _ptr(mass_out), _ptr(work), int(work_bytes), _stream(stream, x, new_entries)))

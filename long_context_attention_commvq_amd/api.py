@@ -160,3 +160,30 @@ def dense_decode_attention(q: torch.Tensor, q_pos: torch.Tensor, k: torch.Tensor
     _lib.commvq_dense_decode_attention(rope, q, q_pos, k, v, seq_lens, B, Hq, Hkv, D, Lmax, max_seq_len, sm_scale,
                                        out, workspace.buf, workspace.nbytes)
     return out
+
+
+# ---- codebook fitting -----------------------------------------------------------
+
+def em_step(quant: Quantizer, x: torch.Tensor, round_index: int, temperature: float = 0.0, min_mass: float = 0.0,
+            new_entries: torch.Tensor | None = None, work: torch.Tensor | None = None,
+            with_mass: bool = False):
+    """One EM iteration for round `round_index` of `quant`'s codebook on x fp16
+    [N, Hkv, D]. Returns the entries tensor holding the update (in place in
+    quant.entries unless new_entries is given) and, with with_mass, the mass
+    fp32 [Hkv, D/g, Nc']."""
+    N, H, D = x.shape
+    x = x.contiguous()
+    if new_entries is None:
+        new_entries = quant.entries
+    if work is None:
+        n = _lib.commvq_em_work_bytes(quant.desc)
+        if n < 0:
+            raise _lib.CommvqError(int(n), _lib.commvq_last_error())
+        work = torch.empty(int(n), dtype=torch.uint8, device=x.device)
+    mass = None
+    if with_mass:
+        mass = torch.empty((quant.n_kv_heads, quant.head_dim // quant.group_size, quant.n_entries),
+                           dtype=torch.float32, device=x.device)
+    _lib.commvq_em_step(quant.desc, x, N, H * D, round_index, temperature, min_mass, new_entries, mass, work,
+                        work.numel())
+    return (new_entries, mass) if with_mass else new_entries

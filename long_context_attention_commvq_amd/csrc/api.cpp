@@ -508,3 +508,59 @@ int32_t commvq_dense_decode_attention(const commvq_rope* rope, const float* q, c
 }
 
 }  // extern "C"
+
+// ---- codebook fitting --------------------------------------------------------
+
+extern "C" {
+
+int64_t commvq_em_work_bytes(const commvq_codebook* cb) {
+  g_err[0] = 0;
+  commvq::CbShape s;
+  const int32_t st = check_shape(cb, "codebook", &s);
+  if (st) return st;
+  return (int64_t)commvq::em_work_bytes(s);
+}
+
+int32_t commvq_em_step(const commvq_codebook* cb, const void* x, int64_t n_tokens, int64_t x_token_stride,
+                       int32_t round, float temperature, float min_mass, void* new_entries, float* mass_out,
+                       void* work, size_t work_bytes, void* stream) {
+  g_err[0] = 0;
+  commvq::CbShape s;
+  int32_t st = check_shape(cb, "codebook", &s);
+  if (st) return st;
+  if (n_tokens < 1) return fail(COMMVQ_ERR_INVALID_ARG, "n_tokens %lld < 1", (long long)n_tokens);
+  if (round < 0 || round >= s.R) return fail(COMMVQ_ERR_INVALID_ARG, "round %d not in [0, %d)", round, s.R);
+  if (!std::isfinite(temperature) || temperature < 0.f)
+    return fail(COMMVQ_ERR_INVALID_ARG, "temperature must be finite and >= 0");
+  if (!std::isfinite(min_mass) || min_mass < 0.f) return fail(COMMVQ_ERR_INVALID_ARG, "min_mass must be finite and >= 0");
+  if (x_token_stride < (int64_t)s.Hkv * s.D)
+    return fail(COMMVQ_ERR_INVALID_ARG, "x_token_stride %lld < n_kv_heads*head_dim", (long long)x_token_stride);
+  st = check_entries(cb, "codebook");
+  if (st) return st;
+  if (!x || !new_entries) return fail(COMMVQ_ERR_INVALID_ARG, "null x or new_entries pointer");
+  if (reinterpret_cast<uintptr_t>(x) & 1) return fail(COMMVQ_ERR_INVALID_ARG, "x must be 2-byte aligned");
+  if (reinterpret_cast<uintptr_t>(new_entries) & 15)
+    return fail(COMMVQ_ERR_INVALID_ARG, "new_entries must be 16-byte aligned");
+  if (mass_out && (reinterpret_cast<uintptr_t>(mass_out) & 3))
+    return fail(COMMVQ_ERR_INVALID_ARG, "mass_out must be 4-byte aligned");
+  const size_t need = commvq::em_work_bytes(s);
+  if (!work || work_bytes < need)
+    return fail(COMMVQ_ERR_WORKSPACE, "work buffer of %zu bytes is smaller than the %zu required", work_bytes, need);
+  if (reinterpret_cast<uintptr_t>(work) & 255) return fail(COMMVQ_ERR_WORKSPACE, "work must be 256-byte aligned");
+  if ((n_tokens + 255) / 256 > INT32_MAX) return fail(COMMVQ_ERR_UNSUPPORTED, "n_tokens exceeds the launch grid");
+  commvq::EmArgs a{};
+  a.x = static_cast<const _Float16*>(x);
+  a.n_tokens = n_tokens;
+  a.x_token_stride = x_token_stride;
+  a.cb = static_cast<const _Float16*>(cb->entries);
+  a.new_cb = static_cast<_Float16*>(new_entries);
+  a.work = static_cast<float*>(work);
+  a.mass_out = mass_out;
+  a.round = round;
+  a.temperature = temperature;
+  a.min_mass = min_mass;
+  a.s = s;
+  return hip_status(commvq::launch_em_step(a, static_cast<hipStream_t>(stream)), "commvq_em_step launch");
+}
+
+}  // extern "C"

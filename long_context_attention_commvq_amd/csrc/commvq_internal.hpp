@@ -94,6 +94,22 @@ struct DenseArgs {
   float sm_scale;
 };
 
+// Codebook fitting: one EM iteration for round `round` (fp32 accumulators
+// work [Hkv][G][Nc][g + 1]: responsibility-weighted sums, then the mass).
+struct EmArgs {
+  const _Float16* x;          // token t, head h at x + t * x_token_stride + h * D
+  int64_t n_tokens;
+  int64_t x_token_stride;     // elements
+  const _Float16* cb;         // [Hkv][G][R][Nc][g], read
+  _Float16* new_cb;           // same layout; the fitted round's entries are written (may equal cb)
+  float* work;
+  float* mass_out;            // nullable [Hkv][G][Nc]
+  int round;
+  float temperature;          // 0: nearest entry
+  float min_mass;
+  CbShape s;
+};
+
 // Raises a kernel's dynamic-LDS limit to the whole 160 KiB of a CU, once per
 // device: `done` is a per-kernel bit set of the devices already configured.
 inline hipError_t allow_full_lds(const void* kernel, std::atomic<uint64_t>& done) {
@@ -123,5 +139,7 @@ hipError_t launch_dequant_kv(const DequantArgs& a, const PhaseTable& ph, hipStre
 size_t dense_workspace_bytes(int B, int Hq, int max_len);
 // dense_decode_kernel, then the chunk merge into a.out
 hipError_t launch_dense_decode(const DenseArgs& a, const PhaseTable& ph, hipStream_t stream);
+size_t em_work_bytes(const CbShape& s);
+hipError_t launch_em_step(const EmArgs& a, hipStream_t stream);
 
 }  // namespace commvq

@@ -1,0 +1,209 @@
+// Codebook fitting: one EM iteration for one residual round of a codebook.
+//
+// The abstract says the codebook is trained with an Expectation-Maximization
+// algorithm; the review ("Pith review of CommVQ", "Assumptions & free
+// parameters") describes alternating assignment and update in the k-means
+// manner with soft assignment and annealing, and ("Referee Report",
+// Significance) a closed-form update. For round r of every (KV head, group):
+//  E-step: each vector is reduced greedily by the nearest entry of rounds
+//          0..r-1 (squared Euclidean distance in fp32, lowest index on ties, as
+//          the encoder); for the residual e and the round's entries c_l,
+//          d_l = |e - c_l|^2 and w_l = exp((min d - d_l) / T) / sum over l
+//          (T > 0), or 1 for the nearest entry and 0 elsewhere (T = 0);
+//  M-step: c_l = sum_n w_nl e_n / sum_n w_nl (kept where that mass is not
+//          above min_mass).
+// Three launches: a fill of the fp32 accumulators, em_accumulate_kernel, and
+// em_update_kernel.
+//
+// em_accumulate_kernel<g>: a workgroup per (256 vectors, KV head) walks the
+// groups; per group it stages rounds 0..r of the codebook (fp32) and the 256
+// vectors' residuals in LDS. For 16 vectors at a time, thread l computes the
+// distances to entry l; each wavefront reduces four vectors' rows (minimum,
+// lowest index, and for the fitted round the sum of the soft weights); then
+// either the residuals are reduced by their nearest entries (earlier rounds)
+// or thread l adds w_nl e_n and w_nl to its registers (the fitted round). The
+// workgroup's sums go to the accumulators with fp32 atomics.
+
+#include "commvq_internal.hpp"
+
+namespace commvq {
+namespace {
+
+constexpr int kEmThreads = 256, kEmTokens = 256, kEmSub = 16;
+
+__device__ __forceinline__ float em_wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__global__ __launch_bounds__(256) void em_fill_kernel(float* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0.f;
+}
+
+template <int GS>
+__global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
+  extern __shared__ float em_smem[];
+  const CbShape s = a.s;
+  const int Nc = s.Nc, G = s.G, r = a.round;
+  const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * kEmTokens;
+  const int nt = (int)min((int64_t)kEmTokens, a.n_tokens - t0);
+  float* cbf = em_smem;                          // [r + 1][Nc][GS]
+  float* res = cbf + (size_t)(r + 1) * Nc * GS;  // [kEmTokens][GS]
+  float* dist = res + kEmTokens * GS;            // [kEmSub][Nc]
+  float* rmin = dist + kEmSub * Nc;              // [kEmSub]
+  float* rsum = rmin + kEmSub;                   // [kEmSub]
+  int* rarg = reinterpret_cast<int*>(rsum + kEmSub);
+  const bool soft = a.temperature > 0.f;
+  const float invT = soft ? 1.f / a.temperature : 0.f;
+  for (int j = 0; j < G; ++j) {
+    __syncthreads();  // the previous group's reads of LDS are done
+    const _Float16* cbj = a.cb + ((size_t)h * G + j) * s.R * Nc * GS;
+    for (int i = tid; i < (r + 1) * Nc * GS; i += kEmThreads) cbf[i] = (float)cbj[i];
+    for (int i = tid; i < kEmTokens * GS; i += kEmThreads) {
+      const int n = i / GS, k = i - n * GS;
+      res[i] = n < nt ? (float)a.x[(t0 + n) * a.x_token_stride + (int64_t)h * s.D + j * GS + k] : 0.f;
+    }
+    __syncthreads();
+    float acc[GS + 1];
+#pragma unroll
+    for (int k = 0; k <= GS; ++k) acc[k] = 0.f;
+    for (int n0 = 0; n0 < nt; n0 += kEmSub) {
+      const int ns = min(kEmSub, nt - n0);
+      for (int rr = 0; rr <= r; ++rr) {
+        const float* cr = cbf + (size_t)rr * Nc * GS;
+        float dl[kEmSub];
+        if (tid < Nc) {
+          float c[GS];
+#pragma unroll
+          for (int k = 0; k < GS; ++k) c[k] = cr[tid * GS + k];
+#pragma unroll
+          for (int n = 0; n < kEmSub; ++n) {
+            float d = 0.f;
+#pragma unroll
+            for (int k = 0; k < GS; ++k) {
+              const float df = res[(n0 + n) * GS + k] - c[k];
+              d = fmaf(df, df, d);
+            }
+            dl[n] = d;
+            dist[n * Nc + tid] = d;
+          }
+        }
+        __syncthreads();
+        for (int n = wave; n < kEmSub; n += kEmThreads / 64) {
+          float m = INFINITY;
+          int mi = 0;  // (a valid index even if every distance is infinite or NaN)
+          for (int l = lane; l < Nc; l += 64) {
+            const float v = dist[n * Nc + l];
+            if (v < m) m = v, mi = l;  // a lane's entries ascend: the first of equal ones is kept
+          }
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) {
+            const float om = __shfl_xor(m, o, 64);
+            const int oi = __shfl_xor(mi, o, 64);
+            if (om < m || (om == m && oi < mi)) m = om, mi = oi;
+          }
+          float sm = 0.f;
+          if (soft && rr == r) {
+            for (int l = lane; l < Nc; l += 64) sm += __expf((m - dist[n * Nc + l]) * invT);
+            sm = em_wave_sum(sm);
+          }
+          if (lane == 0) {
+            rmin[n] = m;
+            rarg[n] = mi;
+            rsum[n] = sm;
+          }
+        }
+        __syncthreads();
+        if (rr < r) {
+          for (int i = tid; i < ns * GS; i += kEmThreads) {
+            const int n = i / GS, k = i - n * GS;
+            res[(n0 + n) * GS + k] -= cr[rarg[n] * GS + k];
+          }
+          __syncthreads();
+        } else if (tid < Nc) {
+          for (int n = 0; n < ns; ++n) {
+            const float w = soft ? __expf((rmin[n] - dl[n]) * invT) / rsum[n] : (rarg[n] == tid ? 1.f : 0.f);
+            if (w != 0.f) {
+#pragma unroll
+              for (int k = 0; k < GS; ++k) acc[k] = fmaf(w, res[(n0 + n) * GS + k], acc[k]);
+              acc[GS] += w;
+            }
+          }
+        }
+      }
+      __syncthreads();  // rows and residuals of this sub-tile are no longer read
+    }
+    if (tid < Nc) {
+      float* wk = a.work + (((size_t)h * G + j) * Nc + tid) * (GS + 1);
+#pragma unroll
+      for (int k = 0; k <= GS; ++k)
+        if (acc[k] != 0.f) atomicAdd(wk + k, acc[k]);
+    }
+  }
+}
+
+// One thread per (KV head, group, entry) of the fitted round.
+template <int GS>
+__global__ __launch_bounds__(256) void em_update_kernel(EmArgs a) {
+  const CbShape s = a.s;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)s.Hkv * s.G * s.Nc) return;
+  const int64_t hj = i / s.Nc;
+  const int l = (int)(i - hj * s.Nc);
+  const float* wk = a.work + i * (GS + 1);
+  const float m = wk[GS];
+  const size_t off = (((size_t)hj * s.R + a.round) * s.Nc + l) * GS;
+  if (m > a.min_mass) {
+#pragma unroll
+    for (int k = 0; k < GS; ++k) a.new_cb[off + k] = (_Float16)(wk[k] / m);
+  } else if (a.new_cb != a.cb) {
+#pragma unroll
+    for (int k = 0; k < GS; ++k) a.new_cb[off + k] = a.cb[off + k];
+  }
+  if (a.mass_out) a.mass_out[i] = m;
+}
+
+template <int GS>
+hipError_t launch_em_g(const EmArgs& a, hipStream_t stream) {
+  const CbShape& s = a.s;
+  const size_t work_n = (size_t)s.Hkv * s.G * s.Nc * (GS + 1);
+  const size_t fill_blocks = (work_n + 255) / 256 < 4096 ? (work_n + 255) / 256 : 4096;
+  hipLaunchKernelGGL(em_fill_kernel, dim3((unsigned)fill_blocks), dim3(256), 0, stream, a.work, work_n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t smem = ((size_t)(a.round + 1) * s.Nc * GS + kEmTokens * GS + kEmSub * s.Nc + 3 * kEmSub) * 4;
+  if (smem > 160 * 1024) return hipErrorInvalidValue;
+  static std::atomic<uint64_t> configured{0};
+  e = allow_full_lds(reinterpret_cast<const void*>(&em_accumulate_kernel<GS>), configured);
+  if (e != hipSuccess) return e;
+  const int64_t blocks = (a.n_tokens + kEmTokens - 1) / kEmTokens;
+  if (blocks > INT32_MAX || s.Hkv > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((em_accumulate_kernel<GS>), dim3((unsigned)blocks, s.Hkv), dim3(kEmThreads), smem, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t entries = (int64_t)s.Hkv * s.G * s.Nc;
+  hipLaunchKernelGGL((em_update_kernel<GS>), dim3((unsigned)((entries + 255) / 256)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t em_work_bytes(const CbShape& s) { return (size_t)s.Hkv * s.G * s.Nc * (s.g + 1) * sizeof(float); }
+
+hipError_t launch_em_step(const EmArgs& a, hipStream_t stream) {
+  switch (a.s.g) {
+    case 2: return launch_em_g<2>(a, stream);
+    case 4: return launch_em_g<4>(a, stream);
+    case 6: return launch_em_g<6>(a, stream);
+    case 8: return launch_em_g<8>(a, stream);
+    case 10: return launch_em_g<10>(a, stream);
+    case 12: return launch_em_g<12>(a, stream);
+    case 14: return launch_em_g<14>(a, stream);
+    case 16: return launch_em_g<16>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace commvq

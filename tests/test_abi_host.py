@@ -215,3 +215,29 @@ def test_dense_attention_validation_without_launch():
     assert dense(ws=None) == E.COMMVQ_ERR_WORKSPACE
     assert dense(ws=FAKE + 64) == E.COMMVQ_ERR_WORKSPACE
     assert dense(B=0) == E.COMMVQ_ERR_INVALID_ARG
+
+
+def test_em_validation_without_launch():
+    c = cb(D=128, g=8, Nc=256, R=2, H=8)
+    E = _lib
+    assert E.commvq_em_work_bytes(c) == 8 * 16 * 256 * 9 * 4
+    assert E.commvq_em_work_bytes(cb(D=127)) == E.COMMVQ_ERR_INVALID_ARG
+    L = _lib.lib()
+
+    def em(cc=c, x=FAKE, n=100, stride=1024, r=0, T=0.0, mm=0.0, new=FAKE, mass=None, work=FAKE, wb=1 << 30):
+        return L.commvq_em_step(ctypes.byref(cc), x, n, stride, r, T, mm, new, mass, work, wb, None)
+    assert em(n=0) == E.COMMVQ_ERR_INVALID_ARG
+    assert em(r=2) == E.COMMVQ_ERR_INVALID_ARG
+    assert em(r=-1) == E.COMMVQ_ERR_INVALID_ARG
+    assert em(T=-1.0) == E.COMMVQ_ERR_INVALID_ARG
+    assert em(T=float("inf")) == E.COMMVQ_ERR_INVALID_ARG
+    assert em(mm=float("nan")) == E.COMMVQ_ERR_INVALID_ARG
+    assert em(stride=1023) == E.COMMVQ_ERR_INVALID_ARG
+    assert em(x=None) == E.COMMVQ_ERR_INVALID_ARG
+    assert em(x=FAKE + 1) == E.COMMVQ_ERR_INVALID_ARG
+    assert em(new=FAKE + 8) == E.COMMVQ_ERR_INVALID_ARG
+    assert em(mass=FAKE + 2) == E.COMMVQ_ERR_INVALID_ARG
+    assert em(wb=16) == E.COMMVQ_ERR_WORKSPACE
+    assert em(work=None) == E.COMMVQ_ERR_WORKSPACE
+    assert em(work=FAKE + 64) == E.COMMVQ_ERR_WORKSPACE
+    assert em(cc=cb(entries=None)) == E.COMMVQ_ERR_INVALID_ARG

@@ -1,0 +1,164 @@
+"""GPU parity of one EM iteration of codebook fitting (commvq_em_step, through
+the C ABI) against the oracle's em_step on the same seeded inputs.
+
+Where floating point decides an integer (the greedy choice of earlier rounds,
+the nearest entry of the fitted round at temperature 0), the GPU decides in
+fp32 and the oracle in fp64; vectors whose decision is a near tie (relative
+gap below 1e-4 on the oracle's distances) are left out of the input, so that
+the remaining decisions are unique. Bars:
+- masses: equal at temperature 0 (counts), within 1e-4 relative otherwise;
+- updated entries: within half an fp16 ulp plus 1e-4 of the group's largest
+  entry (fp32 sums, one rounding to fp16);
+- entries at or below min_mass and every other round: bit-identical."""
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_attention_commvq_amd import api, synth
+from oracle import commvq_oracle as O
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TIE_REL = 1e-4
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def drop_near_ties(x, cb, r, temperature):
+    """Vectors of x [N, H, D] whose decisions (rounds < r, and round r at
+    temperature 0) all have a relative top-2 gap of at least TIE_REL."""
+    _, gaps = O.encode(x, cb)  # [N, H, R, G]
+    last = r + 1 if temperature == 0 else r
+    if last == 0:
+        return x
+    ok = (gaps[:, :, :last] >= TIE_REL).all(axis=(1, 2, 3))
+    return np.ascontiguousarray(x[ok])
+
+
+def check_update(got, mass_g, ref, mass_r, cb_old, r, temperature, min_mass):
+    """got [H, G, R, Nc, g] fp16 entries after the GPU step; ref [H, G, Nc, g],
+    mass_r [H, G, Nc] from the oracle; cb_old the entries before."""
+    got = got.astype(np.float64)
+    old = cb_old.astype(np.float64)
+    R = cb_old.shape[2]
+    for rr in range(R):
+        if rr != r:
+            assert np.array_equal(got[:, :, rr], old[:, :, rr])
+    if temperature == 0:
+        assert np.array_equal(mass_g, mass_r.astype(np.float32))
+    else:
+        assert np.allclose(mass_g, mass_r, rtol=1e-4, atol=1e-4)
+    kept = mass_r <= min_mass
+    assert np.array_equal(got[:, :, r][kept], old[:, :, r][kept])
+    upd = ~kept
+    g_r = got[:, :, r]
+    scale = np.abs(ref).max(axis=(2, 3), keepdims=True)  # per (head, group)
+    big = np.maximum(np.abs(ref), np.abs(g_r))
+    bound = 0.5 * np.spacing(big.astype(np.float16)).astype(np.float64) + 1e-4 * scale
+    excess = (np.abs(g_r - ref) / bound)[upd]
+    return float(excess.max()) if excess.size else 0.0
+
+
+@pytest.mark.parametrize("case", [
+    dict(H=2, D=128, g=8, Nc=256, R=1, r=0, N=3000, T=0.0),
+    dict(H=2, D=128, g=8, Nc=256, R=2, r=1, N=2000, T=0.0),
+    dict(H=1, D=64, g=4, Nc=16, R=3, r=2, N=1000, T=0.0, min_mass=20.0),
+    dict(H=3, D=48, g=6, Nc=8, R=1, r=0, N=517, T=0.0),        # ragged last tile of 256 vectors
+    dict(H=1, D=64, g=16, Nc=64, R=2, r=1, N=700, T=0.0),
+    dict(H=2, D=128, g=8, Nc=256, R=1, r=0, N=3000, T=0.5),
+    dict(H=1, D=64, g=4, Nc=16, R=2, r=1, N=1000, T=2.0),
+    dict(H=1, D=32, g=2, Nc=4, R=1, r=0, N=300, T=100.0),
+    dict(H=1, D=128, g=8, Nc=256, R=4, r=3, N=600, T=0.0),      # four rounds of fp32 codebook in LDS
+])
+def test_em_step_matches_oracle(case):
+    H, D, g, Nc, R, r, N, T = (case[k] for k in ("H", "D", "g", "Nc", "R", "r", "N", "T"))
+    min_mass = case.get("min_mass", 0.0)
+    seed = 4000 + 17 * D + 5 * g + Nc + 3 * R + r + int(T * 10)
+    x = synth.kv(seed, N, H, D)
+    cb = synth.codebook(seed + 1, H, D, g, Nc, R)
+    x = drop_near_ties(x, cb, r, T)
+    ref, mass_r = O.em_step(x, cb, r, T, min_mass)
+    q = api.Quantizer(dev(cb), g)
+    out = dev(cb)  # updated out of place; every other round must stay as it was
+    new, mass = api.em_step(q, dev(x), r, T, min_mass, new_entries=out, with_mass=True)
+    torch.cuda.synchronize()
+    worst = check_update(new.cpu().numpy(), mass.cpu().numpy(), ref, mass_r, cb, r, T, min_mass)
+    print(f"[em {case}] {x.shape[0]} vectors, max entry error / bound {worst:.3f}", flush=True)
+    assert worst <= 1.0
+    # in place (the codebook the quantizer holds): the same bar (the fp32 atomics
+    # may add in another order, so the bytes need not repeat)
+    _, mass2 = api.em_step(q, dev(x), r, T, min_mass, with_mass=True)
+    torch.cuda.synchronize()
+    assert check_update(q.entries.cpu().numpy(), mass2.cpu().numpy(), ref, mass_r, cb, r, T, min_mass) <= 1.0
+
+
+def test_em_annealed_iterations_track_the_oracle():
+    """Three iterations with a falling temperature, then two hard ones, each
+    GPU iteration starting from the GPU's previous codebook and the oracle's
+    from the same fp16 entries: every iteration meets the bar."""
+    H, D, g, Nc, R = 1, 64, 8, 32, 1
+    x = synth.kv(4500, 2000, H, D)
+    cb = synth.codebook(4501, H, D, g, Nc, R)
+    q = api.Quantizer(dev(cb), g)
+    xd = dev(x)
+    for it, T in enumerate([4.0, 1.0, 0.25, 0.0, 0.0]):
+        start = q.entries.cpu().numpy()
+        xs = drop_near_ties(x, start, 0, T)
+        xd = dev(xs)
+        ref, mass_r = O.em_step(xs, start, 0, T)
+        new, mass = api.em_step(q, xd, 0, T, with_mass=True)
+        torch.cuda.synchronize()
+        worst = check_update(new.cpu().numpy(), mass.cpu().numpy(), ref, mass_r, start, 0, T, 0.0)
+        print(f"[em anneal] iteration {it} T={T}: {xs.shape[0]} vectors, max error / bound {worst:.3f}", flush=True)
+        assert worst <= 1.0
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_em_full_size_128k_sampled(T):
+    """The prefill workload's key tensor (131072 tokens x 8 KV heads, g = 8,
+    Nc' = 256), round 0, in one call over every head and group; the oracle
+    recomputes three sampled (head, group) slices over all 131072 vectors. At
+    temperature 0 the few vectors with near-tie decisions may go either way:
+    the entries they touch are checked with their count allowed for."""
+    w = synth.WORKLOADS["llama8b_encode128k_b4_2bit"]
+    N, H, D, g, Nc = w.context, w.n_kv_heads, w.head_dim, w.group_size, w.n_entries
+    x = synth.kv(w.seed + 10, N, H, D, heavy_tail=True)
+    cb = synth.codebook(w.seed + 1, H, D, g, Nc, 1)
+    q = api.Quantizer(dev(cb), g)
+    print(f"[em full size T={T}] N={N} H={H}", flush=True)
+    out = dev(cb)
+    new, mass = api.em_step(q, dev(x), 0, T, new_entries=out, with_mass=True)
+    torch.cuda.synchronize()
+    got = new.cpu().numpy().astype(np.float64)
+    mass_g = mass.cpu().numpy()
+    rng = np.random.default_rng(4600)
+    for h, j in [(0, 0), (int(rng.integers(0, H)), int(rng.integers(0, D // g))), (H - 1, D // g - 1)]:
+        xs = x[:, h:h + 1, j * g:(j + 1) * g]
+        cs = cb[h:h + 1, j:j + 1]
+        ref, mass_r = O.em_step(xs, cs, 0, T)
+        ref, mass_r = ref[0, 0], mass_r[0, 0]
+        gr, mg = got[h, j, 0], mass_g[h, j]
+        scale = np.abs(ref).max()
+        bound = 0.5 * np.spacing(np.maximum(np.abs(ref), np.abs(gr)).astype(np.float16)).astype(np.float64) + 1e-4 * scale
+        if T == 0:
+            _, gaps = O.encode(xs, cs)
+            d = O.sq_distances(xs.reshape(N, 1, 1, g).astype(np.float64), cs[:, :, 0][None].astype(np.float64))
+            ties = np.flatnonzero(gaps[:, 0, 0, 0] < TIE_REL)
+            touched = np.zeros(Nc, dtype=np.int64)
+            for n in ties:  # the two nearest entries of a near-tie vector may each gain or lose it
+                top2 = np.argsort(d[n, 0, 0])[:2]
+                touched[top2] += 1
+            assert np.all(np.abs(mg - mass_r) <= touched), (h, j)
+            clean = (touched == 0) & (mass_r > 0)
+            err = (np.abs(gr - ref) / bound)[clean]
+            print(f"[em full size T=0] head {h} group {j}: {len(ties)} near-tie vectors, "
+                  f"max error / bound over {clean.sum()} untouched entries {err.max():.3f}", flush=True)
+            assert err.max() <= 1.0
+        else:
+            assert np.allclose(mg, mass_r, rtol=1e-4, atol=1e-3)
+            err = np.abs(gr - ref) / bound
+            print(f"[em full size T={T}] head {h} group {j}: max error / bound {err.max():.3f}", flush=True)
+            assert err.max() <= 1.0
