@@ -18,10 +18,12 @@
 // em_accumulate_kernel<g>: a workgroup per (256 vectors, KV head) walks the
 // groups; per group it stages rounds 0..r of the codebook (fp32) and the 256
 // vectors' residuals in LDS. For 16 vectors at a time, thread l computes the
-// distances to entry l; each wavefront reduces four vectors' rows (minimum,
-// lowest index, and for the fitted round the sum of the soft weights); then
-// either the residuals are reduced by their nearest entries (earlier rounds)
-// or thread l adds w_nl e_n and w_nl to its registers (the fitted round). The
+// distances to entry l; each wavefront reduces four vectors' rows (minimum
+// and its lowest index). For an earlier round the residuals are then reduced
+// by their nearest entries; for the fitted round at temperature 0 the
+// wavefront adds the vector and a count of 1 to its nearest entry's sums in
+// LDS (fp32 LDS atomics), and at temperature > 0 it also sums the row's soft
+// weights, after which thread l adds w_nl e_n and w_nl in registers. The
 // workgroup's sums go to the accumulators with fp32 atomics.
 
 #include "commvq_internal.hpp"
@@ -55,6 +57,7 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
   float* rmin = dist + kEmSub * Nc;              // [kEmSub]
   float* rsum = rmin + kEmSub;                   // [kEmSub]
   int* rarg = reinterpret_cast<int*>(rsum + kEmSub);
+  float* hacc = rsum + 2 * kEmSub;               // [Nc][GS + 1]: nearest-entry sums (temperature 0 only)
   const bool soft = a.temperature > 0.f;
   const float invT = soft ? 1.f / a.temperature : 0.f;
   for (int j = 0; j < G; ++j) {
@@ -65,6 +68,8 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
       const int n = i / GS, k = i - n * GS;
       res[i] = n < nt ? (float)a.x[(t0 + n) * a.x_token_stride + (int64_t)h * s.D + j * GS + k] : 0.f;
     }
+    if (!soft)
+      for (int i = tid; i < Nc * (GS + 1); i += kEmThreads) hacc[i] = 0.f;
     __syncthreads();
     float acc[GS + 1];
 #pragma unroll
@@ -73,6 +78,8 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
       const int ns = min(kEmSub, nt - n0);
       for (int rr = 0; rr <= r; ++rr) {
         const float* cr = cbf + (size_t)rr * Nc * GS;
+        const bool fitted = rr == r;
+        // distances: thread l to entry l, for the sub-tile's vectors
         float dl[kEmSub];
         if (tid < Nc) {
           float c[GS];
@@ -91,6 +98,8 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
           }
         }
         __syncthreads();
+        // rows: minimum and its lowest index; for the fitted round the soft
+        // weights' sum, or (nearest entry) the vector added to its entry's sums
         for (int n = wave; n < kEmSub; n += kEmThreads / 64) {
           float m = INFINITY;
           int mi = 0;  // (a valid index even if every distance is infinite or NaN)
@@ -104,36 +113,48 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
             const int oi = __shfl_xor(mi, o, 64);
             if (om < m || (om == m && oi < mi)) m = om, mi = oi;
           }
-          float sm = 0.f;
-          if (soft && rr == r) {
+          if (fitted && soft) {
+            float sm = 0.f;
             for (int l = lane; l < Nc; l += 64) sm += __expf((m - dist[n * Nc + l]) * invT);
             sm = em_wave_sum(sm);
-          }
-          if (lane == 0) {
-            rmin[n] = m;
+            if (lane == 0) {
+              rmin[n] = m;
+              rsum[n] = sm;
+            }
+          } else if (fitted) {
+            if (n < ns && lane <= GS) atomicAdd(&hacc[mi * (GS + 1) + lane], lane < GS ? res[(n0 + n) * GS + lane] : 1.f);
+          } else if (lane == 0) {
             rarg[n] = mi;
-            rsum[n] = sm;
           }
         }
         __syncthreads();
-        if (rr < r) {
+        if (!fitted) {
           for (int i = tid; i < ns * GS; i += kEmThreads) {
             const int n = i / GS, k = i - n * GS;
             res[(n0 + n) * GS + k] -= cr[rarg[n] * GS + k];
           }
           __syncthreads();
-        } else if (tid < Nc) {
-          for (int n = 0; n < ns; ++n) {
-            const float w = soft ? __expf((rmin[n] - dl[n]) * invT) / rsum[n] : (rarg[n] == tid ? 1.f : 0.f);
-            if (w != 0.f) {
+        } else if (soft && tid < Nc) {
 #pragma unroll
-              for (int k = 0; k < GS; ++k) acc[k] = fmaf(w, res[(n0 + n) * GS + k], acc[k]);
-              acc[GS] += w;
+          for (int n = 0; n < kEmSub; ++n) {
+            if (n < ns) {
+              const float w = __expf((rmin[n] - dl[n]) * invT) / rsum[n];
+              if (w != 0.f) {
+#pragma unroll
+                for (int k = 0; k < GS; ++k) acc[k] = fmaf(w, res[(n0 + n) * GS + k], acc[k]);
+                acc[GS] += w;
+              }
             }
           }
         }
       }
-      __syncthreads();  // rows and residuals of this sub-tile are no longer read
+    }
+    if (!soft) {
+      __syncthreads();  // every nearest-entry sum is in
+      if (tid < Nc) {
+#pragma unroll
+        for (int k = 0; k <= GS; ++k) acc[k] = hacc[tid * (GS + 1) + k];
+      }
     }
     if (tid < Nc) {
       float* wk = a.work + (((size_t)h * G + j) * Nc + tid) * (GS + 1);
@@ -173,7 +194,8 @@ hipError_t launch_em_g(const EmArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(em_fill_kernel, dim3((unsigned)fill_blocks), dim3(256), 0, stream, a.work, work_n);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t smem = ((size_t)(a.round + 1) * s.Nc * GS + kEmTokens * GS + kEmSub * s.Nc + 3 * kEmSub) * 4;
+  const size_t smem = ((size_t)(a.round + 1) * s.Nc * GS + kEmTokens * GS + kEmSub * s.Nc + 3 * kEmSub +
+                       (a.temperature > 0.f ? 0 : (size_t)s.Nc * (GS + 1))) * 4;
   if (smem > 160 * 1024) return hipErrorInvalidValue;
   static std::atomic<uint64_t> configured{0};
   e = allow_full_lds(reinterpret_cast<const void*>(&em_accumulate_kernel<GS>), configured);
