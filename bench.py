@@ -421,6 +421,10 @@ def bench_em(args):
                       "frac_valu": ops / (ms * 1e-3) / VALU_PEAK_LANE_OPS}
         print(f"[bench] em {label}: {ms:.2f} ms", file=sys.stderr, flush=True)
     main_rec = out["round0_hard"]
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] cpu oracle sample (em_step)", file=sys.stderr, flush=True)
+        cpu = em_cpu_baseline(args.cpu_seconds, x.cpu().numpy(), q.entries.cpu().numpy())
     rec = {
         "metric": "codebook-fitting EM iteration, (vector, group) pairs per second (131072 tokens x 8 KV heads x 16 groups)",
         "value": main_rec["vectors_per_s"], "unit": "vector-groups/s", "n_gpus": 1, "steps": args.steps,
@@ -432,8 +436,36 @@ def bench_em(args):
                      "unit": "T lane-ops/s", "frac": main_rec["frac_valu"],
                      "work": "(2 g + 1) vector ops per (vector, group, entry, round searched)"},
         "variants": out,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def em_cpu_baseline(budget_s: float, x, cb):
+    """Time the fp64 oracle's em_step (round 0, temperature 0) on (KV head,
+    group) slices of the same key tensor, each over all its vectors, until the
+    budget is spent; scale the mean slice time to all slices."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import commvq_oracle as O
+
+    N, H, D = x.shape
+    _, G, R, Nc, g = cb.shape
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    done, t_total = 0, 0.0
+    with threadpool_limits(limits=cores):
+        while done < H * G and (done < 2 or t_total < budget_s):
+            h, j = divmod(done, G)
+            xs = x[:, h:h + 1, j * g:(j + 1) * g]
+            cs = cb[h:h + 1, j:j + 1]
+            t0 = time.perf_counter()
+            O.em_step(xs, cs, 0, 0.0)
+            t_total += time.perf_counter() - t0
+            done += 1
+    t_all = t_total / done * H * G
+    return {"value": N * H * G / t_all, "unit": "vector-groups/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {H * G} (KV head, group) slices, {N} vectors each, em_step round 0 at "
+                      f"temperature 0, fp64 NumPy, BLAS threads={cores}; {t_total:.1f} s measured, scaled to all slices"}
 
 
 def main():
