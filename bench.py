@@ -258,18 +258,46 @@ def bench_decode_workload(args):
     toks = int(lens.sum())
     code_bytes = toks * H * 2 * bpt
     achieved = code_bytes / (ms * 1e-3) / 1e9
+    # beside it: dense fp16 attention over keys and values of the same shape
+    # (commvq_dense_decode_attention, one fp16 buffer pair per layer slice)
+    dense = None
+    if D == 128:
+        f16_bytes = B * H * Lmax * D * 2
+        NLd = max(1, min(args.layers, -(-(512 << 20) // (2 * f16_bytes))))
+        kv16 = [(torch.randn((B, H, Lmax, D), dtype=torch.float16, device=dev, generator=g),
+                 torch.randn((B, H, Lmax, D), dtype=torch.float16, device=dev, generator=g)) for _ in range(NLd)]
+        dws = api.DenseWorkspace(B, Hq, H, D, Lmax, dev)
+
+        def dcall(i):
+            k16, v16 = kv16[i % NLd]
+            _lib.commvq_dense_decode_attention(rope, q.data_ptr(), qpos.data_ptr(), k16.data_ptr(), v16.data_ptr(),
+                                               lens_d.data_ptr(), B, Hq, H, D, Lmax, Lmax, sm, out.data_ptr(),
+                                               dws.buf.data_ptr(), dws.nbytes, sid)
+        for i in range(args.warmup):
+            dcall(i)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(args.steps):
+            dcall(args.warmup + i)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        dms = start.elapsed_time(stop) / args.steps
+        dense = {"ms_per_step": dms, "commvq_over_dense": ms / dms, "layer_slices": NLd,
+                 "call": "commvq_dense_decode_attention over fp16 keys and values of the same shape"}
     rec = {
         "metric": METRIC, "value": toks / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp16", "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "n_q_heads": Hq, "n_kv_heads": H, "head_dim": D,
-                   "context": Lmax, "sum_len": toks, "n_rounds": w.n_rounds, "layer_slices": NL,
+                   "context": Lmax, "sum_len": toks, "group_size": w.group_size, "n_entries": w.n_entries,
+                   "n_rounds": w.n_rounds, "layer_slices": NL,
                    "step": "commvq_decode_attention over every sequence and head"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": code_bytes,
                      "avg_launch_us": ms * 1e3,
                      "kernel": "commvq_decode_attention call: decode kernel, then chunk-merge kernel"},
         "cpu_baseline": None,
+        "dense_fp16_same_shape": dense,
     }
     print(json.dumps(rec), flush=True)
 

@@ -38,12 +38,12 @@ int32_t check_shape(const commvq_codebook* cb, const char* name, commvq::CbShape
   if (D < 2 || D > 2 * commvq::kMaxPairs || (D & 1))
     return fail(COMMVQ_ERR_INVALID_ARG, "%s: head_dim %d must be even and in [2, %d]", name, D,
                 2 * commvq::kMaxPairs);
-  if (g < 2 || g > 16 || (g & 1) || D % g)
-    return fail(COMMVQ_ERR_INVALID_ARG, "%s: group_size %d must be even, in [2, 16] and divide head_dim %d",
+  if (g < 2 || g > 128 || (g & 1) || D % g)
+    return fail(COMMVQ_ERR_INVALID_ARG, "%s: group_size %d must be even, in [2, 128] and divide head_dim %d",
                 name, g, D);
   if (!is_pow2(Nc) || Nc < 2 || Nc > 256)
     return fail(COMMVQ_ERR_INVALID_ARG, "%s: n_entries %d must be a power of two in [2, 256]", name, Nc);
-  if (R < 1 || R > 4) return fail(COMMVQ_ERR_INVALID_ARG, "%s: n_rounds %d must be in [1, 4]", name, R);
+  if (R < 1 || R > 32) return fail(COMMVQ_ERR_INVALID_ARG, "%s: n_rounds %d must be in [1, 32]", name, R);
   if (cb->n_kv_heads < 1) return fail(COMMVQ_ERR_INVALID_ARG, "%s: n_kv_heads %d < 1", name, cb->n_kv_heads);
   if (cb->n_kv_heads > 65535) return fail(COMMVQ_ERR_UNSUPPORTED, "%s: n_kv_heads %d > 65535", name, cb->n_kv_heads);
   if (cb->dtype != COMMVQ_F16) return fail(COMMVQ_ERR_INVALID_ARG, "%s: dtype %d is not COMMVQ_F16", name, cb->dtype);
@@ -57,6 +57,21 @@ int32_t check_shape(const commvq_codebook* cb, const char* name, commvq::CbShape
     out->bits = ilog2(Nc);
     out->bpt = (R * (D / g) * out->bits + 7) / 8;
   }
+  return COMMVQ_OK;
+}
+
+// Group sizes the encoder and the generic decode kernel are built for.
+bool kernel_group_size(int g) { return g <= 16 || g == 32 || g == 64 || g == 128; }
+
+// The encoder keeps a tile's codes (R * D/g bytes per token, tile >= 64 tokens)
+// and one round of one group's codebook in LDS.
+int32_t check_encodable(const commvq::CbShape& s, const char* name) {
+  if (!kernel_group_size(s.g))
+    return fail(COMMVQ_ERR_UNSUPPORTED, "%s: group_size %d: the kernels take even sizes up to 16, 32, 64 or 128", name,
+                s.g);
+  if ((size_t)s.Nc * s.g * 4 + (size_t)64 * s.R * s.G > 160 * 1024)
+    return fail(COMMVQ_ERR_UNSUPPORTED, "%s: %d rounds x %d groups of codes do not fit the encoder's LDS", name, s.R,
+                s.G);
   return COMMVQ_OK;
 }
 
@@ -92,8 +107,11 @@ int32_t decode_shapes(const commvq_codebook* kcb, const commvq_codebook* vcb, in
   if (batch > 65535) return fail(COMMVQ_ERR_UNSUPPORTED, "batch %d > 65535", batch);
   if ((int64_t)((max_seq_len + 1023) / 1024) * k->Hkv > INT32_MAX)
     return fail(COMMVQ_ERR_UNSUPPORTED, "max_seq_len %d x n_kv_heads %d exceeds the launch grid", max_seq_len, k->Hkv);
-  if (k->g != 2 && k->g != 4 && k->g != 8 && k->g != 16)
-    return fail(COMMVQ_ERR_UNSUPPORTED, "decode supports group_size 2, 4, 8 or 16, not %d", k->g);
+  if (k->g != 2 && k->g != 4 && k->g != 8 && k->g != 16 && k->g != 32 && k->g != 64 && k->g != 128)
+    return fail(COMMVQ_ERR_UNSUPPORTED, "decode supports group_size 2, 4, 8, 16, 32, 64 or 128, not %d", k->g);
+  if (commvq::decode_generic_smem(*k, *v, NH) > 160 * 1024)
+    return fail(COMMVQ_ERR_UNSUPPORTED, "the query x codebook table of %d query heads x %d entries x %d pairs exceeds LDS",
+                NH, k->Nc, k->g / 2);
   return COMMVQ_OK;
 }
 
@@ -175,6 +193,8 @@ int32_t commvq_encode(const commvq_codebook* cb, const void* x, int64_t n_tokens
   commvq::CbShape s;
   int32_t st = check_shape(cb, "codebook", &s);
   if (st) return st;
+  st = check_encodable(s, "codebook");
+  if (st) return st;
   if (n_tokens < 0) return fail(COMMVQ_ERR_INVALID_ARG, "n_tokens %lld < 0", (long long)n_tokens);
   if (n_tokens == 0) return COMMVQ_OK;
   st = check_entries(cb, "codebook");
@@ -215,6 +235,8 @@ int32_t commvq_append(const commvq_codebook* cb, const void* x, int32_t batch, c
   g_err[0] = 0;
   commvq::CbShape s;
   int32_t st = check_shape(cb, "codebook", &s);
+  if (st) return st;
+  st = check_encodable(s, "codebook");
   if (st) return st;
   if (batch < 0) return fail(COMMVQ_ERR_INVALID_ARG, "batch %d < 0", batch);
   if (batch == 0) return COMMVQ_OK;
@@ -276,6 +298,10 @@ int32_t decode_impl(const commvq_codebook* kcb, const commvq_codebook* vcb, cons
   if ((reinterpret_cast<uintptr_t>(kcodes) | reinterpret_cast<uintptr_t>(vcodes)) & 15)
     return fail(COMMVQ_ERR_INVALID_ARG, "code caches must be 16-byte aligned");
   if (step) {
+    st = check_encodable(k, "key codebook");
+    if (st) return st;
+    st = check_encodable(v, "value codebook");
+    if (st) return st;
     if (!step->k_new || !step->v_new || !step->positions)
       return fail(COMMVQ_ERR_INVALID_ARG, "null k_new, v_new or positions pointer");
     if ((reinterpret_cast<uintptr_t>(step->k_new) | reinterpret_cast<uintptr_t>(step->v_new)) & 15)
@@ -420,6 +446,7 @@ int32_t commvq_dequantize_kv(const commvq_codebook* kcb, const commvq_codebook* 
   if (st) return st;
   if (k.D != v.D || k.g != v.g || k.Hkv != v.Hkv)
     return fail(COMMVQ_ERR_INVALID_ARG, "key and value codebooks disagree on head_dim, group_size or n_kv_heads");
+  if (k.g > 16) return fail(COMMVQ_ERR_UNSUPPORTED, "dequantisation supports group_size up to 16, not %d", k.g);
   st = check_rope(rope);
   if (st) return st;
   if (batch < 1) return fail(COMMVQ_ERR_INVALID_ARG, "batch %d < 1", batch);
@@ -530,6 +557,10 @@ int32_t commvq_em_step(const commvq_codebook* cb, const void* x, int64_t n_token
   if (st) return st;
   if (n_tokens < 1) return fail(COMMVQ_ERR_INVALID_ARG, "n_tokens %lld < 1", (long long)n_tokens);
   if (round < 0 || round >= s.R) return fail(COMMVQ_ERR_INVALID_ARG, "round %d not in [0, %d)", round, s.R);
+  if (s.g > 16) return fail(COMMVQ_ERR_UNSUPPORTED, "codebook fitting supports group_size up to 16, not %d", s.g);
+  if (commvq::em_accumulate_smem(s, round, temperature > 0.f) > 160 * 1024)
+    return fail(COMMVQ_ERR_UNSUPPORTED, "rounds 0..%d of %d entries x %d scalars exceed the fitting kernel's LDS", round,
+                s.Nc, s.g);
   if (!std::isfinite(temperature) || temperature < 0.f)
     return fail(COMMVQ_ERR_INVALID_ARG, "temperature must be finite and >= 0");
   if (!std::isfinite(min_mass) || min_mass < 0.f) return fail(COMMVQ_ERR_INVALID_ARG, "min_mass must be finite and >= 0");

@@ -127,6 +127,8 @@ inline hipError_t allow_full_lds(const void* kernel, std::atomic<uint64_t>& done
 // query and the launch use the same rule.
 int decode_chunk_len(const CbShape& k, const CbShape& v, int B, int Hq, int max_len, int flags);
 bool decode_fast_path(const CbShape& k, const CbShape& v, int NH, int flags);
+// LDS bytes of the generic decode kernel for a shape (at most 160 KiB can run).
+size_t decode_generic_smem(const CbShape& k, const CbShape& v, int NH);
 size_t decode_workspace_bytes(const CbShape& k, int B, int Hq, int max_len, int chunk);
 // Byte offset of the new-token area in the workspace (after the partials, 256-aligned).
 size_t decode_newtok_offset(const CbShape& k, int B, int Hq, int max_len, int chunk);
@@ -140,6 +142,7 @@ size_t dense_workspace_bytes(int B, int Hq, int max_len);
 // dense_decode_kernel, then the chunk merge into a.out
 hipError_t launch_dense_decode(const DenseArgs& a, const PhaseTable& ph, hipStream_t stream);
 size_t em_work_bytes(const CbShape& s);
+size_t em_accumulate_smem(const CbShape& s, int round, bool soft);
 hipError_t launch_em_step(const EmArgs& a, hipStream_t stream);
 
 }  // namespace commvq

@@ -207,12 +207,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, 
 
 template <int NH, int GS>
 hipError_t launch_generic(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
-  const int P = a.k.D / 2;
-  const int NW = kThreads / 64;
-  size_t table_bytes = (size_t)NH * a.k.Nc * (GS / 2) * sizeof(float2);
-  size_t hist_bytes = (size_t)NH * a.v.Nc * sizeof(uint32_t);
-  size_t smem = (2 * NH * P + NH * a.k.D + ((NH * (NW > 2 ? NW : 2) + 2 * NH + 4) & ~3)) * sizeof(float) +
-                (table_bytes > hist_bytes ? table_bytes : hist_bytes);
+  const size_t smem = decode_generic_smem(a.k, a.v, NH);
   if (smem > 160 * 1024) return hipErrorInvalidValue;
   static std::atomic<uint64_t> configured{0};
   hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&decode_generic_kernel<NH, GS>), configured);
@@ -229,11 +224,24 @@ hipError_t launch_generic_nh(const DecodeArgs& a, const PhaseTable& ph, hipStrea
     case 4: return launch_generic<NH, 4>(a, ph, stream);
     case 8: return launch_generic<NH, 8>(a, ph, stream);
     case 16: return launch_generic<NH, 16>(a, ph, stream);
+    case 32: return launch_generic<NH, 32>(a, ph, stream);
+    case 64: return launch_generic<NH, 64>(a, ph, stream);
+    case 128: return launch_generic<NH, 128>(a, ph, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
+
+size_t decode_generic_smem(const CbShape& k, const CbShape& v, int NH) {
+  // rotated queries (float2 per pair), output accumulators, reductions, then
+  // the query x codebook table of one (group, round) or a value histogram
+  const int P = k.D / 2, NW = kThreads / 64;
+  const size_t table_bytes = (size_t)NH * k.Nc * (k.g / 2) * sizeof(float2);
+  const size_t hist_bytes = (size_t)NH * v.Nc * sizeof(uint32_t);
+  return (2 * NH * P + NH * k.D + ((NH * (NW > 2 ? NW : 2) + 2 * NH + 4) & ~3)) * sizeof(float) +
+         (table_bytes > hist_bytes ? table_bytes : hist_bytes);
+}
 
 bool decode_fast_path(const CbShape& k, const CbShape& v, int NH, int flags) {
   return !(flags & 1) && k.D == 128 && k.g == 8 && k.Nc == 256 && v.Nc == 256 && k.R == v.R &&

@@ -194,8 +194,7 @@ hipError_t launch_em_g(const EmArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(em_fill_kernel, dim3((unsigned)fill_blocks), dim3(256), 0, stream, a.work, work_n);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t smem = ((size_t)(a.round + 1) * s.Nc * GS + kEmTokens * GS + kEmSub * s.Nc + 3 * kEmSub +
-                       (a.temperature > 0.f ? 0 : (size_t)s.Nc * (GS + 1))) * 4;
+  const size_t smem = em_accumulate_smem(s, a.round, a.temperature > 0.f);
   if (smem > 160 * 1024) return hipErrorInvalidValue;
   static std::atomic<uint64_t> configured{0};
   e = allow_full_lds(reinterpret_cast<const void*>(&em_accumulate_kernel<GS>), configured);
@@ -211,6 +210,13 @@ hipError_t launch_em_g(const EmArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+size_t em_accumulate_smem(const CbShape& s, int round, bool soft) {
+  // rounds 0..round of the codebook (fp32), the residuals, one sub-tile's
+  // distances, the rows' terms, and at temperature 0 the nearest-entry sums
+  return ((size_t)(round + 1) * s.Nc * s.g + (size_t)kEmTokens * s.g + (size_t)kEmSub * s.Nc + 3 * kEmSub +
+          (soft ? 0 : (size_t)s.Nc * (s.g + 1))) * sizeof(float);
+}
 
 size_t em_work_bytes(const CbShape& s) { return (size_t)s.Hkv * s.G * s.Nc * (s.g + 1) * sizeof(float); }
 

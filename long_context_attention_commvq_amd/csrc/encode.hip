@@ -17,7 +17,7 @@
 //    residual into two fp16 values (products are exact, sums fp32). The argmin
 //    compares the fp32 scores, lowest index on ties.
 //  * encode_kernel (any shape): distances accumulated term by term in fp32
-//    with fmaf against a codebook slice staged in LDS.
+//    with fmaf against the codebook of one (group, round) staged in LDS.
 //  * encode_few_kernel (n <= 64 tokens, the decode-time append): one wavefront
 //    per group, the same fp32 arithmetic as encode_kernel.
 // The two arithmetic forms may pick different entries only where two
@@ -33,8 +33,8 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a, int tile) {
   extern __shared__ float enc_smem[];
   const CbShape s = a.s;
   const int R = s.R, Nc = s.Nc, G = s.G, D = s.D, RG = s.R * s.G;
-  float* cbs = enc_smem;                                                    // [R][Nc][GS]
-  uint8_t* codes_l = reinterpret_cast<uint8_t*>(cbs + (size_t)R * Nc * GS);  // [tile][R*G]
+  float* cbs = enc_smem;                                                // [Nc][GS]: one round
+  uint8_t* codes_l = reinterpret_cast<uint8_t*>(cbs + (size_t)Nc * GS);  // [tile][R*G]
   const int tid = threadIdx.x;
   const int h = blockIdx.y;
   const int64_t t = (int64_t)blockIdx.x * tile + tid;
@@ -53,16 +53,18 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a, int tile) {
     }
   }
   for (int j = 0; j < G; ++j) {
-    __syncthreads();
-    const _Float16* src = a.cb + ((int64_t)h * G + j) * R * Nc * GS;
-    for (int i = tid; i < R * Nc * GS; i += blockDim.x) cbs[i] = (float)src[i];
-    __syncthreads();
+    float e[GS];
     if (valid) {
-      float e[GS];
 #pragma unroll
       for (int i = 0; i < GS; ++i) e[i] = (float)xp[j * GS + i];
-      for (int r = 0; r < R; ++r) {
-        const float* c = cbs + (size_t)r * Nc * GS;
+    }
+    for (int r = 0; r < R; ++r) {
+      __syncthreads();
+      const _Float16* src = a.cb + (((int64_t)h * G + j) * R + r) * Nc * GS;
+      for (int i = tid; i < Nc * GS; i += blockDim.x) cbs[i] = (float)src[i];
+      __syncthreads();
+      if (valid) {
+        const float* c = cbs;
         float best = INFINITY;
         int bi = 0;
         for (int l = 0; l < Nc; ++l) {
@@ -293,10 +295,11 @@ hipError_t launch_encode_g(const EncodeArgs& a, hipStream_t stream) {
     }
   }
   const CbShape& s = a.s;
-  const size_t cb_bytes = (size_t)s.R * s.Nc * GS * sizeof(float);
+  const size_t cb_bytes = (size_t)s.Nc * GS * sizeof(float);  // one round at a time
   int tile = 256;
   while (tile > 64 && cb_bytes + (size_t)tile * s.R * s.G > 160 * 1024) tile /= 2;
   const size_t smem = cb_bytes + (size_t)tile * s.R * s.G;
+  if (smem > 160 * 1024) return hipErrorInvalidValue;
   static std::atomic<uint64_t> configured{0};
   hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&encode_kernel<GS>), configured);
   if (e != hipSuccess) return e;
@@ -318,6 +321,9 @@ hipError_t launch_encode(const EncodeArgs& a, hipStream_t stream) {
     case 12: return launch_encode_g<12>(a, stream);
     case 14: return launch_encode_g<14>(a, stream);
     case 16: return launch_encode_g<16>(a, stream);
+    case 32: return launch_encode_g<32>(a, stream);
+    case 64: return launch_encode_g<64>(a, stream);
+    case 128: return launch_encode_g<128>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -103,4 +103,12 @@ WORKLOADS = {
         "llama8b_encode128k_b4_2bit", batch=4, n_q_heads=32, n_kv_heads=8, head_dim=128,
         context=131072, group_size=8, n_entries=256, n_rounds=2, heavy_tail=True, seed=5000,
         notes="encode 131072 x 8 heads (1% channels x8), then batch-4 decode at full context"),
+    "llama8b_ctx32k_paper_1bit": Workload(
+        "llama8b_ctx32k_paper_1bit", batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, context=32768,
+        group_size=64, n_entries=64, n_rounds=11, seed=6000,
+        notes="the paper's 1-bit quantizer (g 64, Nc' 64, R 11: 1.03 bits per scalar), B1, L32768"),
+    "llama8b_ctx32k_paper_2bit": Workload(
+        "llama8b_ctx32k_paper_2bit", batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, context=32768,
+        group_size=64, n_entries=64, n_rounds=21, seed=6100,
+        notes="the paper's 2-bit quantizer (g 64, Nc' 64, R 21: 1.97 bits per scalar), B1, L32768"),
 }

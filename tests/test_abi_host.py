@@ -56,7 +56,7 @@ def test_workspace_query():
 
 @pytest.mark.parametrize("bad", [
     dict(D=127), dict(D=0), dict(D=512), dict(g=7), dict(g=0), dict(g=18), dict(D=128, g=12),
-    dict(Nc=100), dict(Nc=1), dict(Nc=512), dict(R=0), dict(R=5), dict(H=0),
+    dict(Nc=100), dict(Nc=1), dict(Nc=512), dict(R=0), dict(R=33), dict(H=0), dict(D=256, g=256), dict(D=130, g=130),
 ])
 def test_invalid_descriptors(bad):
     c = cb(**bad)
@@ -241,3 +241,35 @@ def test_em_validation_without_launch():
     assert em(work=None) == E.COMMVQ_ERR_WORKSPACE
     assert em(work=FAKE + 64) == E.COMMVQ_ERR_WORKSPACE
     assert em(cc=cb(entries=None)) == E.COMMVQ_ERR_INVALID_ARG
+
+
+def test_wide_groups_and_many_rounds():
+    """The paper's own hyperparameters (g = 64 scalars, Nc' = 64, R = 11 or 21)
+    and g = 128 are valid descriptors; the entry points that have no kernel for
+    a shape say so with COMMVQ_ERR_UNSUPPORTED before any GPU call."""
+    E = _lib
+    L = _lib.lib()
+    for R, bits in [(11, 11 * 6 / 64), (21, 21 * 6 / 64)]:
+        c = cb(D=128, g=64, Nc=64, R=R)
+        assert E.commvq_validate_codebook(c) == 0
+        assert E.commvq_bits_per_scalar(c) == bits
+        assert E.commvq_code_bytes_per_token(c) == -(-R * 2 * 6 // 8)
+    assert E.commvq_validate_codebook(cb(D=128, g=128, Nc=64, R=32)) == 0
+    rope = _lib.make_rope(500000.0)
+
+    def enc(c):
+        return L.commvq_encode(ctypes.byref(c), FAKE, 4, c.n_kv_heads * c.head_dim, FAKE, 4096, 512, None)
+    assert enc(cb(D=96, g=24, Nc=16, R=1)) == E.COMMVQ_ERR_UNSUPPORTED          # no kernel for g = 24
+    assert enc(cb(D=256, g=2, Nc=256, R=32)) == E.COMMVQ_ERR_UNSUPPORTED        # 4096 fields per record
+    k = cb(D=128, g=128, Nc=256, R=1)
+    assert _raw_decode(k, k, rope, Hq=64) == E.COMMVQ_ERR_UNSUPPORTED           # 8 heads x 256 x 64 pairs of table
+    assert "table" in _lib.commvq_last_error()
+    assert _raw_decode(cb(D=96, g=24), cb(D=96, g=24), rope) == E.COMMVQ_ERR_UNSUPPORTED
+    w = cb(D=128, g=32, Nc=64, R=2)
+    assert L.commvq_dequantize_kv(ctypes.byref(w), ctypes.byref(w), ctypes.byref(rope), FAKE, FAKE, FAKE, 1, 64, 64,
+                                  FAKE, FAKE, None) == E.COMMVQ_ERR_UNSUPPORTED
+    assert L.commvq_em_step(ctypes.byref(w), FAKE, 10, 1024, 0, 0.0, 0.0, FAKE, None, FAKE, 1 << 30,
+                            None) == E.COMMVQ_ERR_UNSUPPORTED
+    big = cb(D=128, g=16, Nc=256, R=32)
+    assert L.commvq_em_step(ctypes.byref(big), FAKE, 10, 1024, 31, 0.0, 0.0, FAKE, None, FAKE, 1 << 30,
+                            None) == E.COMMVQ_ERR_UNSUPPORTED  # 32 rounds of fp32 codebook in LDS
