@@ -65,9 +65,11 @@ typedef enum commvq_dtype { COMMVQ_F16 = 1 } commvq_dtype;
  * R rounds, Nc' entries). */
 typedef struct commvq_codebook {
   int32_t head_dim;    /* D: even, 2..256 */
-  int32_t group_size;  /* g scalars sharing one index: even, divides D, 2..16 */
+  int32_t group_size;  /* g scalars sharing one index: even, divides D, 2..128;
+                          the kernels take even g <= 16, 32, 64 and 128 (other
+                          values: COMMVQ_ERR_UNSUPPORTED from the compute calls) */
   int32_t n_entries;   /* Nc': power of two, 2..256 */
-  int32_t n_rounds;    /* R: 1..4 */
+  int32_t n_rounds;    /* R: 1..32 */
   int32_t n_kv_heads;  /* 1 <= Hkv <= 65535 (larger: COMMVQ_ERR_UNSUPPORTED) */
   int32_t dtype;       /* COMMVQ_F16 */
   const void* entries; /* device fp16 [Hkv][D/g][R][Nc'][g]; within a group the
@@ -118,8 +120,11 @@ int64_t commvq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t 
  *   codes  device bytes; record (t, h) starts at
  *          codes + t*code_token_stride + h*code_head_stride (strides in bytes);
  *          records must not overlap; every byte of each record is written.
- * n_tokens == 0 launches nothing. Pages: "What carries the argument" (shared
- * index per group, R residual rounds). */
+ * n_tokens == 0 launches nothing. One round of one group's codebook (Nc' * g
+ * fp32) plus 64 tokens' codes (64 * R * D/g bytes) must fit 160 KiB of LDS
+ * (otherwise COMMVQ_ERR_UNSUPPORTED; commvq_append and commvq_decode_step
+ * share the rule). Pages: "What carries the argument" (shared index per
+ * group, R residual rounds). */
 int32_t commvq_encode(const commvq_codebook* cb, const void* x, int64_t n_tokens,
                       int64_t x_token_stride, uint8_t* codes, int64_t code_token_stride,
                       int64_t code_head_stride, void* stream);
@@ -143,7 +148,9 @@ int32_t commvq_append(const commvq_codebook* cb, const void* x, int32_t batch,
  *            zero output row.
  *   n_q_heads must be a multiple of Hkv; query head hq reads KV head
  *   hq / (n_q_heads / Hkv). n_q_heads / Hkv must be 1, 2, 4 or 8, group_size
- *   2, 4, 8 or 16, batch <= 65535 and ceil(max_seq_len / 1024) * Hkv < 2^31
+ *   2, 4, 8, 16, 32, 64 or 128, batch <= 65535, ceil(max_seq_len / 1024) *
+ *   Hkv < 2^31, and one (group, round)'s query x codebook table, NH * Nc' *
+ *   g/2 complex fp32 values plus the queries, must fit 160 KiB of LDS
  *   (otherwise COMMVQ_ERR_UNSUPPORTED).
  *   sm_scale multiplies q.k (normally 1/sqrt(D)).
  *   out      device fp32 [batch][n_q_heads][D]
