@@ -110,8 +110,9 @@ int32_t decode_shapes(const commvq_codebook* kcb, const commvq_codebook* vcb, in
   if (k->g != 2 && k->g != 4 && k->g != 8 && k->g != 16 && k->g != 32 && k->g != 64 && k->g != 128)
     return fail(COMMVQ_ERR_UNSUPPORTED, "decode supports group_size 2, 4, 8, 16, 32, 64 or 128, not %d", k->g);
   if (commvq::decode_generic_smem(*k, *v, NH) > 160 * 1024)
-    return fail(COMMVQ_ERR_UNSUPPORTED, "the query x codebook table of %d query heads x %d entries x %d pairs exceeds LDS",
-                NH, k->Nc, k->g / 2);
+    return fail(COMMVQ_ERR_UNSUPPORTED,
+                "decode's LDS staging for %d query heads, %d entries, %d rounds, group size %d exceeds 160 KiB", NH, k->Nc,
+                k->R, k->g);
   return COMMVQ_OK;
 }
 

@@ -29,6 +29,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kGenericTPT = 4;  // tokens per lane in the generic kernel
 constexpr int kHistShift = 20;  // fixed-point weights: w * 2^20 (chunk <= 1024 keeps sums < 2^31)
+constexpr int kWideGroup = 32;  // group sizes from which keys are rebuilt per slice instead of tabled
 
 __device__ __forceinline__ int read_field(const uint8_t* rec, int f, int bits) {
   const int o = f * bits, byte = o >> 3, sh = o & 7;
@@ -53,7 +54,6 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, 
   const int m0 = chunk_id * a.chunk;
   const int hq0 = h * NH;
   const int red_floats = (NH * (NW > 2 ? NW : 2) + 2 * NH + 4) & ~3;
-  const int uni_floats = max(NH * K.Nc * PP * 2, NH * V.Nc);
   const size_t pstride = (size_t)a.n_chunks * (D + 2);
   float* part = a.part + ((size_t)b * a.Hq + hq0) * pstride + (size_t)chunk_id * (D + 2);
   if (m0 >= L) {
@@ -89,6 +89,61 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, 
   const uint8_t* kbase = a.kcodes + ((size_t)b * K.Hkv + h) * (size_t)a.cache_len * K.bpt;
   const uint8_t* vbase = a.vcodes + ((size_t)b * V.Hkv + h) * (size_t)a.cache_len * V.bpt;
 
+  if constexpr (GS >= kWideGroup) {
+    // Wide groups (many pairs share an index): the key itself is rebuilt per
+    // 32-scalar slice of a group - every round's entries of the slice staged in
+    // LDS as fp16, summed in fp32 over the rounds - then rotated once per pair
+    // and dotted with the rotated queries. A query x codebook table per (group,
+    // round) would cost a phase and NH products per pair and round instead.
+    constexpr int SL = 32, SP = SL / 2;
+    _Float16* cbs = reinterpret_cast<_Float16*>(uni);  // [R][Nc][SL]
+    for (int j = 0; j < G; ++j) {
+      for (int sl = 0; sl < GS / SL; ++sl) {
+        __syncthreads();
+        const _Float16* src = a.kcb + ((size_t)h * G + j) * K.R * K.Nc * GS + sl * SL;  // entry (r, l) at (r Nc + l) GS
+        for (int i = tid; i < K.R * K.Nc * (SL / 8); i += kThreads) {
+          const int rl = i / (SL / 8), c8 = i % (SL / 8);
+          reinterpret_cast<uint4*>(cbs)[i] = *reinterpret_cast<const uint4*>(src + (size_t)rl * GS + c8 * 8);
+        }
+        __syncthreads();
+#pragma unroll 1
+        for (int t = 0; t < TPT; ++t) {
+          const int m = m0 + tid + kThreads * t;
+          if (m < L) {
+            float kx[SL];
+#pragma unroll
+            for (int i = 0; i < SL; ++i) kx[i] = 0.f;
+            for (int r = 0; r < K.R; ++r) {
+              const int code = read_field(kbase + (size_t)m * K.bpt, r * G + j, K.bits);
+              const uint4* e = reinterpret_cast<const uint4*>(cbs + ((size_t)r * K.Nc + code) * SL);
+#pragma unroll
+              for (int v = 0; v < SL / 8; ++v) {
+                const uint4 w = e[v];
+                const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                  const half2_t xy = __builtin_bit_cast(half2_t, wd[u]);
+                  kx[8 * v + 2 * u] += (float)xy.x;
+                  kx[8 * v + 2 * u + 1] += (float)xy.y;
+                }
+              }
+            }
+#pragma unroll
+            for (int pp = 0; pp < SP; ++pp) {
+              const int p = j * PP + sl * SP + pp;
+              const float2 w = phase_exact((uint32_t)m, ph.lo[p], ph.hi[p]);
+              const float rx = kx[2 * pp] * w.x - kx[2 * pp + 1] * w.y, ry = kx[2 * pp] * w.y + kx[2 * pp + 1] * w.x;
+#pragma unroll
+              for (int hh = 0; hh < NH; ++hh) {
+                const float2 qv = qz[hh * P + p];
+                s[t][hh] += qv.x * rx + qv.y * ry;  // Re(conj(q~) (R_m k))
+              }
+            }
+          }
+        }
+      }
+    }
+  } else {
   for (int j = 0; j < G; ++j) {
     for (int r = 0; r < K.R; ++r) {
       __syncthreads();
@@ -119,6 +174,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, 
         }
       }
     }
+  }
   }
 
   // softmax over the chunk
@@ -237,7 +293,8 @@ size_t decode_generic_smem(const CbShape& k, const CbShape& v, int NH) {
   // rotated queries (float2 per pair), output accumulators, reductions, then
   // the query x codebook table of one (group, round) or a value histogram
   const int P = k.D / 2, NW = kThreads / 64;
-  const size_t table_bytes = (size_t)NH * k.Nc * (k.g / 2) * sizeof(float2);
+  const size_t table_bytes = k.g >= kWideGroup ? (size_t)k.R * k.Nc * 32 * sizeof(_Float16)  // one slice, all rounds
+                                               : (size_t)NH * k.Nc * (k.g / 2) * sizeof(float2);
   const size_t hist_bytes = (size_t)NH * v.Nc * sizeof(uint32_t);
   return (2 * NH * P + NH * k.D + ((NH * (NW > 2 ? NW : 2) + 2 * NH + 4) & ~3)) * sizeof(float) +
          (table_bytes > hist_bytes ? table_bytes : hist_bytes);

@@ -261,9 +261,9 @@ def test_wide_groups_and_many_rounds():
         return L.commvq_encode(ctypes.byref(c), FAKE, 4, c.n_kv_heads * c.head_dim, FAKE, 4096, 512, None)
     assert enc(cb(D=96, g=24, Nc=16, R=1)) == E.COMMVQ_ERR_UNSUPPORTED          # no kernel for g = 24
     assert enc(cb(D=256, g=2, Nc=256, R=32)) == E.COMMVQ_ERR_UNSUPPORTED        # 4096 fields per record
-    k = cb(D=128, g=128, Nc=256, R=1)
-    assert _raw_decode(k, k, rope, Hq=64) == E.COMMVQ_ERR_UNSUPPORTED           # 8 heads x 256 x 64 pairs of table
-    assert "table" in _lib.commvq_last_error()
+    k = cb(D=128, g=64, Nc=256, R=16)
+    assert _raw_decode(k, k, rope) == E.COMMVQ_ERR_UNSUPPORTED                  # 16 rounds x 256 entries of a slice
+    assert "LDS" in _lib.commvq_last_error()
     assert _raw_decode(cb(D=96, g=24), cb(D=96, g=24), rope) == E.COMMVQ_ERR_UNSUPPORTED
     w = cb(D=128, g=32, Nc=64, R=2)
     assert L.commvq_dequantize_kv(ctypes.byref(w), ctypes.byref(w), ctypes.byref(rope), FAKE, FAKE, FAKE, 1, 64, 64,
