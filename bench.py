@@ -405,9 +405,9 @@ def bench_naive(args):
 
 def bench_em(args):
     """One EM iteration of codebook fitting on the prefill workload's key tensor
-    (131072 tokens x 8 KV heads, heavy-tailed channels, g = 8, Nc' = 256): round
-    0 at temperature 0 (nearest entry) and 1, and round 1 of a two-round
-    codebook at temperature 0 (which first reduces every vector by its round-0
+    (131072 tokens x 8 KV heads, heavy-tailed channels, g = 8, Nc' = 256, a
+    two-round codebook): round 0 at temperature 0 (nearest entry) and 1, and
+    round 1 at temperature 0 (which first reduces every vector by its round-0
     choice). Each is timed over the steps with HIP events on the launch stream."""
     import torch
 
@@ -439,10 +439,12 @@ def bench_em(args):
         stop.record(stream)
         torch.cuda.synchronize()
         ms = start.elapsed_time(stop) / args.steps
-        # vector-ALU work: per (vector, group, entry) of each round searched, g subtractions and g FMAs for the
-        # distance and one compare-select in the row minimum; the fitted round at temperature > 0 adds two
-        # exponentials and g + 1 FMAs of the weighted sums
-        per_entry = (r + 1) * (2 * g + 1) + (2 + g + 1 if T > 0 else 0)
+        # vector-ALU work per (vector, group, entry): at temperature 0 the step runs the matrix-core encoder
+        # (distances on MFMA; a compare and two selects per candidate, every round of the codebook searched) and
+        # adds each vector to its entry's sums; at temperature > 0 the fitting kernel spends g subtractions, g FMAs
+        # and a compare-select per candidate of each round searched, and two exponentials and g + 1 FMAs per entry
+        # of the fitted round
+        per_entry = 3 * q.n_rounds if T == 0 else (r + 1) * (2 * g + 1) + (2 + g + 1)
         ops = N * H * G * Nc * per_entry
         out[label] = {"ms": ms, "vectors_per_s": N * H * G / (ms * 1e-3),
                       "achieved_T_lane_ops": ops / (ms * 1e-3) / 1e12,
@@ -462,7 +464,8 @@ def bench_em(args):
                    "group_size": g, "n_entries": Nc, "step": "commvq_em_step, round 0, temperature 0"},
         "roofline": {"bound": "alu", "achieved": main_rec["achieved_T_lane_ops"], "peak": VALU_PEAK_LANE_OPS / 1e12,
                      "unit": "T lane-ops/s", "frac": main_rec["frac_valu"],
-                     "work": "(2 g + 1) vector ops per (vector, group, entry, round searched)"},
+                     "work": "3 vector ops (compare, two selects) per (vector, group, entry, codebook round) of the "
+                             "matrix-core encoder that makes the nearest-entry choices"},
         "variants": out,
         "cpu_baseline": cpu,
     }

@@ -256,8 +256,11 @@ int32_t commvq_dense_decode_attention(const commvq_rope* rope, const float* q, c
  * caller anneals by lowering the temperature over iterations and fits the
  * rounds in order. */
 
-/* Bytes of the fp32 work buffer commvq_em_step needs for this codebook:
- * Hkv * (D/g) * Nc' * (g + 1) * 4; negative commvq_status if invalid. */
+/* Bytes of the work buffer commvq_em_step needs for this codebook: the fp32
+ * accumulators, Hkv * (D/g) * Nc' * (g + 1) * 4 rounded up to 256, plus, for
+ * the shapes whose nearest-entry step reuses the matrix-core encoder (g = 8,
+ * Nc' = 256, R <= 2, Hkv * R * 16 <= 16 KiB), a 4 MiB scratch for a batch of
+ * codes; negative commvq_status if invalid. */
 int64_t commvq_em_work_bytes(const commvq_codebook* cb);
 
 /* One EM iteration fitting round `round` of `cb` to n_tokens vectors of every
@@ -269,8 +272,12 @@ int64_t commvq_em_work_bytes(const commvq_codebook* cb);
  *     temperature 0, 1 on the nearest entry (lowest index on ties) and 0 else.
  *   M-step: c_l = sum w_l e / sum w_l over the vectors (fp32 sums, written as
  *     fp16); an entry whose mass sum w_l is not above min_mass keeps its value.
- *   x            device fp16, token t head h scalar d at
- *                x[t * x_token_stride + h * D + d] (stride in elements >= Hkv*D)
+ *   At temperature 0 the E-step's choices for g = 8, Nc' = 256, R <= 2 are
+ *   those of commvq_encode's matrix-core search (which may differ from the
+ *   fp32 distance form only at near ties).
+ *   x            device fp16, 4-byte aligned, token t head h scalar d at
+ *                x[t * x_token_stride + h * D + d] (stride in elements, even,
+ *                >= Hkv*D)
  *   new_entries  device fp16 with cb->entries' layout, 16-byte aligned: the
  *                round's entries are written, nothing else (it may be
  *                cb->entries itself: the update runs after every read)

@@ -570,7 +570,8 @@ int32_t commvq_em_step(const commvq_codebook* cb, const void* x, int64_t n_token
   st = check_entries(cb, "codebook");
   if (st) return st;
   if (!x || !new_entries) return fail(COMMVQ_ERR_INVALID_ARG, "null x or new_entries pointer");
-  if (reinterpret_cast<uintptr_t>(x) & 1) return fail(COMMVQ_ERR_INVALID_ARG, "x must be 2-byte aligned");
+  if (reinterpret_cast<uintptr_t>(x) & 3) return fail(COMMVQ_ERR_INVALID_ARG, "x must be 4-byte aligned");
+  if (x_token_stride & 1) return fail(COMMVQ_ERR_INVALID_ARG, "x_token_stride must be even");
   if (reinterpret_cast<uintptr_t>(new_entries) & 15)
     return fail(COMMVQ_ERR_INVALID_ARG, "new_entries must be 16-byte aligned");
   if (mass_out && (reinterpret_cast<uintptr_t>(mass_out) & 3))

@@ -135,6 +135,8 @@ size_t decode_newtok_offset(const CbShape& k, int B, int Hq, int max_len, int ch
 hipError_t launch_decode_fast(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream);
 
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t stream);
+// Whether launch_encode searches this shape on the matrix cores (more than 64 tokens).
+bool encode_uses_matrix_cores(const CbShape& s);
 hipError_t launch_decode_generic(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_dequant_kv(const DequantArgs& a, const PhaseTable& ph, hipStream_t stream);
@@ -142,6 +144,8 @@ size_t dense_workspace_bytes(int B, int Hq, int max_len);
 // dense_decode_kernel, then the chunk merge into a.out
 hipError_t launch_dense_decode(const DenseArgs& a, const PhaseTable& ph, hipStream_t stream);
 size_t em_work_bytes(const CbShape& s);
+size_t em_accum_bytes(const CbShape& s);  // the fp32 accumulators, 256-byte padded
+int64_t em_code_batch(const CbShape& s);  // vectors per encoder batch of the nearest-entry path (0: not used)
 size_t em_accumulate_smem(const CbShape& s, int round, bool soft);
 hipError_t launch_em_step(const EmArgs& a, hipStream_t stream);
 

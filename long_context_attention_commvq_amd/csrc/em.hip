@@ -12,8 +12,10 @@
 //          (T > 0), or 1 for the nearest entry and 0 elsewhere (T = 0);
 //  M-step: c_l = sum_n w_nl e_n / sum_n w_nl (kept where that mass is not
 //          above min_mass).
-// Three launches: a fill of the fp32 accumulators, em_accumulate_kernel, and
-// em_update_kernel.
+// Launches: a fill of the fp32 accumulators; em_accumulate_kernel, or at
+// temperature 0 for the shapes the encoder searches on the matrix cores the
+// encoder (codes of a batch into the work buffer) and em_scatter_kernel per
+// batch; then em_update_kernel.
 //
 // em_accumulate_kernel<g>: a workgroup per (256 vectors, KV head) walks the
 // groups; per group it stages rounds 0..r of the codebook (fp32) and the 256
@@ -32,6 +34,7 @@ namespace commvq {
 namespace {
 
 constexpr int kEmThreads = 256, kEmTokens = 256, kEmSub = 16;
+constexpr size_t kEmCodeScratch = size_t(4) << 20;  // codes of one encoder batch (nearest-entry path)
 
 __device__ __forceinline__ float em_wave_sum(float v) {
 #pragma unroll
@@ -165,6 +168,47 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
   }
 }
 
+// Nearest-entry path (temperature 0, shapes the encoder searches on the matrix
+// cores): the encoder writes a batch's codes, then this kernel adds every
+// vector's round-r residual (x minus the chosen entries of rounds < r, in
+// fp32 as the encoder subtracts them) with a count of 1 to its chosen entry's
+// sums. A workgroup per (kScatterTokens vectors of the batch, KV head, group)
+// sums in LDS (fp32 atomics) before one flush to the accumulators.
+constexpr int kScatterTokens = 2048;
+
+template <int GS>
+__global__ __launch_bounds__(256) void em_scatter_kernel(EmArgs a, const uint8_t* codes, int64_t t_begin, int n_batch) {
+  __shared__ float sums[256 * (GS + 1)];  // Nc' = 256
+  const CbShape s = a.s;
+  const int Nc = s.Nc, G = s.G, r = a.round;
+  const int h = blockIdx.y, j = blockIdx.z, tid = threadIdx.x;
+  const int n0 = blockIdx.x * kScatterTokens, n1 = min(n0 + kScatterTokens, n_batch);
+  {
+    for (int i = tid; i < Nc * (GS + 1); i += 256) sums[i] = 0.f;
+    __syncthreads();
+    for (int n = n0 + tid; n < n1; n += 256) {
+      const uint8_t* rec = codes + ((size_t)n * s.Hkv + h) * s.bpt;  // 8-bit fields, round-major
+      const _Float16* xp = a.x + (t_begin + n) * a.x_token_stride + (int64_t)h * s.D + j * GS;
+      float e[GS];
+#pragma unroll
+      for (int k = 0; k < GS; ++k) e[k] = (float)xp[k];
+      for (int rr = 0; rr < r; ++rr) {
+        const _Float16* ce = a.cb + ((((size_t)h * G + j) * s.R + rr) * Nc + rec[rr * G + j]) * GS;
+#pragma unroll
+        for (int k = 0; k < GS; ++k) e[k] -= (float)ce[k];
+      }
+      float* dst = sums + rec[r * G + j] * (GS + 1);
+#pragma unroll
+      for (int k = 0; k < GS; ++k) atomicAdd(dst + k, e[k]);
+      atomicAdd(dst + GS, 1.f);
+    }
+    __syncthreads();
+    float* wk = a.work + ((size_t)h * G + j) * Nc * (GS + 1);
+    for (int i = tid; i < Nc * (GS + 1); i += 256)
+      if (sums[i] != 0.f) atomicAdd(wk + i, sums[i]);
+  }
+}
+
 // One thread per (KV head, group, entry) of the fitted round.
 template <int GS>
 __global__ __launch_bounds__(256) void em_update_kernel(EmArgs a) {
@@ -194,6 +238,35 @@ hipError_t launch_em_g(const EmArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(em_fill_kernel, dim3((unsigned)fill_blocks), dim3(256), 0, stream, a.work, work_n);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const int64_t batch = em_code_batch(s);
+  if (a.temperature == 0.f && batch > 0) {
+    if constexpr (GS == 8) {
+      uint8_t* codes = reinterpret_cast<uint8_t*>(a.work) + em_accum_bytes(s);
+      for (int64_t t0 = 0; t0 < a.n_tokens; t0 += batch) {
+        const int nb = (int)(a.n_tokens - t0 < batch ? a.n_tokens - t0 : batch);
+        EncodeArgs ea{};
+        ea.x = a.x + t0 * a.x_token_stride;
+        ea.cb = a.cb;
+        ea.codes = codes;
+        ea.n_tokens = nb;
+        ea.x_token_stride = a.x_token_stride;
+        ea.code_token_stride = (int64_t)s.Hkv * s.bpt;
+        ea.code_head_stride = s.bpt;
+        ea.positions = nullptr;
+        ea.cache_len = 0;
+        ea.s = s;
+        e = launch_encode(ea, stream);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(em_scatter_kernel<8>, dim3((nb + kScatterTokens - 1) / kScatterTokens, s.Hkv, s.G),
+                           dim3(256), 0, stream, a, codes, t0, nb);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      const int64_t entries = (int64_t)s.Hkv * s.G * s.Nc;
+      hipLaunchKernelGGL((em_update_kernel<8>), dim3((unsigned)((entries + 255) / 256)), dim3(256), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   const size_t smem = em_accumulate_smem(s, a.round, a.temperature > 0.f);
   if (smem > 160 * 1024) return hipErrorInvalidValue;
   static std::atomic<uint64_t> configured{0};
@@ -218,7 +291,19 @@ size_t em_accumulate_smem(const CbShape& s, int round, bool soft) {
           (soft ? 0 : (size_t)s.Nc * (s.g + 1))) * sizeof(float);
 }
 
-size_t em_work_bytes(const CbShape& s) { return (size_t)s.Hkv * s.G * s.Nc * (s.g + 1) * sizeof(float); }
+size_t em_accum_bytes(const CbShape& s) {
+  return ((size_t)s.Hkv * s.G * s.Nc * (s.g + 1) * sizeof(float) + 255) / 256 * 256;
+}
+
+int64_t em_code_batch(const CbShape& s) {
+  // the nearest-entry path: shapes the encoder searches on the matrix cores,
+  // codes of a batch of vectors in a 4 MiB scratch (at least 256 vectors)
+  if (!encode_uses_matrix_cores(s) || s.Hkv > 65535) return 0;
+  const int64_t batch = (int64_t)kEmCodeScratch / ((int64_t)s.Hkv * s.bpt);
+  return batch >= 256 ? batch : 0;
+}
+
+size_t em_work_bytes(const CbShape& s) { return em_accum_bytes(s) + (em_code_batch(s) > 0 ? kEmCodeScratch : 0); }
 
 hipError_t launch_em_step(const EmArgs& a, hipStream_t stream) {
   switch (a.s.g) {

@@ -270,11 +270,6 @@ __global__ __launch_bounds__(MF_THREADS, 2) void encode_mfma_kernel(EncodeArgs a
   }
 }
 
-// The MFMA search covers g = 8, Nc' = 256 (8-bit fields) and R <= 2 when the
-// tile's codes fit the workgroup's LDS.
-bool mfma_encoder_applies(const CbShape& s) {
-  return s.g == 8 && s.Nc == 256 && s.R <= 2 && (size_t)MF_TOKENS * s.R * s.G <= 64 * 1024;
-}
 
 template <int GS>
 hipError_t launch_encode_g(const EncodeArgs& a, hipStream_t stream) {
@@ -283,7 +278,7 @@ hipError_t launch_encode_g(const EncodeArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   if constexpr (GS == 8) {
-    if (mfma_encoder_applies(a.s)) {
+    if (encode_uses_matrix_cores(a.s)) {
       const int64_t nblk = (a.n_tokens + MF_TOKENS - 1) / MF_TOKENS;
       if (nblk > 0x7fffffff) return hipErrorInvalidValue;
       const size_t smem = (size_t)MF_TOKENS * a.s.R * a.s.G;
@@ -310,6 +305,12 @@ hipError_t launch_encode_g(const EncodeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// The MFMA search covers g = 8, Nc' = 256 (8-bit fields) and R <= 2 when the
+// tile's codes fit the workgroup's LDS.
+bool encode_uses_matrix_cores(const CbShape& s) {
+  return s.g == 8 && s.Nc == 256 && s.R <= 2 && (size_t)MF_TOKENS * s.R * s.G <= 64 * 1024;
+}
 
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t stream) {
   switch (a.s.g) {

@@ -220,7 +220,8 @@ def test_dense_attention_validation_without_launch():
 def test_em_validation_without_launch():
     c = cb(D=128, g=8, Nc=256, R=2, H=8)
     E = _lib
-    assert E.commvq_em_work_bytes(c) == 8 * 16 * 256 * 9 * 4
+    assert E.commvq_em_work_bytes(c) == 8 * 16 * 256 * 9 * 4 + (4 << 20)  # accumulators + a batch of codes
+    assert E.commvq_em_work_bytes(cb(D=64, g=4, Nc=16, R=3, H=2)) == (2 * 16 * 16 * 5 * 4 + 255) // 256 * 256
     assert E.commvq_em_work_bytes(cb(D=127)) == E.COMMVQ_ERR_INVALID_ARG
     L = _lib.lib()
 
@@ -234,7 +235,8 @@ def test_em_validation_without_launch():
     assert em(mm=float("nan")) == E.COMMVQ_ERR_INVALID_ARG
     assert em(stride=1023) == E.COMMVQ_ERR_INVALID_ARG
     assert em(x=None) == E.COMMVQ_ERR_INVALID_ARG
-    assert em(x=FAKE + 1) == E.COMMVQ_ERR_INVALID_ARG
+    assert em(x=FAKE + 2) == E.COMMVQ_ERR_INVALID_ARG
+    assert em(stride=1025) == E.COMMVQ_ERR_INVALID_ARG
     assert em(new=FAKE + 8) == E.COMMVQ_ERR_INVALID_ARG
     assert em(mass=FAKE + 2) == E.COMMVQ_ERR_INVALID_ARG
     assert em(wb=16) == E.COMMVQ_ERR_WORKSPACE
