@@ -71,6 +71,9 @@ def parse():
                     help="decode workload to time (default: the 128K 1-bit decode-step workload)")
     ap.add_argument("--encode", action="store_true",
                     help="time the prefill encoder instead (131072 tokens x 8 KV heads of K and V, 2-bit)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the timed steps in one HIP graph and time its replay (the default issues each "
+                         "commvq_decode_step call from the host)")
     ap.add_argument("--naive", action="store_true",
                     help="time the comparison path (dequantise the codes to fp16, then dense attention) against "
                          "commvq_decode_attention on the same 128K 1-bit caches, instead of the headline step")
@@ -578,22 +581,36 @@ def main():
         calls.append((knew[i].data_ptr(), vnew[i].data_ptr(), positions[t].data_ptr(), qs[i].data_ptr(),
                       positions[t].data_ptr(), kcaches[li].data_ptr(), vcaches[li].data_ptr(), lens[t].data_ptr()))
 
-    def run_step(i):
+    def run_step(i, stream_id=sid):
         kn, vn, pos, q, qp, kc, vc, ln = calls[i]
         _lib.commvq_decode_step(kq.desc, vq.desc, rope, kn, vn, pos, q, qp, kc, vc, ln, B, Hq, Lmax, Lmax, sm_scale,
-                                out, ws.buf, ws.nbytes, 0, sid)
+                                out, ws.buf, ws.nbytes, 0, stream_id)
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         run_step(i)
     torch.cuda.synchronize()
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    graph = None
+    if args.graph:
+        # the timed steps recorded once, replayed as one graph launch
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream().cuda_stream
+            for k in range(args.steps):
+                run_step(args.warmup + k, cap)
+        torch.cuda.synchronize()
+        graph.replay()  # one untimed replay
+        torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps" + (" (one graph replay)" if graph else ""), file=sys.stderr, flush=True)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
-    for k in range(args.steps):
-        run_step(args.warmup + k)
+    if graph is not None:
+        graph.replay()
+    else:
+        for k in range(args.steps):
+            run_step(args.warmup + k)
     stop.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall

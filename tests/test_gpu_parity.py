@@ -412,3 +412,42 @@ def test_decode_step_search_spread_over_few_chunks(Lmax):
     err = row_errors(out.cpu().numpy().reshape(-1, D), ref.reshape(-1, D))
     print(f"[decode step spread] Lmax={Lmax} max row rel err {err.max():.3e}", flush=True)
     assert err.max() <= ATTN_TOL
+
+
+def test_decode_calls_replay_in_a_hip_graph():
+    """Decode calls recorded into one HIP graph (torch.cuda.CUDAGraph) give the
+    eager result on every replay, with eager work and synchronisations between
+    the replays: the library records no memset and needs no initialised
+    workspace."""
+    B, Hq, Hkv, D, g, Nc, R, Lmax = 1, 8, 2, 128, 8, 256, 1, 6000
+    G = D // g
+    rng = np.random.default_rng(880)
+    kcb = synth.codebook(881, Hkv, D, g, Nc, R)
+    vcb = synth.codebook(882, Hkv, D, g, Nc, R)
+    kp = _pack_cache(rng.integers(0, Nc, size=(B, Lmax, Hkv, R, G)), Nc)
+    vp = _pack_cache(rng.integers(0, Nc, size=(B, Lmax, Hkv, R, G)), Nc)
+    kq, vq = api.Quantizer(dev(kcb), g), api.Quantizer(dev(vcb), g)
+    kd, vd = dev(kp), dev(vp)
+    qs = [dev(synth.queries(883 + i, B, Hq, D)) for i in range(3)]
+    lens = dev(np.array([Lmax - 7], dtype=np.int32))
+    qpos = lens - 1
+    ws = api.DecodeWorkspace(kq, vq, B, Hq, Lmax, DEV)
+    outs = [torch.empty((B, Hq, D), dtype=torch.float32, device=DEV) for _ in range(3)]
+    for i in range(3):  # eager, which also configures the kernels before capture
+        api.decode_attention(kq, vq, qs[i], qpos, kd, vd, lens, Lmax, 500000.0, out=outs[i], workspace=ws)
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(3):
+            api.decode_attention(kq, vq, qs[i], qpos, kd, vd, lens, Lmax, 500000.0, out=outs[i], workspace=ws)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        other = api.decode_attention(kq, vq, qs[rep], qpos, kd, vd, lens, Lmax, 500000.0)  # eager work in between
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i in range(3):
+            assert torch.equal(outs[i], eager[i]), (rep, i)
+        assert torch.equal(other, eager[rep])
