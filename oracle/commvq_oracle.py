@@ -421,3 +421,69 @@ def reconstruction_error(x: np.ndarray, codebook: np.ndarray) -> float:
     codes, _ = encode(x, cb)
     xh = dequantize(codes, cb)
     return float(np.mean((x - xh) ** 2))
+
+
+# ---------------------------------------------------------------------------
+# The paper's value coder (review, "Assumptions & free parameters": Nc value
+# codebook rows, 1024 for 1 bit and 2048 for 2 bits, average bit width Nc/d;
+# "Referee Report", minor comment 4: values use binary codes s in {0,1}^Nc,
+# keys the index-sharing code). Reading taken: a token's whole value vector
+# (all KV heads, d = Hkv * D scalars) is one Nc-bit code s, decoded as
+# s^T C = the sum of the codebook rows whose bits are set; bits are stored
+# LSB-first, Nc/8 bytes per token.
+# ---------------------------------------------------------------------------
+
+
+def unpack_bits(packed: np.ndarray, n_bits: int) -> np.ndarray:
+    """bytes [..., n_bits/8] -> {0, 1} [..., n_bits]; bit i is bit i % 8 of byte i // 8."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    out = np.zeros(packed.shape[:-1] + (n_bits,), dtype=np.int64)
+    for i in range(n_bits):
+        out[..., i] = (packed[..., i // 8] >> (i % 8)) & 1
+    return out
+
+
+def binary_values(packed: np.ndarray, rows: np.ndarray) -> np.ndarray:
+    """Decoded values s^T C: packed bits [..., Nc/8], rows C [Nc, d] -> [..., d] float64."""
+    C = np.asarray(rows, dtype=np.float64)
+    s = unpack_bits(packed, C.shape[0]).astype(np.float64)
+    return s @ C
+
+
+def decode_attention_bit_values(q, q_pos, kpacked, vbits, seq_lens, kcb, rows, theta_base, sm_scale=None):
+    """Dense oracle with keys from the residual commutative codebook (as
+    decode_attention_from_packed) and values from binary codes: vbits
+    [B, Lmax, Nc/8] uint8, rows [Nc, Hkv * D]. Query head hq reads KV head
+    hq // (Hq // Hkv) and its value slice [h D, (h + 1) D)."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv, G, R, Nc, g = kcb.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    thetas = rope_thetas(D, theta_base)
+    rep = Hq // Hkv
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L <= 0:
+            continue
+        pos = np.arange(L)
+        qr = apply_rope(q[b], np.full(Hq, int(q_pos[b])), thetas)
+        vv = binary_values(vbits[b, :L], rows)  # [L, Hkv * D]
+        for h in range(Hkv):
+            kc = unpack_codes(kpacked[b, h, :L], R, G, Nc)[:, None]
+            kr = apply_rope(dequantize(kc, kcb[h:h + 1])[:, 0], pos, thetas)
+            for a in range(rep):
+                hq = h * rep + a
+                out[b, hq] = attend_one(qr[hq], kr, vv[:, h * D:(h + 1) * D], sm_scale)
+    return out
+
+
+def bit_values_reordered(weights: np.ndarray, packed: np.ndarray, rows: np.ndarray) -> np.ndarray:
+    """The reordered value path (review, "If this is right", fourth bullet): the
+    weighted sum of the binary codes first, u = sum_m w_m s_m, then one product
+    u^T C. weights [L], packed [L, Nc/8], rows [Nc, d] -> [d]."""
+    C = np.asarray(rows, dtype=np.float64)
+    s = unpack_bits(packed, C.shape[0]).astype(np.float64)
+    u = np.asarray(weights, dtype=np.float64) @ s
+    return u @ C

@@ -160,3 +160,20 @@ def test_mutant_em_update_is_not_the_mean(monkeypatch):
         return 0.5 * (new + np.asarray(codebook, dtype=np.float64)[:, :, round_index]), mass  # half step
     monkeypatch.setattr(O, "em_step", bad)
     _expect_fail(P.test_em_hard_step_equals_brute_force_lloyd_step)
+
+
+def test_mutant_bits_msb_first(monkeypatch):
+    def bad(packed, n_bits):
+        packed = np.asarray(packed, dtype=np.uint8)
+        out = np.zeros(packed.shape[:-1] + (n_bits,), dtype=np.int64)
+        for i in range(n_bits):
+            out[..., i] = (packed[..., i // 8] >> (7 - i % 8)) & 1
+        return out
+    monkeypatch.setattr(O, "unpack_bits", bad)
+    _expect_fail(P.test_unpack_bits_hand_built_record)
+
+
+def test_mutant_bit_values_wrong_head_slice(monkeypatch):
+    real = O.binary_values
+    monkeypatch.setattr(O, "binary_values", lambda packed, rows: real(packed, rows)[..., ::-1])  # columns reversed
+    _expect_fail(P.test_bit_value_attention_matches_torch_sdpa)

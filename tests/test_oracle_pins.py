@@ -458,3 +458,57 @@ def test_em_later_round_fits_what_earlier_rounds_leave():
     assert used.any() and np.allclose(new[0, 0][used], 0.0, atol=1e-15)
     cb[0, 0, 1] = new[0, 0]
     assert O.reconstruction_error(x, cb) < 1e-30
+
+
+# ---------------------------------------------------------------- binary value codes
+
+def test_unpack_bits_hand_built_record():
+    # bytes 0b00000101, 0b10000000: bits 0 and 2 of byte 0, bit 7 of byte 1 -> indices 0, 2, 15
+    bits = O.unpack_bits(np.array([[0b00000101, 0b10000000]], dtype=np.uint8), 16)
+    assert list(np.flatnonzero(bits[0])) == [0, 2, 15]
+    rng = np.random.default_rng(20)
+    raw = rng.integers(0, 256, size=(5, 32), dtype=np.uint8)
+    assert np.array_equal(O.unpack_bits(raw, 256), np.unpackbits(raw, axis=-1, bitorder="little"))  # library routine
+
+
+def test_binary_values_special_cases():
+    rng = np.random.default_rng(21)
+    C = rng.standard_normal((64, 12))
+    one = np.zeros((1, 8), dtype=np.uint8)
+    one[0, 37 // 8] = 1 << (37 % 8)
+    assert np.array_equal(O.binary_values(one, C)[0], C[37])            # one bit: that row
+    ones = np.full((1, 8), 255, dtype=np.uint8)
+    assert np.allclose(O.binary_values(ones, C)[0], C.sum(axis=0), atol=1e-12)  # every bit: the column sums
+    assert np.array_equal(O.binary_values(np.zeros((1, 8), dtype=np.uint8), C)[0], np.zeros(12))
+
+
+def test_bit_values_reordered_equals_dense():
+    """(sum_m w_m s_m)^T C = sum_m w_m (s_m^T C): the reordering the decode
+    kernel relies on."""
+    rng = np.random.default_rng(22)
+    C = rng.standard_normal((256, 40))
+    packed = rng.integers(0, 256, size=(300, 32), dtype=np.uint8)
+    w = rng.random(300)
+    dense = w @ O.binary_values(packed, C)
+    assert np.allclose(O.bit_values_reordered(w, packed, C), dense, rtol=1e-12, atol=1e-10)
+
+
+def test_bit_value_attention_matches_torch_sdpa():
+    rng = np.random.default_rng(23)
+    B, Hq, Hkv, D, g, Nc, R, L, Nb = 1, 4, 2, 16, 4, 8, 2, 40, 64
+    kcb = rng.standard_normal((Hkv, D // g, R, Nc, g))
+    kc = rng.integers(0, Nc, size=(L, Hkv, R, D // g))
+    kp = O.pack_codes(kc, Nc).transpose(1, 0, 2)[None]
+    vb = rng.integers(0, 256, size=(B, L, Nb // 8), dtype=np.uint8)
+    C = rng.standard_normal((Nb, Hkv * D))
+    q = rng.standard_normal((B, Hq, D))
+    got = O.decode_attention_bit_values(q, [L - 1], kp, vb, [L], kcb, C, 10000.0)
+    th = O.rope_thetas(D, 10000.0)
+    kr = O.apply_rope(O.dequantize(kc, kcb).transpose(1, 0, 2), np.arange(L), th)  # [Hkv, L, D]
+    vv = (np.unpackbits(vb[0], axis=-1, bitorder="little").astype(np.float64) @ C).reshape(L, Hkv, D).transpose(1, 0, 2)
+    qr = O.apply_rope(q[0], np.full(Hq, L - 1), th)
+    rep = Hq // Hkv
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(qr).reshape(Hq, 1, 1, D), torch.from_numpy(np.repeat(kr, rep, axis=0))[:, None],
+        torch.from_numpy(np.repeat(vv, rep, axis=0))[:, None], scale=1 / math.sqrt(D)).reshape(Hq, D).numpy()
+    assert np.allclose(got[0], ref, atol=1e-10)
