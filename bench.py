@@ -77,6 +77,9 @@ def parse():
     ap.add_argument("--naive", action="store_true",
                     help="time the comparison path (dequantise the codes to fp16, then dense attention) against "
                          "commvq_decode_attention on the same 128K 1-bit caches, instead of the headline step")
+    ap.add_argument("--bitv", action="store_true",
+                    help="time decode attention with binary value codes (1024 bits per token) at 128K against the "
+                         "same generic kernel with residual-codebook values, and the fast path")
     ap.add_argument("--em", action="store_true",
                     help="time one EM iteration of codebook fitting (commvq_em_step) on the prefill workload's keys")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -406,6 +409,91 @@ def bench_naive(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_bitv(args):
+    """Decode attention at 128K (B 1, 32 query / 8 KV heads, 1-bit keys g 8,
+    Nc' 256, R 1) with the paper's binary value codes, 1024 bits per token over
+    the 1024 value scalars (1 bit per scalar): commvq_decode_attention_bitv,
+    beside commvq_decode_attention on the same keys with residual-codebook
+    values through the same generic kernel (COMMVQ_DECODE_EXACT) and through
+    the fast kernel. Caches of seeded random records rotated over layer slices
+    beyond the Infinity Cache; HIP events on the launch stream."""
+    import torch
+
+    from long_context_attention_commvq_amd import _lib, api, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[WORKLOAD]
+    B, Hq, H, D, Lmax = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.context
+    nb = 1024
+    kq = api.Quantizer(torch.from_numpy(synth.codebook(w.seed + 1, H, D, w.group_size, w.n_entries, w.n_rounds)).to(dev),
+                       w.group_size)
+    vq = api.Quantizer(torch.from_numpy(synth.codebook(w.seed + 2, H, D, w.group_size, w.n_entries, w.n_rounds)).to(dev),
+                       w.group_size)
+    rows = (torch.randn((nb, H * D), device=dev) / math.sqrt(nb / 2)).to(torch.float16)
+    vcb = _lib.make_bit_codebook(rows, nb, H * D)
+    bpt = kq.bytes_per_token
+    NL = max(1, min(args.layers, 8))
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 90)
+    slices = [(torch.randint(0, 256, (B, H, Lmax, bpt), dtype=torch.uint8, device=dev, generator=g),
+               torch.randint(0, 256, (B, H, Lmax, bpt), dtype=torch.uint8, device=dev, generator=g),
+               torch.randint(0, 256, (B, Lmax, nb // 8), dtype=torch.uint8, device=dev, generator=g)) for _ in range(NL)]
+    q = torch.from_numpy(synth.queries(w.seed + 91, B, Hq, D)).to(dev)
+    lens = torch.full((B,), Lmax, dtype=torch.int32, device=dev)
+    qpos = lens - 1
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ws = api.DecodeWorkspace(kq, vq, B, Hq, Lmax, dev)
+    rope = _lib.make_rope(w.theta_base)
+    stream = torch.cuda.current_stream()
+    sid = stream.cuda_stream
+    sm = 1.0 / math.sqrt(D)
+
+    def bitv(i):
+        kc, _, vb = slices[i % NL]
+        _lib.commvq_decode_attention_bitv(kq.desc, vcb, rope, q.data_ptr(), qpos.data_ptr(), kc.data_ptr(),
+                                          vb.data_ptr(), lens.data_ptr(), B, Hq, Lmax, Lmax, sm, out.data_ptr(),
+                                          ws.buf.data_ptr(), ws.nbytes, sid)
+
+    def residual(flags):
+        def call(i):
+            kc, vc, _ = slices[i % NL]
+            _lib.commvq_decode_attention(kq.desc, vq.desc, rope, q.data_ptr(), qpos.data_ptr(), kc.data_ptr(),
+                                         vc.data_ptr(), lens.data_ptr(), B, Hq, Lmax, Lmax, sm, out.data_ptr(),
+                                         ws.buf.data_ptr(), ws.nbytes, flags, sid)
+        return call
+
+    def timed(fn, label):
+        print(f"[bench] {label}", file=sys.stderr, flush=True)
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for i in range(args.steps):
+            fn(args.warmup + i)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / args.steps * 1e3
+
+    t_bitv = timed(bitv, "binary value codes (generic kernel)")
+    t_gen = timed(residual(_lib.COMMVQ_DECODE_EXACT), "residual value codebook (generic kernel)")
+    t_fast = timed(residual(0), "residual value codebook (fast kernel)")
+    toks = B * Lmax
+    rec = {
+        "metric": "decode-attn cached tokens/s with the paper's binary value codes (GQA 32q/8kv, 128K ctx, 1 bit per "
+                  "value scalar)",
+        "value": toks / (t_bitv * 1e-6), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": t_bitv * 1e-3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": "llama8b_ctx128k_1bit_binary_values", "batch": B, "n_q_heads": Hq, "n_kv_heads": H,
+                   "head_dim": D, "context": Lmax, "value_bits": nb, "layer_slices": NL},
+        "calls_us": {"commvq_decode_attention_bitv": t_bitv, "commvq_decode_attention_exact_generic": t_gen,
+                     "commvq_decode_attention_fast": t_fast},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def bench_em(args):
     """One EM iteration of codebook fitting on the prefill workload's key tensor
     (131072 tokens x 8 KV heads, heavy-tailed channels, g = 8, Nc' = 256, a
@@ -519,6 +607,9 @@ def main():
         return
     if args.em:
         bench_em(args)
+        return
+    if args.bitv:
+        bench_bitv(args)
         return
     if args.workload != WORKLOAD:
         bench_decode_workload(args)

@@ -194,6 +194,41 @@ int32_t commvq_decode_step(const commvq_codebook* kcb, const commvq_codebook* vc
                            int32_t max_seq_len, float sm_scale, float* out, void* workspace,
                            size_t workspace_bytes, uint32_t flags, void* stream);
 
+/* ---- binary value codes ------------------------------------------------------
+ * The paper codes a value vector with a binary code s in {0,1}^Nc and decodes
+ * it as s^T C ("Pith review of CommVQ", "Referee Report", minor comment 4;
+ * "Assumptions & free parameters": Nc = 1024 rows for 1 bit, 2048 for 2 bits,
+ * average bit width Nc/d). Here one code covers a token's whole value, all KV
+ * heads (d = Hkv * D); keys keep the commutative residual codebook. Its learned
+ * encoder is not part of this library; the decode side is. */
+typedef struct commvq_bit_codebook {
+  int32_t n_bits;      /* Nc: power of two, 32..2048 */
+  int32_t dim;         /* d = Hkv * D of the key codebook it is used with */
+  int32_t dtype;       /* COMMVQ_F16 */
+  int32_t reserved;    /* must be 0 */
+  const void* rows;    /* device fp16 [n_bits][dim], 16-byte aligned */
+} commvq_bit_codebook;
+
+/* Decode attention with binary value codes: as commvq_decode_attention for the
+ * keys (kcb, kcodes, rope, q, q_pos, seq_lens, sizes, sm_scale, out), with the
+ * value of position t of sequence b equal to the sum of the rows of vcb whose
+ * bits are set in vbits[b][t] (bit i = bit i % 8 of byte i / 8); query head hq
+ * reads columns [h D, h D + D) of that sum, h its KV head.
+ *   vbits     device bytes [batch][cache_len][n_bits / 8], 16-byte aligned
+ *   workspace >= commvq_decode_workspace_bytes(batch, n_q_heads, max_seq_len,
+ *             kcb, kcb) bytes, 256-byte aligned, no initialisation needed.
+ * Runs the generic kernel (fp32 table or rebuilt keys, exact phases); the
+ * weights meet the codes before the rows (u = sum_t p_t s_t, then u^T C).
+ * Shapes as commvq_decode_attention's generic path; vcb->dim must equal
+ * Hkv * D (else COMMVQ_ERR_INVALID_ARG). */
+int32_t commvq_decode_attention_bitv(const commvq_codebook* kcb, const commvq_bit_codebook* vcb,
+                                     const commvq_rope* rope, const float* q, const int32_t* q_pos,
+                                     const uint8_t* kcodes, const uint8_t* vbits,
+                                     const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
+                                     int32_t cache_len, int32_t max_seq_len, float sm_scale,
+                                     float* out, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
 /* ---- comparison path: the "naive" decode of the same codes ----------------
  * The review ("Pith review of CommVQ", "The pith") compares the method's decode
  * latency with a naive implementation of the same quantization. These two calls

@@ -35,7 +35,7 @@ EXPORTED = [
     "commvq_abi_version", "commvq_last_error", "commvq_validate_codebook", "commvq_bits_per_scalar",
     "commvq_code_bytes_per_token", "commvq_decode_workspace_bytes", "commvq_encode", "commvq_append",
     "commvq_decode_attention", "commvq_decode_step", "commvq_dequantize_kv", "commvq_dense_workspace_bytes",
-    "commvq_dense_decode_attention", "commvq_em_work_bytes", "commvq_em_step",
+    "commvq_dense_decode_attention", "commvq_em_work_bytes", "commvq_em_step", "commvq_decode_attention_bitv",
 ]
 
 
@@ -49,6 +49,11 @@ class commvq_codebook(ctypes.Structure):
     _fields_ = [("head_dim", c_int32), ("group_size", c_int32), ("n_entries", c_int32),
                 ("n_rounds", c_int32), ("n_kv_heads", c_int32), ("dtype", c_int32),
                 ("entries", c_void_p)]
+
+
+class commvq_bit_codebook(ctypes.Structure):
+    _fields_ = [("n_bits", c_int32), ("dim", c_int32), ("dtype", c_int32), ("reserved", c_int32),
+                ("rows", c_void_p)]
 
 
 class commvq_rope(ctypes.Structure):
@@ -99,6 +104,10 @@ def lib():
         L.commvq_dense_decode_attention.argtypes = [POINTER(commvq_rope), c_void_p, c_void_p, c_void_p, c_void_p,
                                                     c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                                     c_float, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.commvq_decode_attention_bitv.restype = c_int32
+        L.commvq_decode_attention_bitv.argtypes = [CB, POINTER(commvq_bit_codebook), POINTER(commvq_rope), c_void_p,
+                                                   c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                                   c_int32, c_float, c_void_p, c_void_p, c_size_t, c_void_p]
         L.commvq_em_work_bytes.restype = c_int64
         L.commvq_em_work_bytes.argtypes = [CB]
         L.commvq_em_step.restype = c_int32
@@ -137,6 +146,11 @@ def make_codebook(entries, head_dim: int, group_size: int, n_entries: int, n_rou
     """Descriptor for fp16 entries [Hkv][D/g][R][Nc'][g] (keep `entries` alive)."""
     return commvq_codebook(head_dim, group_size, n_entries, n_rounds, n_kv_heads, COMMVQ_F16,
                            _ptr(entries) if entries is not None else None)
+
+
+def make_bit_codebook(rows, n_bits: int, dim: int) -> commvq_bit_codebook:
+    """Descriptor for fp16 rows [n_bits][dim] (keep `rows` alive)."""
+    return commvq_bit_codebook(n_bits, dim, COMMVQ_F16, 0, _ptr(rows) if rows is not None else None)
 
 
 def make_rope(theta_base: float, pairing: int = 0) -> commvq_rope:
@@ -231,3 +245,12 @@ def commvq_em_step(cb: commvq_codebook, x, n_tokens: int, x_token_stride: int, r
     return _check(lib().commvq_em_step(
         ctypes.byref(cb), _ptr(x), n_tokens, x_token_stride, round_index, float(temperature), float(min_mass),
         _ptr(new_entries), _ptr(mass_out), _ptr(work), int(work_bytes), _stream(stream, x, new_entries)))
+
+
+def commvq_decode_attention_bitv(kcb: commvq_codebook, vcb: commvq_bit_codebook, rope: commvq_rope, q, q_pos, kcodes,
+                                 vbits, seq_lens, batch: int, n_q_heads: int, cache_len: int, max_seq_len: int,
+                                 sm_scale: float, out, workspace, workspace_bytes: int, stream=None) -> int:
+    return _check(lib().commvq_decode_attention_bitv(
+        ctypes.byref(kcb), ctypes.byref(vcb), ctypes.byref(rope), _ptr(q), _ptr(q_pos), _ptr(kcodes), _ptr(vbits),
+        _ptr(seq_lens), batch, n_q_heads, cache_len, max_seq_len, float(sm_scale), _ptr(out), _ptr(workspace),
+        int(workspace_bytes), _stream(stream, q, out)))

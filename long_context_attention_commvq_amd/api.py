@@ -187,3 +187,26 @@ def em_step(quant: Quantizer, x: torch.Tensor, round_index: int, temperature: fl
     _lib.commvq_em_step(quant.desc, x, N, H * D, round_index, temperature, min_mass, new_entries, mass, work,
                         work.numel())
     return (new_entries, mass) if with_mass else new_entries
+
+
+# ---- binary value codes ---------------------------------------------------------
+
+def decode_attention_bitv(kq: Quantizer, rows: torch.Tensor, q: torch.Tensor, q_pos: torch.Tensor,
+                          kcache: torch.Tensor, vbits: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                          theta_base: float, sm_scale: float | None = None, out: torch.Tensor | None = None,
+                          workspace: DecodeWorkspace | None = None) -> torch.Tensor:
+    """Keys from packed caches [B, Hkv, Lmax, bpt]; values from binary codes
+    vbits uint8 [B, Lmax, Nc/8] and rows fp16 [Nc, Hkv * D]."""
+    B, Hq, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = DecodeWorkspace(kq, kq, B, Hq, max_seq_len, q.device)
+    rows = rows.contiguous()
+    vcb = _lib.make_bit_codebook(rows, rows.shape[0], rows.shape[1])
+    rope = _lib.make_rope(theta_base)
+    _lib.commvq_decode_attention_bitv(kq.desc, vcb, rope, q, q_pos, kcache, vbits, seq_lens, B, Hq, kcache.shape[2],
+                                      max_seq_len, sm_scale, out, workspace.buf, workspace.nbytes)
+    return out

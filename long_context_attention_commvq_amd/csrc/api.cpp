@@ -597,3 +597,82 @@ int32_t commvq_em_step(const commvq_codebook* cb, const void* x, int64_t n_token
 }
 
 }  // extern "C"
+
+// ---- binary value codes --------------------------------------------------------
+
+extern "C" {
+
+int32_t commvq_decode_attention_bitv(const commvq_codebook* kcb, const commvq_bit_codebook* vcb,
+                                     const commvq_rope* rope, const float* q, const int32_t* q_pos,
+                                     const uint8_t* kcodes, const uint8_t* vbits, const int32_t* seq_lens,
+                                     int32_t batch, int32_t n_q_heads, int32_t cache_len, int32_t max_seq_len,
+                                     float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  g_err[0] = 0;
+  commvq::CbShape k, kk;
+  int32_t st = decode_shapes(kcb, kcb, batch, n_q_heads, max_seq_len, &k, &kk);
+  if (st) return st;
+  if (!vcb) return fail(COMMVQ_ERR_INVALID_ARG, "null binary value codebook");
+  const int nb = vcb->n_bits;
+  if (nb < 32 || nb > 2048 || (nb & (nb - 1)))
+    return fail(COMMVQ_ERR_INVALID_ARG, "n_bits %d must be a power of two in [32, 2048]", nb);
+  if ((int64_t)vcb->dim != (int64_t)k.Hkv * k.D)
+    return fail(COMMVQ_ERR_INVALID_ARG, "binary value codebook dim %d must equal n_kv_heads*head_dim %d", vcb->dim,
+                k.Hkv * k.D);
+  if (vcb->dtype != COMMVQ_F16 || vcb->reserved != 0)
+    return fail(COMMVQ_ERR_INVALID_ARG, "binary value codebook: dtype must be COMMVQ_F16, reserved 0");
+  if (!vcb->rows || (reinterpret_cast<uintptr_t>(vcb->rows) & 15))
+    return fail(COMMVQ_ERR_INVALID_ARG, "binary value codebook rows must be non-null and 16-byte aligned");
+  st = check_rope(rope);
+  if (st) return st;
+  if (cache_len < max_seq_len)
+    return fail(COMMVQ_ERR_INVALID_ARG, "max_seq_len %d exceeds cache_len %d", max_seq_len, cache_len);
+  if (!std::isfinite(sm_scale)) return fail(COMMVQ_ERR_INVALID_ARG, "sm_scale is not finite");
+  st = check_entries(kcb, "key codebook");
+  if (st) return st;
+  if (!q || !q_pos || !kcodes || !vbits || !seq_lens || !out)
+    return fail(COMMVQ_ERR_INVALID_ARG, "null q, q_pos, codes, bits, seq_lens or out pointer");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return fail(COMMVQ_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(kcodes) | reinterpret_cast<uintptr_t>(vbits)) & 15)
+    return fail(COMMVQ_ERR_INVALID_ARG, "kcodes and vbits must be 16-byte aligned");
+  const int NH = n_q_heads / k.Hkv;
+  if (commvq::decode_bitv_smem(k, nb, NH) > 160 * 1024)
+    return fail(COMMVQ_ERR_UNSUPPORTED, "binary value decode's LDS staging for %d query heads and %d bits exceeds 160 KiB",
+                NH, nb);
+  const int64_t need = commvq_decode_workspace_bytes(batch, n_q_heads, max_seq_len, kcb, kcb);
+  if (need < 0) return (int32_t)need;
+  if (!workspace || workspace_bytes < (size_t)need)
+    return fail(COMMVQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %lld required", workspace_bytes,
+                (long long)need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(COMMVQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  commvq::DecodeArgs a{};
+  a.q = q;
+  a.q_pos = q_pos;
+  a.kcodes = kcodes;
+  a.seq_lens = seq_lens;
+  a.kcb = static_cast<const _Float16*>(kcb->entries);
+  a.vbits = vbits;
+  a.vrows = static_cast<const _Float16*>(vcb->rows);
+  a.nbits = nb;
+  a.part = static_cast<float*>(workspace);
+  a.out = out;
+  a.B = batch;
+  a.Hq = n_q_heads;
+  a.NH = NH;
+  a.cache_len = cache_len;
+  a.max_len = max_seq_len;
+  a.chunk = 1024;  // the generic kernel's chunk
+  a.n_chunks = (max_seq_len + a.chunk - 1) / a.chunk;
+  a.sm_scale = sm_scale;
+  a.k = k;
+  a.v = k;
+  const PhaseConsts& pc = phase_consts(rope->theta_base, k.D);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = commvq::launch_decode_bitv(a, pc.ph, s);
+  if (e == hipSuccess) e = commvq::launch_decode_merge(a, s);
+  return hip_status(e, "commvq_decode_attention_bitv launch");
+}
+
+}  // extern "C"

@@ -60,6 +60,11 @@ struct DecodeArgs {
   float* newtok;
   int fold_new;
   float* out;          // [B][Hq][D]
+  // binary value codes (the generic kernel's bit-value variant): bits
+  // [B][cache_len][nbits / 8] LSB-first, rows C fp16 [nbits][Hkv * D]
+  const uint8_t* vbits;
+  const _Float16* vrows;
+  int nbits;
   int B, Hq, NH, cache_len, max_len, n_chunks, chunk;
   float sm_scale;
   CbShape k, v;
@@ -129,6 +134,10 @@ int decode_chunk_len(const CbShape& k, const CbShape& v, int B, int Hq, int max_
 bool decode_fast_path(const CbShape& k, const CbShape& v, int NH, int flags);
 // LDS bytes of the generic decode kernel for a shape (at most 160 KiB can run).
 size_t decode_generic_smem(const CbShape& k, const CbShape& v, int NH);
+// LDS bytes of the generic kernel's bit-value variant.
+size_t decode_bitv_smem(const CbShape& k, int nbits, int NH);
+// The generic kernel with binary value codes (a.vbits, a.vrows, a.nbits).
+hipError_t launch_decode_bitv(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream);
 size_t decode_workspace_bytes(const CbShape& k, int B, int Hq, int max_len, int chunk);
 // Byte offset of the new-token area in the workspace (after the partials, 256-aligned).
 size_t decode_newtok_offset(const CbShape& k, int B, int Hq, int max_len, int chunk);

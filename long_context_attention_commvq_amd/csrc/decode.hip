@@ -30,6 +30,7 @@ constexpr int kThreads = 256;
 constexpr int kGenericTPT = 4;  // tokens per lane in the generic kernel
 constexpr int kHistShift = 20;  // fixed-point weights: w * 2^20 (chunk <= 1024 keeps sums < 2^31)
 constexpr int kWideGroup = 32;  // group sizes from which keys are rebuilt per slice instead of tabled
+constexpr int kBitSub = 128;    // binary value codes: positions whose bit rows are staged in LDS at a time
 
 __device__ __forceinline__ int read_field(const uint8_t* rec, int f, int bits) {
   const int o = f * bits, byte = o >> 3, sh = o & 7;
@@ -38,7 +39,7 @@ __device__ __forceinline__ int read_field(const uint8_t* rec, int f, int bits) {
   return (int)((v >> sh) & ((1u << bits) - 1u));
 }
 
-template <int NH, int GS>
+template <int NH, int GS, bool BITV>
 __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, PhaseTable ph) {
   constexpr int PP = GS / 2;
   constexpr int TPT = kGenericTPT;
@@ -217,6 +218,65 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, 
     lsum[hh] = acc;
   }
 
+  if constexpr (BITV) {
+    // Binary value codes (a token's whole value, all KV heads, is the sum of
+    // the rows of C whose bits are set): u[hh][i] = sum_m p[hh][m] bit_i(m)
+    // over the chunk, then o[hh] = u[hh]^T C[:, h D .. h D + D) - the weights
+    // meet the codes before the codebook (review, "If this is right", fourth
+    // bullet). Thread (slot, c) takes byte c of the bit rows (bits 8c .. 8c+7)
+    // of every `slots`-th position; bit rows are staged in LDS kBitSub
+    // positions at a time.
+    const int NB = a.nbits, TB = NB / 8, slots = kThreads / TB;
+    float* pw = uni;                                        // [NH][chunk] weights
+    float* u = pw + NH * a.chunk;                           // [NH][NB]
+    uint32_t* rows_l = reinterpret_cast<uint32_t*>(u + NH * NB);  // [kBitSub][TB / 4]
+    __syncthreads();  // the score phase's table is no longer read
+#pragma unroll
+    for (int t = 0; t < TPT; ++t)
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) pw[hh * a.chunk + tid + kThreads * t] = s[t][hh];  // 0 past the length
+    for (int i = tid; i < NH * NB; i += kThreads) u[i] = 0.f;
+    const int c = tid % TB, slot = tid / TB;
+    float acc[8][NH];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) acc[k][hh] = 0.f;
+    const int n = min(L - m0, a.chunk);
+    const uint32_t* bits_g = reinterpret_cast<const uint32_t*>(a.vbits + ((size_t)b * a.cache_len + m0) * TB);
+    for (int s0 = 0; s0 < n; s0 += kBitSub) {
+      const int ns = min(kBitSub, n - s0);
+      __syncthreads();  // (the previous rows are read; the weights and u are written)
+      for (int i = tid; i < ns * (TB / 4); i += kThreads) rows_l[i] = bits_g[(size_t)s0 * (TB / 4) + i];
+      __syncthreads();
+      const uint8_t* rb = reinterpret_cast<const uint8_t*>(rows_l);
+      for (int tl = slot; tl < ns; tl += slots) {
+        const uint32_t byte = rb[tl * TB + c];
+        float w[NH];
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) w[hh] = pw[hh * a.chunk + s0 + tl];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float bit = (float)((byte >> k) & 1u);
+#pragma unroll
+          for (int hh = 0; hh < NH; ++hh) acc[k][hh] = fmaf(bit, w[hh], acc[k][hh]);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) atomicAdd(&u[hh * NB + 8 * c + k], acc[k][hh]);
+    __syncthreads();
+    const _Float16* cv = a.vrows + (size_t)h * D;  // row i, column h D + d at cv[i * Hkv * D + d]
+    const size_t ld = (size_t)K.Hkv * D;
+    for (int i = tid; i < NH * D; i += kThreads) {
+      const int hh = i / D, d = i % D;
+      float o = 0.f;
+      for (int r = 0; r < NB; ++r) o = fmaf(u[hh * NB + r], (float)cv[(size_t)r * ld + d], o);
+      oacc[hh * D + d] = o;
+    }
+  } else {
   // value histograms and contraction with the value codebook
   for (int j = 0; j < G; ++j) {
     for (int r = 0; r < V.R; ++r) {
@@ -246,6 +306,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, 
       }
     }
   }
+  }
   __syncthreads();
   if (tid == 0) {
 #pragma unroll
@@ -261,33 +322,55 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, 
   }
 }
 
-template <int NH, int GS>
+template <int NH, int GS, bool BITV>
 hipError_t launch_generic(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
-  const size_t smem = decode_generic_smem(a.k, a.v, NH);
+  const size_t smem = BITV ? decode_bitv_smem(a.k, a.nbits, NH) : decode_generic_smem(a.k, a.v, NH);
   if (smem > 160 * 1024) return hipErrorInvalidValue;
   static std::atomic<uint64_t> configured{0};
-  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&decode_generic_kernel<NH, GS>), configured);
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&decode_generic_kernel<NH, GS, BITV>), configured);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_generic_kernel<NH, GS>), dim3(a.n_chunks * a.k.Hkv, a.B), dim3(kThreads), smem, stream,
-                     a, ph);
+  hipLaunchKernelGGL((decode_generic_kernel<NH, GS, BITV>), dim3(a.n_chunks * a.k.Hkv, a.B), dim3(kThreads), smem,
+                     stream, a, ph);
   return hipGetLastError();
 }
 
-template <int NH>
+template <int NH, bool BITV>
 hipError_t launch_generic_nh(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
   switch (a.k.g) {
-    case 2: return launch_generic<NH, 2>(a, ph, stream);
-    case 4: return launch_generic<NH, 4>(a, ph, stream);
-    case 8: return launch_generic<NH, 8>(a, ph, stream);
-    case 16: return launch_generic<NH, 16>(a, ph, stream);
-    case 32: return launch_generic<NH, 32>(a, ph, stream);
-    case 64: return launch_generic<NH, 64>(a, ph, stream);
-    case 128: return launch_generic<NH, 128>(a, ph, stream);
+    case 2: return launch_generic<NH, 2, BITV>(a, ph, stream);
+    case 4: return launch_generic<NH, 4, BITV>(a, ph, stream);
+    case 8: return launch_generic<NH, 8, BITV>(a, ph, stream);
+    case 16: return launch_generic<NH, 16, BITV>(a, ph, stream);
+    case 32: return launch_generic<NH, 32, BITV>(a, ph, stream);
+    case 64: return launch_generic<NH, 64, BITV>(a, ph, stream);
+    case 128: return launch_generic<NH, 128, BITV>(a, ph, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool BITV>
+hipError_t launch_generic_all(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
+  switch (a.NH) {
+    case 1: return launch_generic_nh<1, BITV>(a, ph, stream);
+    case 2: return launch_generic_nh<2, BITV>(a, ph, stream);
+    case 4: return launch_generic_nh<4, BITV>(a, ph, stream);
+    case 8: return launch_generic_nh<8, BITV>(a, ph, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
+
+size_t decode_bitv_smem(const CbShape& k, int nbits, int NH) {
+  // the score phase's staging, or the weights [NH][chunk], u [NH][nbits] and
+  // kBitSub positions' bit rows
+  const size_t score = decode_generic_smem(k, k, NH);
+  const int P = k.D / 2, NW = kThreads / 64;
+  const size_t fixed = (2 * NH * P + NH * k.D + ((NH * (NW > 2 ? NW : 2) + 2 * NH + 4) & ~3)) * sizeof(float);
+  const size_t bitv = fixed + ((size_t)NH * kThreads * kGenericTPT + (size_t)NH * nbits) * sizeof(float) +
+                      (size_t)kBitSub * (nbits / 8);
+  return score > bitv ? score : bitv;
+}
 
 size_t decode_generic_smem(const CbShape& k, const CbShape& v, int NH) {
   // rotated queries (float2 per pair), output accumulators, reductions, then
@@ -328,13 +411,13 @@ size_t decode_workspace_bytes(const CbShape& k, int B, int Hq, int max_len, int 
 }
 
 hipError_t launch_decode_generic(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
-  switch (a.NH) {
-    case 1: return launch_generic_nh<1>(a, ph, stream);
-    case 2: return launch_generic_nh<2>(a, ph, stream);
-    case 4: return launch_generic_nh<4>(a, ph, stream);
-    case 8: return launch_generic_nh<8>(a, ph, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_generic_all<false>(a, ph, stream);
+}
+
+hipError_t launch_decode_bitv(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
+  if (a.nbits < 32 || a.nbits > 2048 || (a.nbits & (a.nbits - 1)) || a.chunk != kThreads * kGenericTPT)
+    return hipErrorInvalidValue;
+  return launch_generic_all<true>(a, ph, stream);
 }
 
 }  // namespace commvq

@@ -275,3 +275,23 @@ def test_wide_groups_and_many_rounds():
     big = cb(D=128, g=16, Nc=256, R=32)
     assert L.commvq_em_step(ctypes.byref(big), FAKE, 10, 1024, 31, 0.0, 0.0, FAKE, None, FAKE, 1 << 30,
                             None) == E.COMMVQ_ERR_UNSUPPORTED  # 32 rounds of fp32 codebook in LDS
+
+
+def test_bit_value_decode_validation_without_launch():
+    k, rope = cb(D=128, g=8, Nc=256, R=1, H=8), _lib.make_rope(500000.0)
+    L = _lib.lib()
+    E = _lib
+
+    def bitv(nb=1024, dim=1024, rows=FAKE, Hq=32, bits=FAKE, ws_bytes=1 << 30):
+        v = _lib.make_bit_codebook(rows, nb, dim)
+        return L.commvq_decode_attention_bitv(ctypes.byref(k), ctypes.byref(v), ctypes.byref(rope), FAKE, FAKE, FAKE,
+                                              bits, FAKE, 1, Hq, 1024, 1024, 0.088, FAKE, FAKE, ws_bytes, None)
+    assert bitv(nb=1000) == E.COMMVQ_ERR_INVALID_ARG
+    assert bitv(nb=4096) == E.COMMVQ_ERR_INVALID_ARG
+    assert bitv(dim=512) == E.COMMVQ_ERR_INVALID_ARG
+    assert bitv(rows=None) == E.COMMVQ_ERR_INVALID_ARG
+    assert bitv(rows=FAKE + 8) == E.COMMVQ_ERR_INVALID_ARG
+    assert bitv(bits=None) == E.COMMVQ_ERR_INVALID_ARG
+    assert bitv(bits=FAKE + 4) == E.COMMVQ_ERR_INVALID_ARG
+    assert bitv(Hq=24) == E.COMMVQ_ERR_UNSUPPORTED
+    assert bitv(ws_bytes=16) == E.COMMVQ_ERR_WORKSPACE

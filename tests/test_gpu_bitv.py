@@ -1,0 +1,110 @@
+"""GPU parity of decode attention with the paper's binary value codes
+(commvq_decode_attention_bitv, through the C ABI) against the oracle's
+decode_attention_bit_values on the same seeded inputs: keys from the residual
+commutative codebook, values as the sum of the rows whose bits are set, within
+2e-3 of each row's max |ref|."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_attention_commvq_amd import api, synth, _lib
+from oracle import commvq_oracle as O
+from tests.parity import ATTN_TOL, row_errors
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _pack_cache(codes, n_entries):
+    """codes [B, L, Hkv, R, G] -> packed [B, Hkv, L, bpt] via the oracle's packer."""
+    return np.ascontiguousarray(np.stack([O.pack_codes(codes[b], n_entries) for b in range(codes.shape[0])])
+                                .transpose(0, 2, 1, 3))
+
+
+def bit_rows(seed, n_bits, dim):
+    """Rows C [n_bits, dim] fp16, scaled so a sum of about n_bits / 2 rows is O(1)."""
+    r = np.random.default_rng(seed).standard_normal((n_bits, dim)) / math.sqrt(n_bits / 2)
+    return r.astype(np.float16)
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=1, Hq=32, Hkv=8, D=128, g=8, Nc=256, R=1, nbits=1024, lens=[3000], Lmax=3000),   # 1 bit per scalar
+    dict(B=1, Hq=32, Hkv=8, D=128, g=64, Nc=64, R=11, nbits=2048, lens=[1500], Lmax=1500),  # the paper's 2-bit pair
+    dict(B=2, Hq=4, Hkv=2, D=64, g=4, Nc=16, R=2, nbits=256, lens=[700, 1], Lmax=800),
+    dict(B=1, Hq=8, Hkv=1, D=128, g=8, Nc=256, R=2, nbits=512, lens=[2049], Lmax=2100),     # 8 query heads; chunk edge
+    dict(B=3, Hq=8, Hkv=4, D=32, g=2, Nc=4, R=3, nbits=32, lens=[1024, 0, 5], Lmax=1100),   # a zero length
+])
+def test_bit_value_decode_matches_oracle(case):
+    B, Hq, Hkv, D, g, Nc, R, nb, Lmax = (case[k] for k in ("B", "Hq", "Hkv", "D", "g", "Nc", "R", "nbits", "Lmax"))
+    lens = np.asarray(case["lens"], dtype=np.int32)
+    seed = 9000 + D + g + Nc + R + nb
+    rng = np.random.default_rng(seed)
+    kcb = synth.codebook(seed + 1, Hkv, D, g, Nc, R)
+    kp = _pack_cache(rng.integers(0, Nc, size=(B, Lmax, Hkv, R, D // g)), Nc)
+    vbits = rng.integers(0, 256, size=(B, Lmax, nb // 8), dtype=np.uint8)
+    rows = bit_rows(seed + 2, nb, Hkv * D)
+    q = synth.queries(seed + 3, B, Hq, D)
+    qpos = np.maximum(lens, 1) - 1
+    ref = O.decode_attention_bit_values(q, qpos, kp, vbits, lens, kcb, rows, 500000.0)
+    kq = api.Quantizer(dev(kcb), g)
+    out = api.decode_attention_bitv(kq, dev(rows), dev(q), dev(qpos), dev(kp), dev(vbits), dev(lens), Lmax, 500000.0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    err = row_errors(got.reshape(-1, D), ref.reshape(-1, D))
+    print(f"[bit values {case}] max row rel err {err.max():.3e}", flush=True)
+    for b in range(B):
+        if lens[b] == 0:
+            assert np.all(got[b] == 0.0)
+    assert err.max() <= ATTN_TOL
+
+
+def test_bit_value_decode_rejects_bad_arguments():
+    kcb = synth.codebook(9100, 2, 64, 8, 16, 1)
+    kq = api.Quantizer(dev(kcb), 8)
+    q = torch.zeros((1, 4, 64), dtype=torch.float32, device=DEV)
+    pos = torch.zeros(1, dtype=torch.int32, device=DEV)
+    codes = torch.zeros((1, 2, 16, kq.bytes_per_token), dtype=torch.uint8, device=DEV)
+    bits = torch.zeros((1, 16, 32), dtype=torch.uint8, device=DEV)
+    with pytest.raises(_lib.CommvqError) as e:
+        api.decode_attention_bitv(kq, torch.zeros((256, 100), dtype=torch.float16, device=DEV), q, pos, codes, bits,
+                                  pos + 1, 16, 500000.0)  # dim != Hkv * D
+    assert e.value.status == _lib.COMMVQ_ERR_INVALID_ARG
+    with pytest.raises(_lib.CommvqError) as e:
+        api.decode_attention_bitv(kq, torch.zeros((96, 128), dtype=torch.float16, device=DEV), q, pos, codes, bits,
+                                  pos + 1, 16, 500000.0)  # 96 bits: not a power of two
+    assert e.value.status == _lib.COMMVQ_ERR_INVALID_ARG
+
+
+def test_bit_value_decode_full_size_128k_sampled():
+    """128K positions, 32 query / 8 KV heads, 1024-bit value codes over the
+    1024 value scalars of a token (1 bit per scalar) and the 1-bit key
+    codebook, every head and chunk in one call; the oracle recomputes two KV
+    heads over all positions."""
+    B, Hq, Hkv, D, g, Nc, R, nb, L = 1, 32, 8, 128, 8, 256, 1, 1024, 131072
+    rep = Hq // Hkv
+    rng = np.random.default_rng(9200)
+    kcb = synth.codebook(9201, Hkv, D, g, Nc, R)
+    kp = rng.integers(0, 256, size=(B, Hkv, L, 16), dtype=np.uint8)  # every byte string is a valid 1-round record
+    vbits = rng.integers(0, 256, size=(B, L, nb // 8), dtype=np.uint8)
+    rows = bit_rows(9202, nb, Hkv * D)
+    q = synth.queries(9203, B, Hq, D)
+    lens = np.array([L], dtype=np.int32)
+    kq = api.Quantizer(dev(kcb), g)
+    print("[bit values full size] launching", flush=True)
+    out = api.decode_attention_bitv(kq, dev(rows), dev(q), dev(lens - 1), dev(kp), dev(vbits), dev(lens), L, 500000.0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    for h in (int(rng.integers(0, Hkv)), Hkv - 1):
+        ref = O.decode_attention_bit_values(q[:, h * rep:(h + 1) * rep], lens - 1, kp[:, h:h + 1], vbits, lens,
+                                            kcb[h:h + 1], rows[:, h * D:(h + 1) * D], 500000.0)[0]
+        err = row_errors(got[0, h * rep:(h + 1) * rep], ref)
+        print(f"[bit values full size] head {h} max row rel err {err.max():.3e}", flush=True)
+        assert err.max() <= ATTN_TOL
