@@ -298,11 +298,27 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, 
       }
       __syncthreads();
       const _Float16* cvp = a.vcb + ((((size_t)h * G + j) * V.R + r) * V.Nc) * GS;
-      for (int i = tid; i < NH * GS; i += kThreads) {
-        const int hh = i / GS, e = i % GS;
-        float acc = 0.f;
-        for (int l = 0; l < V.Nc; ++l) acc = fmaf((float)hist[hh * V.Nc + l], (float)cvp[l * GS + e], acc);
-        oacc[hh * D + j * GS + e] += acc * (1.0f / (float)(1 << kHistShift));
+      // NO outputs (head, scalar), each a sum over the Nc bins split over PARTS
+      // lanes of one wavefront and added with shuffles
+      constexpr int NO = NH * GS;
+      constexpr int PARTS = NO >= kThreads ? 1 : (kThreads / NO > 64 ? 64 : kThreads / NO);
+      if constexpr (PARTS == 1) {
+        for (int i = tid; i < NO; i += kThreads) {
+          const int hh = i / GS, e = i % GS;
+          float acc = 0.f;
+          for (int l = 0; l < V.Nc; ++l) acc = fmaf((float)hist[hh * V.Nc + l], (float)cvp[l * GS + e], acc);
+          oacc[hh * D + j * GS + e] += acc * (1.0f / (float)(1 << kHistShift));
+        }
+      } else {
+        const int o = tid / PARTS, part = tid % PARTS;
+        if (o < NO) {  // whole groups of PARTS lanes
+          const int hh = o / GS, e = o % GS;
+          float acc = 0.f;
+          for (int l = part; l < V.Nc; l += PARTS) acc = fmaf((float)hist[hh * V.Nc + l], (float)cvp[l * GS + e], acc);
+#pragma unroll
+          for (int off = PARTS / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+          if (part == 0) oacc[hh * D + j * GS + e] += acc * (1.0f / (float)(1 << kHistShift));
+        }
       }
     }
   }
