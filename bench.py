@@ -145,6 +145,77 @@ def cpu_baseline(budget_s: float):
                       f"mean unit time scaled x{w.n_kv_heads} to one 8-head step"}
 
 
+def decode_cpu_baseline(budget_s: float, w, lens, value_bits: int = 0):
+    """Time the fp64 oracle on (sequence, KV head) units of a decode workload w:
+    unit u is sequence u % B's query heads of one KV head over its L_b cached
+    positions (seeded random records), run for at least one unit and until the
+    budget is spent. One call covers every KV head, so the rate is the units'
+    positions over their time divided by Hkv. value_bits > 0 times the binary
+    value oracle instead (value codes of value_bits bits per token; one KV
+    head's D columns of the rows)."""
+    from threadpoolctl import threadpool_limits
+
+    from long_context_attention_commvq_amd import synth
+    from oracle import commvq_oracle as O
+
+    G = w.head_dim // w.group_size
+    kcb = synth.codebook(w.seed + 1, 1, w.head_dim, w.group_size, w.n_entries, w.n_rounds)
+    vcb = synth.codebook(w.seed + 2, 1, w.head_dim, w.group_size, w.n_entries, w.n_rounds)
+    rep = w.n_q_heads // w.n_kv_heads
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    units, t_total, toks = 0, 0.0, 0
+    with threadpool_limits(limits=cores):
+        while units < len(lens) * w.n_kv_heads and (units == 0 or t_total < budget_s):
+            L = int(lens[units % len(lens)])
+            kc = synth.random_codes(w.seed + 500 + units, (L, 1, w.n_rounds, G), w.n_entries)
+            kp = O.pack_codes(kc, w.n_entries).transpose(1, 0, 2)[None]
+            q = synth.queries(w.seed + 700 + units, 1, rep, w.head_dim)
+            if value_bits:
+                r = synth.rng(w.seed + 600 + units)
+                vb = r.integers(0, 256, size=(1, L, value_bits // 8)).astype(np.uint8)
+                rows = (r.standard_normal((value_bits, w.head_dim)) / math.sqrt(value_bits / 2)).astype(np.float16)
+                t0 = time.perf_counter()
+                O.decode_attention_bit_values(q, np.array([L - 1]), kp, vb, np.array([L]), kcb, rows, w.theta_base)
+            else:
+                vc = synth.random_codes(w.seed + 600 + units, (L, 1, w.n_rounds, G), w.n_entries)
+                vp = O.pack_codes(vc, w.n_entries).transpose(1, 0, 2)[None]
+                t0 = time.perf_counter()
+                O.decode_attention_from_packed(q, np.array([L - 1]), kp, vp, np.array([L]), kcb, vcb, w.theta_base)
+            t_total += time.perf_counter() - t0
+            units += 1
+            toks += L
+    kind = f"binary value codes ({value_bits} bits per token)" if value_bits else "residual value codebook"
+    return {"value": toks / t_total / w.n_kv_heads, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{units} (sequence, KV head) units of the {w.name} shape ({kind}), {toks} cached positions, "
+                      f"fp64 NumPy, BLAS threads={cores}; {t_total:.1f} s measured, scaled to all "
+                      f"{w.n_kv_heads} KV heads of one call"}
+
+
+def encode_cpu_baseline(budget_s: float, w):
+    """Time the fp64 oracle encoder (squared distances to every entry, argmin,
+    residual update, round by round) on slices of 1024 tokens x all KV heads of
+    the workload's heavy-tailed keys, until the budget is spent."""
+    from threadpoolctl import threadpool_limits
+
+    from long_context_attention_commvq_amd import synth
+    from oracle import commvq_oracle as O
+
+    cb = synth.codebook(w.seed + 1, w.n_kv_heads, w.head_dim, w.group_size, w.n_entries, w.n_rounds)
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    n, slices, t_total = 1024, 0, 0.0
+    with threadpool_limits(limits=cores):
+        while slices == 0 or t_total < budget_s:
+            x = synth.kv(w.seed + 800 + slices, n, w.n_kv_heads, w.head_dim, heavy_tail=True)
+            t0 = time.perf_counter()
+            O.encode(x, cb)
+            t_total += time.perf_counter() - t0
+            slices += 1
+    th = slices * n * w.n_kv_heads
+    return {"value": th / t_total, "unit": "token-heads/s", "cores": cores, "kind": "oracle",
+            "sample": f"{slices} slices of {n} tokens x {w.n_kv_heads} KV heads ({th} token-heads), fp64 NumPy, "
+                      f"BLAS threads={cores}; {t_total:.1f} s measured"}
+
+
 VALU_PEAK_LANE_OPS = 256 * 64 * 2.4e9  # CUs x vector lanes per clock per CU x clock
 
 
@@ -206,6 +277,7 @@ def bench_encode(args):
                      "hbm_GBps": (N * H * D * 2 + N * H * bpt) / launch_s / 1e9,
                      "avg_launch_us": launch_s * 1e6,
                      "work": "3 vector ops per (token, head, group, round, entry) candidate score"},
+        "cpu_baseline": None if args.no_cpu else encode_cpu_baseline(args.cpu_seconds, w),
     }
     print(json.dumps(rec), flush=True)
 
@@ -302,7 +374,7 @@ def bench_decode_workload(args):
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": code_bytes,
                      "avg_launch_us": ms * 1e3,
                      "kernel": "commvq_decode_attention call: decode kernel, then chunk-merge kernel"},
-        "cpu_baseline": None,
+        "cpu_baseline": None if args.no_cpu else decode_cpu_baseline(args.cpu_seconds, w, lens),
         "dense_fp16_same_shape": dense,
     }
     print(json.dumps(rec), flush=True)
@@ -405,6 +477,11 @@ def bench_naive(args):
             "hbm_peak_GBps": HBM_PEAK_GBS},
         "pages": "6x-9.6x lower decode latency than a naive implementation of the same quantization "
                  "(GPU and kernel configuration not stated)",
+        # the comparison path's dominant kernel: the dequantisation (codes in, fp16 keys and values out)
+        "roofline": {"bound": "hbm", "achieved": deq_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": deq_gbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": code_bytes + f16_bytes,
+                     "avg_launch_us": t_deq, "kernel": "dequant_kv_kernel (commvq_dequantize_kv)"},
+        "cpu_baseline": None if args.no_cpu else decode_cpu_baseline(args.cpu_seconds, w, np.full(B, Lmax)),
     }
     print(json.dumps(rec), flush=True)
 
@@ -412,11 +489,12 @@ def bench_naive(args):
 def bench_bitv(args):
     """Decode attention at 128K (B 1, 32 query / 8 KV heads, 1-bit keys g 8,
     Nc' 256, R 1) with the paper's binary value codes, 1024 bits per token over
-    the 1024 value scalars (1 bit per scalar): commvq_decode_attention_bitv,
-    beside commvq_decode_attention on the same keys with residual-codebook
-    values through the same generic kernel (COMMVQ_DECODE_EXACT) and through
-    the fast kernel. Caches of seeded random records rotated over layer slices
-    beyond the Infinity Cache; HIP events on the launch stream."""
+    the 1024 value scalars (1 bit per scalar): commvq_decode_attention_bitv on
+    its fast path and on the generic kernel (COMMVQ_DECODE_EXACT), beside
+    commvq_decode_attention on the same keys with residual-codebook values
+    through the generic and the fast kernel. Caches of seeded random records
+    rotated over layer slices beyond the Infinity Cache; HIP events on the
+    launch stream."""
     import torch
 
     from long_context_attention_commvq_amd import _lib, api, synth
@@ -449,11 +527,15 @@ def bench_bitv(args):
     sid = stream.cuda_stream
     sm = 1.0 / math.sqrt(D)
 
-    def bitv(i):
-        kc, _, vb = slices[i % NL]
-        _lib.commvq_decode_attention_bitv(kq.desc, vcb, rope, q.data_ptr(), qpos.data_ptr(), kc.data_ptr(),
-                                          vb.data_ptr(), lens.data_ptr(), B, Hq, Lmax, Lmax, sm, out.data_ptr(),
-                                          ws.buf.data_ptr(), ws.nbytes, sid)
+    wsb = api.BitvWorkspace(kq, nb, H * D, B, Hq, Lmax, dev)
+
+    def bitv(flags):
+        def call(i):
+            kc, _, vb = slices[i % NL]
+            _lib.commvq_decode_attention_bitv(kq.desc, vcb, rope, q.data_ptr(), qpos.data_ptr(), kc.data_ptr(),
+                                              vb.data_ptr(), lens.data_ptr(), B, Hq, Lmax, Lmax, sm, out.data_ptr(),
+                                              wsb.buf.data_ptr(), wsb.nbytes, flags, sid)
+        return call
 
     def residual(flags):
         def call(i):
@@ -476,20 +558,30 @@ def bench_bitv(args):
         torch.cuda.synchronize()
         return start.elapsed_time(stop) / args.steps * 1e3
 
-    t_bitv = timed(bitv, "binary value codes (generic kernel)")
+    t_bitv = timed(bitv(0), "binary value codes (fast kernel scores, matrix-core value sums)")
+    t_bitv_gen = timed(bitv(_lib.COMMVQ_DECODE_EXACT), "binary value codes (generic kernel)")
     t_gen = timed(residual(_lib.COMMVQ_DECODE_EXACT), "residual value codebook (generic kernel)")
     t_fast = timed(residual(0), "residual value codebook (fast kernel)")
     toks = B * Lmax
+    bitv_bytes = toks * (H * bpt + nb // 8)  # key records of every KV head + one value code per token
     rec = {
         "metric": "decode-attn cached tokens/s with the paper's binary value codes (GQA 32q/8kv, 128K ctx, 1 bit per "
                   "value scalar)",
         "value": toks / (t_bitv * 1e-6), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": t_bitv * 1e-3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp32", "data": "synthetic",
+        "dtype": "fp16", "data": "synthetic",
         "config": {"workload": "llama8b_ctx128k_1bit_binary_values", "batch": B, "n_q_heads": Hq, "n_kv_heads": H,
                    "head_dim": D, "context": Lmax, "value_bits": nb, "layer_slices": NL},
-        "calls_us": {"commvq_decode_attention_bitv": t_bitv, "commvq_decode_attention_exact_generic": t_gen,
+        "calls_us": {"commvq_decode_attention_bitv": t_bitv, "commvq_decode_attention_bitv_exact_generic": t_bitv_gen,
+                     "commvq_decode_attention_exact_generic": t_gen,
                      "commvq_decode_attention_fast": t_fast},
+        "roofline": {"bound": "hbm", "achieved": bitv_bytes / (t_bitv * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": bitv_bytes / (t_bitv * 1e-6) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": bitv_bytes, "avg_launch_us": t_bitv,
+                     "kernel": "commvq_decode_attention_bitv call: fast decode kernel (scores, softmax, weights), "
+                               "bitv_values_kernel, chunk-merge kernel"},
+        "cpu_baseline": None if args.no_cpu else decode_cpu_baseline(args.cpu_seconds, w, np.full(B, Lmax),
+                                                                     value_bits=nb),
     }
     print(json.dumps(rec), flush=True)
 

@@ -209,25 +209,37 @@ typedef struct commvq_bit_codebook {
   const void* rows;    /* device fp16 [n_bits][dim], 16-byte aligned */
 } commvq_bit_codebook;
 
+/* Workspace bytes for commvq_decode_attention_bitv with these shapes, enough
+ * for either of its paths (any flags); or a negative status for shapes it
+ * rejects. */
+int64_t commvq_decode_bitv_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
+                                           const commvq_codebook* kcb, const commvq_bit_codebook* vcb);
+
 /* Decode attention with binary value codes: as commvq_decode_attention for the
  * keys (kcb, kcodes, rope, q, q_pos, seq_lens, sizes, sm_scale, out), with the
  * value of position t of sequence b equal to the sum of the rows of vcb whose
  * bits are set in vbits[b][t] (bit i = bit i % 8 of byte i / 8); query head hq
- * reads columns [h D, h D + D) of that sum, h its KV head.
+ * reads columns [h D, h D + D) of that sum, h its KV head. The weights meet
+ * the codes before the rows: u = sum_t p_t s_t, then u^T C.
  *   vbits     device bytes [batch][cache_len][n_bits / 8], 16-byte aligned
- *   workspace >= commvq_decode_workspace_bytes(batch, n_q_heads, max_seq_len,
- *             kcb, kcb) bytes, 256-byte aligned, no initialisation needed.
- * Runs the generic kernel (fp32 table or rebuilt keys, exact phases); the
- * weights meet the codes before the rows (u = sum_t p_t s_t, then u^T C).
- * Shapes as commvq_decode_attention's generic path; vcb->dim must equal
- * Hkv * D (else COMMVQ_ERR_INVALID_ARG). */
+ *   workspace >= commvq_decode_bitv_workspace_bytes(...) bytes, 256-byte
+ *             aligned, no initialisation needed
+ *   flags     0 or COMMVQ_DECODE_EXACT
+ * Paths: on the fast kernel's key shapes (D 128, g 8, Nc' 256, R 1 or 2, four
+ * query heads per KV head), n_bits >= 128, n_q_heads <= 32 and flags 0, the
+ * fast kernel computes the scores and softmax and writes fp16 weights, and a
+ * second kernel forms u on the matrix cores (fp16 weights times the 0/1 bits,
+ * fp32 sums) and u^T C in fp32, per chunk and range of 128 bits. Otherwise
+ * the generic kernel runs (fp32 table or rebuilt keys, exact phases; shapes as
+ * commvq_decode_attention's generic path). vcb->dim must equal Hkv * D (else
+ * COMMVQ_ERR_INVALID_ARG). */
 int32_t commvq_decode_attention_bitv(const commvq_codebook* kcb, const commvq_bit_codebook* vcb,
                                      const commvq_rope* rope, const float* q, const int32_t* q_pos,
                                      const uint8_t* kcodes, const uint8_t* vbits,
                                      const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
                                      int32_t cache_len, int32_t max_seq_len, float sm_scale,
                                      float* out, void* workspace, size_t workspace_bytes,
-                                     void* stream);
+                                     uint32_t flags, void* stream);
 
 /* ---- comparison path: the "naive" decode of the same codes ----------------
  * The review ("Pith review of CommVQ", "The pith") compares the method's decode

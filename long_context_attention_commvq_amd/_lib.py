@@ -35,7 +35,7 @@ EXPORTED = [
     "commvq_abi_version", "commvq_last_error", "commvq_validate_codebook", "commvq_bits_per_scalar",
     "commvq_code_bytes_per_token", "commvq_decode_workspace_bytes", "commvq_encode", "commvq_append",
     "commvq_decode_attention", "commvq_decode_step", "commvq_dequantize_kv", "commvq_dense_workspace_bytes",
-    "commvq_dense_decode_attention", "commvq_em_work_bytes", "commvq_em_step", "commvq_decode_attention_bitv",
+    "commvq_dense_decode_attention", "commvq_em_work_bytes", "commvq_em_step", "commvq_decode_attention_bitv", "commvq_decode_bitv_workspace_bytes",
 ]
 
 
@@ -107,7 +107,10 @@ def lib():
         L.commvq_decode_attention_bitv.restype = c_int32
         L.commvq_decode_attention_bitv.argtypes = [CB, POINTER(commvq_bit_codebook), POINTER(commvq_rope), c_void_p,
                                                    c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
-                                                   c_int32, c_float, c_void_p, c_void_p, c_size_t, c_void_p]
+                                                   c_int32, c_float, c_void_p, c_void_p, c_size_t, ctypes.c_uint32,
+                                                   c_void_p]
+        L.commvq_decode_bitv_workspace_bytes.restype = c_int64
+        L.commvq_decode_bitv_workspace_bytes.argtypes = [c_int32, c_int32, c_int32, CB, POINTER(commvq_bit_codebook)]
         L.commvq_em_work_bytes.restype = c_int64
         L.commvq_em_work_bytes.argtypes = [CB]
         L.commvq_em_step.restype = c_int32
@@ -247,10 +250,17 @@ def commvq_em_step(cb: commvq_codebook, x, n_tokens: int, x_token_stride: int, r
         _ptr(new_entries), _ptr(mass_out), _ptr(work), int(work_bytes), _stream(stream, x, new_entries)))
 
 
+def commvq_decode_bitv_workspace_bytes(batch: int, n_q_heads: int, max_seq_len: int, kcb: commvq_codebook,
+                                      vcb: commvq_bit_codebook) -> int:
+    return lib().commvq_decode_bitv_workspace_bytes(batch, n_q_heads, max_seq_len, ctypes.byref(kcb),
+                                                    ctypes.byref(vcb))
+
+
 def commvq_decode_attention_bitv(kcb: commvq_codebook, vcb: commvq_bit_codebook, rope: commvq_rope, q, q_pos, kcodes,
                                  vbits, seq_lens, batch: int, n_q_heads: int, cache_len: int, max_seq_len: int,
-                                 sm_scale: float, out, workspace, workspace_bytes: int, stream=None) -> int:
+                                 sm_scale: float, out, workspace, workspace_bytes: int, flags: int = 0,
+                                 stream=None) -> int:
     return _check(lib().commvq_decode_attention_bitv(
         ctypes.byref(kcb), ctypes.byref(vcb), ctypes.byref(rope), _ptr(q), _ptr(q_pos), _ptr(kcodes), _ptr(vbits),
         _ptr(seq_lens), batch, n_q_heads, cache_len, max_seq_len, float(sm_scale), _ptr(out), _ptr(workspace),
-        int(workspace_bytes), _stream(stream, q, out)))
+        int(workspace_bytes), int(flags), _stream(stream, q, out)))

@@ -191,10 +191,23 @@ def em_step(quant: Quantizer, x: torch.Tensor, round_index: int, temperature: fl
 
 # ---- binary value codes ---------------------------------------------------------
 
+class BitvWorkspace:
+    """Workspace of commvq_decode_attention_bitv for one shape (either path)."""
+
+    def __init__(self, kq: Quantizer, n_bits: int, dim: int, batch: int, n_q_heads: int, max_seq_len: int,
+                 device):
+        vcb = _lib.make_bit_codebook(None, n_bits, dim)
+        n = _lib.commvq_decode_bitv_workspace_bytes(batch, n_q_heads, max_seq_len, kq.desc, vcb)
+        if n < 0:
+            raise _lib.CommvqError(int(n), _lib.commvq_last_error())
+        self.nbytes = int(n)
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+
+
 def decode_attention_bitv(kq: Quantizer, rows: torch.Tensor, q: torch.Tensor, q_pos: torch.Tensor,
                           kcache: torch.Tensor, vbits: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
                           theta_base: float, sm_scale: float | None = None, out: torch.Tensor | None = None,
-                          workspace: DecodeWorkspace | None = None) -> torch.Tensor:
+                          workspace: BitvWorkspace | None = None, flags: int = 0) -> torch.Tensor:
     """Keys from packed caches [B, Hkv, Lmax, bpt]; values from binary codes
     vbits uint8 [B, Lmax, Nc/8] and rows fp16 [Nc, Hkv * D]."""
     B, Hq, D = q.shape
@@ -203,10 +216,10 @@ def decode_attention_bitv(kq: Quantizer, rows: torch.Tensor, q: torch.Tensor, q_
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = DecodeWorkspace(kq, kq, B, Hq, max_seq_len, q.device)
+        workspace = BitvWorkspace(kq, rows.shape[0], rows.shape[1], B, Hq, max_seq_len, q.device)
     rows = rows.contiguous()
     vcb = _lib.make_bit_codebook(rows, rows.shape[0], rows.shape[1])
     rope = _lib.make_rope(theta_base)
     _lib.commvq_decode_attention_bitv(kq.desc, vcb, rope, q, q_pos, kcache, vbits, seq_lens, B, Hq, kcache.shape[2],
-                                      max_seq_len, sm_scale, out, workspace.buf, workspace.nbytes)
+                                      max_seq_len, sm_scale, out, workspace.buf, workspace.nbytes, flags)
     return out

@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcommvq.so")
-SOURCES = ["api.cpp", "encode.hip", "decode.hip", "decode_fast.hip", "decode_merge.hip", "naive.hip", "em.hip"]
+SOURCES = ["api.cpp", "encode.hip", "decode.hip", "decode_fast.hip", "decode_merge.hip", "decode_bitv.hip", "naive.hip", "em.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 instructions are switched off for all device code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",

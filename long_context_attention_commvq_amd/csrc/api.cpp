@@ -602,25 +602,46 @@ int32_t commvq_em_step(const commvq_codebook* cb, const void* x, int64_t n_token
 
 extern "C" {
 
+// Shapes of a binary-value decode: the key codebook as for decode attention,
+// the bit codebook's descriptor (rows not checked).
+static int32_t bitv_shapes(const commvq_codebook* kcb, const commvq_bit_codebook* vcb, int32_t batch,
+                           int32_t n_q_heads, int32_t max_seq_len, uint32_t flags, commvq::CbShape* k) {
+  commvq::CbShape kk;
+  int32_t st = decode_shapes(kcb, kcb, batch, n_q_heads, max_seq_len, k, &kk);
+  if (st) return st;
+  if (flags & ~(uint32_t)COMMVQ_DECODE_EXACT) return fail(COMMVQ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (!vcb) return fail(COMMVQ_ERR_INVALID_ARG, "null binary value codebook");
+  const int nb = vcb->n_bits;
+  if (nb < 32 || nb > 2048 || (nb & (nb - 1)))
+    return fail(COMMVQ_ERR_INVALID_ARG, "n_bits %d must be a power of two in [32, 2048]", nb);
+  if ((int64_t)vcb->dim != (int64_t)k->Hkv * k->D)
+    return fail(COMMVQ_ERR_INVALID_ARG, "binary value codebook dim %d must equal n_kv_heads*head_dim %d", vcb->dim,
+                k->Hkv * k->D);
+  if (vcb->dtype != COMMVQ_F16 || vcb->reserved != 0)
+    return fail(COMMVQ_ERR_INVALID_ARG, "binary value codebook: dtype must be COMMVQ_F16, reserved 0");
+  return COMMVQ_OK;
+}
+
+int64_t commvq_decode_bitv_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
+                                           const commvq_codebook* kcb, const commvq_bit_codebook* vcb) {
+  g_err[0] = 0;
+  commvq::CbShape k;
+  const int32_t st = bitv_shapes(kcb, vcb, batch, n_q_heads, max_seq_len, 0, &k);
+  if (st) return st;
+  return (int64_t)commvq::decode_bitv_workspace_bytes(k, vcb->n_bits, batch, n_q_heads, max_seq_len);
+}
+
 int32_t commvq_decode_attention_bitv(const commvq_codebook* kcb, const commvq_bit_codebook* vcb,
                                      const commvq_rope* rope, const float* q, const int32_t* q_pos,
                                      const uint8_t* kcodes, const uint8_t* vbits, const int32_t* seq_lens,
                                      int32_t batch, int32_t n_q_heads, int32_t cache_len, int32_t max_seq_len,
                                      float sm_scale, float* out, void* workspace, size_t workspace_bytes,
-                                     void* stream) {
+                                     uint32_t flags, void* stream) {
   g_err[0] = 0;
-  commvq::CbShape k, kk;
-  int32_t st = decode_shapes(kcb, kcb, batch, n_q_heads, max_seq_len, &k, &kk);
+  commvq::CbShape k;
+  int32_t st = bitv_shapes(kcb, vcb, batch, n_q_heads, max_seq_len, flags, &k);
   if (st) return st;
-  if (!vcb) return fail(COMMVQ_ERR_INVALID_ARG, "null binary value codebook");
   const int nb = vcb->n_bits;
-  if (nb < 32 || nb > 2048 || (nb & (nb - 1)))
-    return fail(COMMVQ_ERR_INVALID_ARG, "n_bits %d must be a power of two in [32, 2048]", nb);
-  if ((int64_t)vcb->dim != (int64_t)k.Hkv * k.D)
-    return fail(COMMVQ_ERR_INVALID_ARG, "binary value codebook dim %d must equal n_kv_heads*head_dim %d", vcb->dim,
-                k.Hkv * k.D);
-  if (vcb->dtype != COMMVQ_F16 || vcb->reserved != 0)
-    return fail(COMMVQ_ERR_INVALID_ARG, "binary value codebook: dtype must be COMMVQ_F16, reserved 0");
   if (!vcb->rows || (reinterpret_cast<uintptr_t>(vcb->rows) & 15))
     return fail(COMMVQ_ERR_INVALID_ARG, "binary value codebook rows must be non-null and 16-byte aligned");
   st = check_rope(rope);
@@ -637,11 +658,11 @@ int32_t commvq_decode_attention_bitv(const commvq_codebook* kcb, const commvq_bi
   if ((reinterpret_cast<uintptr_t>(kcodes) | reinterpret_cast<uintptr_t>(vbits)) & 15)
     return fail(COMMVQ_ERR_INVALID_ARG, "kcodes and vbits must be 16-byte aligned");
   const int NH = n_q_heads / k.Hkv;
-  if (commvq::decode_bitv_smem(k, nb, NH) > 160 * 1024)
+  const bool fast = commvq::decode_bitv_fast_path(k, nb, n_q_heads, (int)flags);
+  if (!fast && commvq::decode_bitv_smem(k, nb, NH) > 160 * 1024)
     return fail(COMMVQ_ERR_UNSUPPORTED, "binary value decode's LDS staging for %d query heads and %d bits exceeds 160 KiB",
                 NH, nb);
-  const int64_t need = commvq_decode_workspace_bytes(batch, n_q_heads, max_seq_len, kcb, kcb);
-  if (need < 0) return (int32_t)need;
+  const int64_t need = (int64_t)commvq::decode_bitv_workspace_bytes(k, nb, batch, n_q_heads, max_seq_len);
   if (!workspace || workspace_bytes < (size_t)need)
     return fail(COMMVQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %lld required", workspace_bytes,
                 (long long)need);
@@ -663,14 +684,24 @@ int32_t commvq_decode_attention_bitv(const commvq_codebook* kcb, const commvq_bi
   a.NH = NH;
   a.cache_len = cache_len;
   a.max_len = max_seq_len;
-  a.chunk = 1024;  // the generic kernel's chunk
+  a.chunk = commvq::decode_chunk_len(k, k, batch, n_q_heads, max_seq_len, fast ? (int)flags : COMMVQ_DECODE_EXACT);
   a.n_chunks = (max_seq_len + a.chunk - 1) / a.chunk;
   a.sm_scale = sm_scale;
   a.k = k;
   a.v = k;
   const PhaseConsts& pc = phase_consts(rope->theta_base, k.D);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = commvq::launch_decode_bitv(a, pc.ph, s);
+  hipError_t e;
+  if (fast) {
+    // weights and chunk statistics, then o per (chunk, 128-bit range) slot
+    a.pw = reinterpret_cast<_Float16*>(static_cast<char*>(workspace) +
+                                       commvq::decode_bitv_pw_offset(k, nb, batch, n_q_heads, max_seq_len, a.chunk));
+    a.n_chunks *= nb / 128;
+    e = commvq::launch_decode_fast_bitv_scores(a, pc.ph, s);
+    if (e == hipSuccess) e = commvq::launch_bitv_values(a, s);
+  } else {
+    e = commvq::launch_decode_bitv(a, pc.ph, s);
+  }
   if (e == hipSuccess) e = commvq::launch_decode_merge(a, s);
   return hip_status(e, "commvq_decode_attention_bitv launch");
 }

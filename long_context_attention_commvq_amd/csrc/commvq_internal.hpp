@@ -65,6 +65,9 @@ struct DecodeArgs {
   const uint8_t* vbits;
   const _Float16* vrows;
   int nbits;
+  // binary value codes on the fast kernel: softmax weights e^{s - M} of every
+  // position, fp16 [B][Hq][n_chunks / (nbits / 128) * chunk]
+  _Float16* pw;
   int B, Hq, NH, cache_len, max_len, n_chunks, chunk;
   float sm_scale;
   CbShape k, v;
@@ -138,6 +141,16 @@ size_t decode_generic_smem(const CbShape& k, const CbShape& v, int NH);
 size_t decode_bitv_smem(const CbShape& k, int nbits, int NH);
 // The generic kernel with binary value codes (a.vbits, a.vrows, a.nbits).
 hipError_t launch_decode_bitv(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream);
+// Binary value codes on the fast kernel's shapes (and nbits a multiple of 128,
+// Hq <= 32): the fast kernel's scores and softmax write the weights a.pw and
+// each chunk's (M, l); bitv_values_kernel forms each (chunk, 128-bit range)'s
+// o on the matrix cores. a.n_chunks counts partial slots: chunks x nbits / 128.
+bool decode_bitv_fast_path(const CbShape& k, int nbits, int Hq, int flags);
+size_t decode_bitv_workspace_bytes(const CbShape& k, int nbits, int B, int Hq, int max_len);  // either path
+// byte offset of the weights in the fast path's workspace (after the partials)
+size_t decode_bitv_pw_offset(const CbShape& k, int nbits, int B, int Hq, int max_len, int chunk);
+hipError_t launch_decode_fast_bitv_scores(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream);
+hipError_t launch_bitv_values(const DecodeArgs& a, hipStream_t stream);
 size_t decode_workspace_bytes(const CbShape& k, int B, int Hq, int max_len, int chunk);
 // Byte offset of the new-token area in the workspace (after the partials, 256-aligned).
 size_t decode_newtok_offset(const CbShape& k, int B, int Hq, int max_len, int chunk);

@@ -186,7 +186,12 @@ __device__ __forceinline__ int search_row64_dot(const half2_t (&e2)[4], const h8
   return bi;
 }
 
-template <int R, int TL>
+// BV: binary value codes (a.vbits). The workgroup then stops after the
+// softmax: it writes its positions' weights e^{s - M} (fp16, a.pw) and the
+// chunk's (M, l) into each of its nbits / 128 partial slots (one per range of
+// value-code bits; l in the first only), and bitv_values_kernel adds each
+// range's o.
+template <int R, int TL, bool BV>
 __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseTable ph) {
   using Cfg = FastCfg<R>;
   constexpr int BPT = Cfg::BPT;
@@ -210,8 +215,9 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   const int h = blockIdx.x % a.k.Hkv, chunk = blockIdx.x / a.k.Hkv, b = blockIdx.y;
   const int L = min(max(a.seq_lens[b], 0), a.max_len);
   const int m0 = chunk * C;
+  const int NR = BV ? a.nbits / 128 : 1;  // partial slots per chunk
   const size_t pstride = (size_t)a.n_chunks * (FD + 2);
-  float* part = a.part + ((size_t)b * a.Hq + h * FNH) * pstride + (size_t)chunk * (FD + 2);
+  float* part = a.part + ((size_t)b * a.Hq + h * FNH) * pstride + (size_t)chunk * NR * (FD + 2);
   // the query pair this lane rotates (lanes < 256: head tid / 64, pair tid % 64),
   // requested before anything else
   const float2 qx = tid < FNH * FPR
@@ -360,9 +366,9 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     for (int t = 0; t < NB - (NB < TL ? 1 : 0); ++t)
 #pragma unroll
       for (int r = 0; r < R; ++r) asm volatile("" ::"v"(cw[t][r][0]), "v"(cw[t][r][1]), "v"(cw[t][r][2]), "v"(cw[t][r][3]));
-    for (int i = tid; i < FNH * (FD + 2); i += FT) {
-      const int hh = i / (FD + 2), k = i % (FD + 2);
-      part[hh * pstride + k] = (k == 0) ? -INFINITY : 0.f;
+    for (int i = tid; i < FNH * NR * (FD + 2); i += FT) {
+      const int hh = i / (NR * (FD + 2)), k = i % (NR * (FD + 2));
+      part[hh * pstride + k] = (k % (FD + 2) == 0) ? -INFINITY : 0.f;
     }
     row_job();
     return;
@@ -509,8 +515,8 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   // rotation over groups in the histogram stage)
   const int g16 = tid & 15, h16 = (tid >> 4) & 1;
   const int q4 = (g16 >> 2) & 3, sh4 = g16 & 3;
-  uint32_t ve[TL][R][4];
-  {
+  uint32_t ve[TL][R][4];  // (unused, and removed, when BV)
+  if constexpr (!BV) {
     const uint8_t* vb = a.vcodes + ((size_t)b * a.v.Hkv + h) * (size_t)a.cache_len * BPT;
 #pragma unroll
     for (int t = 0; t < TL; ++t) {
@@ -528,7 +534,7 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   // factor e^{M_w - M} then enters the fixed-point scale of the histogram stage,
   // and the wavefront sums are combined with it at the end.
   float M[FNH], fw[FNH], lsum[FNH];
-  if constexpr (Cfg::HOFF >= Cfg::KCB) {
+  if constexpr (!BV && Cfg::HOFF >= Cfg::KCB) {
     uint4* hs = reinterpret_cast<uint4*>(lds + Cfg::HOFF) + wave * (Cfg::HIST / 16 / FW);
 #pragma unroll
     for (int i = 0; i < Cfg::HIST / 16 / FT; ++i) hs[lane + 64 * i] = make_uint4(0, 0, 0, 0);
@@ -585,6 +591,29 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
 #pragma unroll
     for (int k = 0; k < FNH; ++k)
       lsum[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, term), 8 * k));
+  }
+  if constexpr (BV) {
+    // weights e^{s - M} = e^{s - M_w} e^{M_w - M} of the lane's positions
+    // (0 past the sequence), rows [B][Hq][n_pos_chunks * C]
+    const size_t plen = (size_t)(a.n_chunks / NR) * C;
+    _Float16* pwb = a.pw + ((size_t)b * a.Hq + h * FNH) * plen;
+#pragma unroll
+    for (int t = 0; t < TL; ++t)
+#pragma unroll
+      for (int k = 0; k < FNH; ++k) pwb[k * plen + m0 + tid + FT * t] = (_Float16)(s[t][k] * fw[k]);
+    if (tid < FNH * NR) {
+      const int hh = tid / NR, rr = tid % NR;
+      float mk = M[0], lk = lsum[0];
+#pragma unroll
+      for (int k = 1; k < FNH; ++k)
+        if (hh == k) {
+          mk = M[k];
+          lk = lsum[k];
+        }
+      part[hh * pstride + rr * (FD + 2)] = mk;
+      part[hh * pstride + rr * (FD + 2) + 1] = rr == 0 ? lk : 0.f;
+    }
+    return;
   }
   if constexpr (Cfg::HOFF < Cfg::KCB) {
     // the histograms replace the key codebook
@@ -739,18 +768,19 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
   }
 }
 
-template <int R, int TL>
+template <int R, int TL, bool BV>
 hipError_t launch_fast_t(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_fast_kernel<R, TL>), dim3(a.n_chunks * a.k.Hkv, a.B), dim3(FT), 0, stream, a, ph);
+  const int npc = BV ? a.n_chunks / (a.nbits / 128) : a.n_chunks;  // chunks of positions
+  hipLaunchKernelGGL((decode_fast_kernel<R, TL, BV>), dim3(npc * a.k.Hkv, a.B), dim3(FT), 0, stream, a, ph);
   return hipGetLastError();
 }
 
-template <int R>
+template <int R, bool BV>
 hipError_t launch_fast_r(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
   switch (a.chunk) {
-    case 4096: return launch_fast_t<R, 8>(a, ph, stream);
-    case 2048: return launch_fast_t<R, 4>(a, ph, stream);
-    case 1024: return launch_fast_t<R, 2>(a, ph, stream);
+    case 4096: return launch_fast_t<R, 8, BV>(a, ph, stream);
+    case 2048: return launch_fast_t<R, 4, BV>(a, ph, stream);
+    case 1024: return launch_fast_t<R, 2, BV>(a, ph, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -758,8 +788,15 @@ hipError_t launch_fast_r(const DecodeArgs& a, const PhaseTable& ph, hipStream_t 
 }  // namespace
 
 hipError_t launch_decode_fast(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
-  if (a.k.R == 1) return launch_fast_r<1>(a, ph, stream);
-  if (a.k.R == 2) return launch_fast_r<2>(a, ph, stream);
+  if (a.k.R == 1) return launch_fast_r<1, false>(a, ph, stream);
+  if (a.k.R == 2) return launch_fast_r<2, false>(a, ph, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_fast_bitv_scores(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
+  if (a.nbits < 128 || a.nbits % 128 || a.n_chunks % (a.nbits / 128) || !a.pw || a.k_new) return hipErrorInvalidValue;
+  if (a.k.R == 1) return launch_fast_r<1, true>(a, ph, stream);
+  if (a.k.R == 2) return launch_fast_r<2, true>(a, ph, stream);
   return hipErrorInvalidValue;
 }
 

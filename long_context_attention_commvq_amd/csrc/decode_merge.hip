@@ -14,14 +14,15 @@
 namespace commvq {
 namespace {
 
-constexpr int kMergeThreads = 256;
-
-// One workgroup per (sequence, query head). Lane t takes dimension t % D and the
-// chunks c = t / D (mod 256 / D), loading 16 of them at a time before using
-// any (one memory round trip per batch; batches are combined with a running max
-// and rescaling). The lanes sharing a dimension are combined the same way
-// through LDS.
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
+// One workgroup (T lanes) per (sequence, query head). Lane t takes dimension
+// t % D and the chunks c = t / D (mod T / D), loading 16 of them at a time
+// before using any (one memory round trip per batch; batches are combined with
+// a running max and rescaling). The lanes sharing a dimension are combined the
+// same way through LDS. T = 1024 when there are many partials (the binary-value
+// path's chunk x bit-range slots), so that fewer batches run in a row.
+template <int T>
+__global__ __launch_bounds__(T) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int kMergeThreads = T;
   __shared__ float sm[3][kMergeThreads];
   __shared__ float sc_new;
   const float* __restrict__ part = a.part;
@@ -112,9 +113,12 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
 }  // namespace
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
-  if (a.k.D > kMergeThreads) return hipErrorInvalidValue;
+  if (a.k.D > 256) return hipErrorInvalidValue;
   if (a.fold_new && (a.k.D != 128 || a.NH != 4)) return hipErrorInvalidValue;  // the fast kernel's shape
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.Hq, a.B), dim3(kMergeThreads), 0, stream, a);
+  if (a.n_chunks > 64)
+    hipLaunchKernelGGL(decode_merge_kernel<1024>, dim3(a.Hq, a.B), dim3(1024), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<256>, dim3(a.Hq, a.B), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

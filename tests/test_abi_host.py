@@ -282,10 +282,11 @@ def test_bit_value_decode_validation_without_launch():
     L = _lib.lib()
     E = _lib
 
-    def bitv(nb=1024, dim=1024, rows=FAKE, Hq=32, bits=FAKE, ws_bytes=1 << 30):
+    def bitv(nb=1024, dim=1024, rows=FAKE, Hq=32, bits=FAKE, ws_bytes=1 << 30, flags=0):
         v = _lib.make_bit_codebook(rows, nb, dim)
         return L.commvq_decode_attention_bitv(ctypes.byref(k), ctypes.byref(v), ctypes.byref(rope), FAKE, FAKE, FAKE,
-                                              bits, FAKE, 1, Hq, 1024, 1024, 0.088, FAKE, FAKE, ws_bytes, None)
+                                              bits, FAKE, 1, Hq, 1024, 1024, 0.088, FAKE, FAKE, ws_bytes, flags, None)
+    assert bitv(flags=2) == E.COMMVQ_ERR_INVALID_ARG
     assert bitv(nb=1000) == E.COMMVQ_ERR_INVALID_ARG
     assert bitv(nb=4096) == E.COMMVQ_ERR_INVALID_ARG
     assert bitv(dim=512) == E.COMMVQ_ERR_INVALID_ARG
@@ -295,3 +296,20 @@ def test_bit_value_decode_validation_without_launch():
     assert bitv(bits=FAKE + 4) == E.COMMVQ_ERR_INVALID_ARG
     assert bitv(Hq=24) == E.COMMVQ_ERR_UNSUPPORTED
     assert bitv(ws_bytes=16) == E.COMMVQ_ERR_WORKSPACE
+
+
+def test_bit_value_workspace_sizes():
+    """Workspace of the binary-value decode, in closed form. 128K positions, 32
+    query / 8 KV heads, 1-bit keys, 1024-bit codes (fast path, chunks of 4096):
+    partial slots [1][32][32 chunks x 8 ranges][130] fp32 plus fp16 weights
+    [1][32][131072]; the generic kernel's need (chunks of 1024, and the
+    new-token area) is smaller. 64-bit codes: the generic path only."""
+    k = cb(D=128, g=8, Nc=256, R=1, H=8)
+    v = _lib.make_bit_codebook(None, 1024, 1024)
+    fast = 32 * 32 * 8 * 130 * 4 + 32 * 131072 * 2
+    assert _lib.commvq_decode_bitv_workspace_bytes(1, 32, 131072, k, v) == fast
+    generic = 32 * 128 * 130 * 4 + 8 * 192 * 4
+    v64 = _lib.make_bit_codebook(None, 64, 1024)
+    assert _lib.commvq_decode_bitv_workspace_bytes(1, 32, 131072, k, v64) == generic
+    assert _lib.commvq_decode_bitv_workspace_bytes(1, 32, 131072, k, _lib.make_bit_codebook(None, 1000, 1024)) == \
+        _lib.COMMVQ_ERR_INVALID_ARG

@@ -65,6 +65,47 @@ def test_bit_value_decode_matches_oracle(case):
     assert err.max() <= ATTN_TOL
 
 
+@pytest.mark.parametrize("case", [
+    # the fast kernel's key shapes (g 8, Nc' 256, R 1 or 2, 4 query heads per KV head), >= 128-bit codes
+    dict(B=2, Hq=4, Hkv=1, R=2, nbits=128, lens=[1500, 0], Lmax=2048),          # one range; 12 padded heads; a zero length
+    dict(B=3, Hq=16, Hkv=4, R=1, nbits=256, lens=[1, 33, 1025], Lmax=1100),     # ragged tails inside a k-step
+    dict(B=1, Hq=32, Hkv=8, R=2, nbits=2048, lens=[5000], Lmax=5000),           # 16 ranges (the paper's 2-bit width)
+    dict(B=1, Hq=32, Hkv=8, R=1, nbits=1024, lens=[9000], Lmax=9000, qscale=8.0),  # peaked scores
+    dict(B=2, Hq=8, Hkv=2, R=1, nbits=512, lens=[2047, 2049], Lmax=4100),       # chunk and range edges
+])
+def test_bit_value_fast_path_matches_oracle_and_generic(case):
+    """On the fast kernel's shapes commvq_decode_attention_bitv takes the fast
+    path (fp16 weights on the matrix cores); COMMVQ_DECODE_EXACT takes the
+    generic kernel. Both meet the bar against the oracle, and they differ (two
+    paths ran)."""
+    B, Hq, Hkv, R, nb, Lmax = (case[k] for k in ("B", "Hq", "Hkv", "R", "nbits", "Lmax"))
+    D, g, Nc = 128, 8, 256
+    lens = np.asarray(case["lens"], dtype=np.int32)
+    seed = 9300 + R + nb + Hq + int(lens.sum()) % 97
+    rng = np.random.default_rng(seed)
+    kcb = synth.codebook(seed + 1, Hkv, D, g, Nc, R)
+    kp = rng.integers(0, 256, size=(B, Hkv, Lmax, 16 * R), dtype=np.uint8)  # every byte string is a valid record
+    vbits = rng.integers(0, 256, size=(B, Lmax, nb // 8), dtype=np.uint8)
+    rows = bit_rows(seed + 2, nb, Hkv * D)
+    q = synth.queries(seed + 3, B, Hq, D) * np.float32(case.get("qscale", 1.0))
+    qpos = np.maximum(lens, 1) - 1
+    ref = O.decode_attention_bit_values(q, qpos, kp, vbits, lens, kcb, rows, 500000.0)
+    kq = api.Quantizer(dev(kcb), g)
+    args = (kq, dev(rows), dev(q), dev(qpos), dev(kp), dev(vbits), dev(lens), Lmax, 500000.0)
+    fast = api.decode_attention_bitv(*args)
+    exact = api.decode_attention_bitv(*args, flags=_lib.COMMVQ_DECODE_EXACT)
+    torch.cuda.synchronize()
+    fast, exact = fast.cpu().numpy(), exact.cpu().numpy()
+    for name, got in (("fast", fast), ("generic", exact)):
+        err = row_errors(got.reshape(-1, D), ref.reshape(-1, D))
+        print(f"[bit values {name} {case}] max row rel err {err.max():.3e}", flush=True)
+        assert err.max() <= ATTN_TOL
+        for b in range(B):
+            if lens[b] == 0:
+                assert np.all(got[b] == 0.0)
+    assert not np.array_equal(fast, exact)
+
+
 def test_bit_value_decode_rejects_bad_arguments():
     kcb = synth.codebook(9100, 2, 64, 8, 16, 1)
     kq = api.Quantizer(dev(kcb), 8)
