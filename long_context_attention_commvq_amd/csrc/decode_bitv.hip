@@ -146,9 +146,14 @@ __global__ __launch_bounds__(kBvThreads, 1) void bitv_values_kernel(DecodeArgs a
   const int dimc = a.k.Hkv * kBvD;
   const bool kv_ok = kv < a.k.Hkv;
   const _Float16* crow = a.vrows + (size_t)(kBvRange * r + 32 * qq) * dimc + (kv_ok ? kv : 0) * kBvD + 8 * d8;
-  h8_t cv0[16], cv1[16];  // rows 0..15 now, 16..31 once the reduction is done
+  // four batches of 8 rows, each requested one batch ahead of its use (the
+  // first before the reduction)
+  h8_t cvb[2][8];
+  auto load_rows = [&](h8_t (&dst)[8], int i0) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) cv0[i] = *reinterpret_cast<const h8_t*>(crow + (size_t)i * dimc);
+    for (int i = 0; i < 8; ++i) dst[i] = *reinterpret_cast<const h8_t*>(crow + (size_t)(i0 + i) * dimc);
+  };
+  load_rows(cvb[0], 0);
   for (int e = tid; e < HP * kBvRange; e += kBvThreads) {
     const int head = e / kBvRange, bit = e % kBvRange;
     float sum = 0.f;
@@ -159,17 +164,18 @@ __global__ __launch_bounds__(kBvThreads, 1) void bitv_values_kernel(DecodeArgs a
   __syncthreads();
 
   // o[4 kv + k][d] over the quarter's rows: sum_i u[4 kv + k][i] C[128 r + i][kv D + d]
-#pragma unroll
-  for (int i = 0; i < 16; ++i) cv1[i] = *reinterpret_cast<const h8_t*>(crow + (size_t)(16 + i) * dimc);
   float o[4][8];
 #pragma unroll
   for (int k = 0; k < 4; ++k)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[k][e] = 0.f;
-  auto rows16 = [&](const h8_t (&cvh)[16], int i0) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float4_t u4 = *reinterpret_cast<const float4_t*>(ub + (32 * qq + i0 + i) * kBvURow + 4 * (kv_ok ? kv : 0));
+  for (int bt = 0; bt < 4; ++bt) {
+    if (bt < 3) load_rows(cvb[(bt + 1) & 1], 8 * (bt + 1));
+    const h8_t (&cvh)[8] = cvb[bt & 1];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4_t u4 = *reinterpret_cast<const float4_t*>(ub + (32 * qq + 8 * bt + i) * kBvURow + 4 * (kv_ok ? kv : 0));
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float cf = (float)cvh[i][e];
@@ -177,9 +183,7 @@ __global__ __launch_bounds__(kBvThreads, 1) void bitv_values_kernel(DecodeArgs a
         for (int k = 0; k < 4; ++k) o[k][e] = fmaf(u4[k], cf, o[k][e]);
       }
     }
-  };
-  rows16(cv0, 0);
-  rows16(cv1, 16);
+  }
   float* osum = reinterpret_cast<float*>(r0);  // [quarter][head][dim] (u's partials are consumed)
   if (kv_ok) {
 #pragma unroll

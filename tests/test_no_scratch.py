@@ -12,7 +12,7 @@ import pytest
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(ROOT, "long_context_attention_commvq_amd", "csrc")
-SOURCES = ["decode_fast.hip", "decode.hip", "decode_merge.hip", "encode.hip"]
+SOURCES = ["decode_fast.hip", "decode.hip", "decode_merge.hip", "decode_bitv.hip", "encode.hip", "naive.hip", "em.hip"]
 
 
 @pytest.mark.skipif(shutil.which("hipcc") is None, reason="hipcc not available")
