@@ -57,7 +57,10 @@ typedef enum commvq_dtype { COMMVQ_F16 = 1 } commvq_dtype;
  * fp32): its score error is about 4e-4 of |q||k|/sqrt(D), which keeps outputs
  * within 1e-4 of an fp64 reference for unit-variance queries but grows with the
  * spread of the scores. COMMVQ_DECODE_EXACT keeps the table in fp32 and every
- * phase exact (slower), for strongly peaked attention. */
+ * phase exact (slower), for strongly peaked attention. The kernel for the other
+ * shapes (fp32 table or rebuilt keys) takes each position's phase from the
+ * hardware sine and cosine of its exact turn count (within 2e-7), and from an
+ * exact sincospi under COMMVQ_DECODE_EXACT. */
 #define COMMVQ_DECODE_EXACT 1u
 
 /* One codebook (keys or values) for all KV heads of one layer.
@@ -230,7 +233,7 @@ int64_t commvq_decode_bitv_workspace_bytes(int32_t batch, int32_t n_q_heads, int
  * fast kernel computes the scores and softmax and writes fp16 weights, and a
  * second kernel forms u on the matrix cores (fp16 weights times the 0/1 bits,
  * fp32 sums) and u^T C in fp32, per chunk and range of 128 bits. Otherwise
- * the generic kernel runs (fp32 table or rebuilt keys, exact phases; shapes as
+ * the generic kernel runs (fp32 table or rebuilt keys, phases as above; shapes as
  * commvq_decode_attention's generic path). vcb->dim must equal Hkv * D (else
  * COMMVQ_ERR_INVALID_ARG). */
 int32_t commvq_decode_attention_bitv(const commvq_codebook* kcb, const commvq_bit_codebook* vcb,

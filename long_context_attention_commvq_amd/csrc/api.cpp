@@ -335,6 +335,7 @@ int32_t decode_impl(const commvq_codebook* kcb, const commvq_codebook* vcb, cons
   a.chunk = commvq::decode_chunk_len(k, v, batch, n_q_heads, max_seq_len, (int)flags);
   a.n_chunks = (max_seq_len + a.chunk - 1) / a.chunk;
   a.sm_scale = sm_scale;
+  a.exact_phase = (flags & COMMVQ_DECODE_EXACT) ? 1 : 0;
   a.k = k;
   a.v = v;
   const PhaseConsts& pc = phase_consts(rope->theta_base, k.D);
@@ -687,6 +688,7 @@ int32_t commvq_decode_attention_bitv(const commvq_codebook* kcb, const commvq_bi
   a.chunk = commvq::decode_chunk_len(k, k, batch, n_q_heads, max_seq_len, fast ? (int)flags : COMMVQ_DECODE_EXACT);
   a.n_chunks = (max_seq_len + a.chunk - 1) / a.chunk;
   a.sm_scale = sm_scale;
+  a.exact_phase = (flags & COMMVQ_DECODE_EXACT) ? 1 : 0;
   a.k = k;
   a.v = k;
   const PhaseConsts& pc = phase_consts(rope->theta_base, k.D);

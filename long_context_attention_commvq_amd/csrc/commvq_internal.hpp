@@ -70,6 +70,9 @@ struct DecodeArgs {
   _Float16* pw;
   int B, Hq, NH, cache_len, max_len, n_chunks, chunk;
   float sm_scale;
+  // generic kernel: 1 = exact position phases (COMMVQ_DECODE_EXACT), 0 = the
+  // hardware sine and cosine of the exact turn count
+  int exact_phase;
   CbShape k, v;
 };
 

@@ -16,10 +16,13 @@
 //      codebook (review, "If this is right", fourth bullet);
 //   5. the chunk's (max, sum, unnormalised output) go to the workspace and the
 //      last workgroup to finish for (b, h) merges the chunks.
-// This kernel keeps the table in fp32 and computes every phase exactly; it serves
-// every supported shape and the exact-precision mode.
+// This kernel keeps the table in fp32; position phases come from the hardware
+// sine and cosine of the exact turn count, or from sincospi of it in the
+// exact-precision mode (a.exact_phase). It serves every supported shape.
 // Positions' phases come from 64-bit fixed-point turn counts, exact for any
 // position below 2^31.
+
+#include <type_traits>
 
 #include "decode_common.hpp"
 
@@ -90,93 +93,103 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, 
   const uint8_t* kbase = a.kcodes + ((size_t)b * K.Hkv + h) * (size_t)a.cache_len * K.bpt;
   const uint8_t* vbase = a.vcodes + ((size_t)b * V.Hkv + h) * (size_t)a.cache_len * V.bpt;
 
-  if constexpr (GS >= kWideGroup) {
-    // Wide groups (many pairs share an index): the key itself is rebuilt per
-    // 32-scalar slice of a group - every round's entries of the slice staged in
-    // LDS as fp16, summed in fp32 over the rounds - then rotated once per pair
-    // and dotted with the rotated queries. A query x codebook table per (group,
-    // round) would cost a phase and NH products per pair and round instead.
-    constexpr int SL = 32, SP = SL / 2;
-    _Float16* cbs = reinterpret_cast<_Float16*>(uni);  // [R][Nc][SL]
-    for (int j = 0; j < G; ++j) {
-      for (int sl = 0; sl < GS / SL; ++sl) {
-        __syncthreads();
-        const _Float16* src = a.kcb + ((size_t)h * G + j) * K.R * K.Nc * GS + sl * SL;  // entry (r, l) at (r Nc + l) GS
-        for (int i = tid; i < K.R * K.Nc * (SL / 8); i += kThreads) {
-          const int rl = i / (SL / 8), c8 = i % (SL / 8);
-          reinterpret_cast<uint4*>(cbs)[i] = *reinterpret_cast<const uint4*>(src + (size_t)rl * GS + c8 * 8);
-        }
-        __syncthreads();
-#pragma unroll 1
-        for (int t = 0; t < TPT; ++t) {
-          const int m = m0 + tid + kThreads * t;
-          if (m < L) {
-            float kx[SL];
-#pragma unroll
-            for (int i = 0; i < SL; ++i) kx[i] = 0.f;
-            for (int r = 0; r < K.R; ++r) {
-              const int code = read_field(kbase + (size_t)m * K.bpt, r * G + j, K.bits);
-              const uint4* e = reinterpret_cast<const uint4*>(cbs + ((size_t)r * K.Nc + code) * SL);
-#pragma unroll
-              for (int v = 0; v < SL / 8; ++v) {
-                const uint4 w = e[v];
-                const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                  const half2_t xy = __builtin_bit_cast(half2_t, wd[u]);
-                  kx[8 * v + 2 * u] += (float)xy.x;
-                  kx[8 * v + 2 * u + 1] += (float)xy.y;
+  // scores; the position phases are exact (sincospi of the exact turn count)
+  // under COMMVQ_DECODE_EXACT, else from the hardware sine and cosine (turns)
+  auto scores = [&](auto exc) {
+    constexpr bool EX = decltype(exc)::value;
+    if constexpr (GS >= kWideGroup) {
+      // Wide groups (many pairs share an index): the key itself is rebuilt per
+      // 32-scalar slice of a group - every round's entries of the slice staged in
+      // LDS as fp16, summed in fp32 over the rounds - then rotated once per pair
+      // and dotted with the rotated queries. A query x codebook table per (group,
+      // round) would cost a phase and NH products per pair and round instead.
+      constexpr int SL = 32, SP = SL / 2;
+      _Float16* cbs = reinterpret_cast<_Float16*>(uni);  // [R][Nc][SL]
+      for (int j = 0; j < G; ++j) {
+        for (int sl = 0; sl < GS / SL; ++sl) {
+          __syncthreads();
+          const _Float16* src = a.kcb + ((size_t)h * G + j) * K.R * K.Nc * GS + sl * SL;  // entry (r, l) at (r Nc + l) GS
+          for (int i = tid; i < K.R * K.Nc * (SL / 8); i += kThreads) {
+            const int rl = i / (SL / 8), c8 = i % (SL / 8);
+            reinterpret_cast<uint4*>(cbs)[i] = *reinterpret_cast<const uint4*>(src + (size_t)rl * GS + c8 * 8);
+          }
+          __syncthreads();
+  #pragma unroll 1
+          for (int t = 0; t < TPT; ++t) {
+            const int m = m0 + tid + kThreads * t;
+            if (m < L) {
+              float kx[SL];
+  #pragma unroll
+              for (int i = 0; i < SL; ++i) kx[i] = 0.f;
+              for (int r = 0; r < K.R; ++r) {
+                const int code = read_field(kbase + (size_t)m * K.bpt, r * G + j, K.bits);
+                const uint4* e = reinterpret_cast<const uint4*>(cbs + ((size_t)r * K.Nc + code) * SL);
+  #pragma unroll
+                for (int v = 0; v < SL / 8; ++v) {
+                  const uint4 w = e[v];
+                  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  #pragma unroll
+                  for (int u = 0; u < 4; ++u) {
+                    const half2_t xy = __builtin_bit_cast(half2_t, wd[u]);
+                    kx[8 * v + 2 * u] += (float)xy.x;
+                    kx[8 * v + 2 * u + 1] += (float)xy.y;
+                  }
+                }
+              }
+  #pragma unroll
+              for (int pp = 0; pp < SP; ++pp) {
+                const int p = j * PP + sl * SP + pp;
+                const float2 w = (EX ? phase_exact((uint32_t)m, ph.lo[p], ph.hi[p]) : phase_hw((uint32_t)m, ph.lo[p], ph.hi[p]));
+                const float rx = kx[2 * pp] * w.x - kx[2 * pp + 1] * w.y, ry = kx[2 * pp] * w.y + kx[2 * pp + 1] * w.x;
+  #pragma unroll
+                for (int hh = 0; hh < NH; ++hh) {
+                  const float2 qv = qz[hh * P + p];
+                  s[t][hh] += qv.x * rx + qv.y * ry;  // Re(conj(q~) (R_m k))
                 }
               }
             }
-#pragma unroll
-            for (int pp = 0; pp < SP; ++pp) {
-              const int p = j * PP + sl * SP + pp;
-              const float2 w = phase_exact((uint32_t)m, ph.lo[p], ph.hi[p]);
-              const float rx = kx[2 * pp] * w.x - kx[2 * pp + 1] * w.y, ry = kx[2 * pp] * w.y + kx[2 * pp + 1] * w.x;
-#pragma unroll
+          }
+        }
+      }
+    } else {
+    for (int j = 0; j < G; ++j) {
+      for (int r = 0; r < K.R; ++r) {
+        __syncthreads();
+        const _Float16* cbp = a.kcb + ((((size_t)h * G + j) * K.R + r) * K.Nc) * GS;
+        for (int i = tid; i < NH * K.Nc * PP; i += kThreads) {
+          const int hh = i / (K.Nc * PP), rem = i % (K.Nc * PP), l = rem / PP, pp = rem % PP;
+          const float x = (float)cbp[l * GS + 2 * pp], y = (float)cbp[l * GS + 2 * pp + 1];
+          const float2 qv = qz[hh * P + j * PP + pp];
+          table[i] = make_float2(qv.x * x + qv.y * y, qv.x * y - qv.y * x);  // conj(q~) * z
+        }
+        __syncthreads();
+        const int f = r * G + j;
+  #pragma unroll
+        for (int t = 0; t < TPT; ++t) {
+          const int m = m0 + tid + kThreads * t;
+          if (m < L) {
+            const int code = read_field(kbase + (size_t)m * K.bpt, f, K.bits);
+  #pragma unroll
+            for (int pp = 0; pp < PP; ++pp) {
+              const int p = j * PP + pp;
+              const float2 w = (EX ? phase_exact((uint32_t)m, ph.lo[p], ph.hi[p]) : phase_hw((uint32_t)m, ph.lo[p], ph.hi[p]));
+  #pragma unroll
               for (int hh = 0; hh < NH; ++hh) {
-                const float2 qv = qz[hh * P + p];
-                s[t][hh] += qv.x * rx + qv.y * ry;  // Re(conj(q~) (R_m k))
+                const float2 T = table[(hh * K.Nc + code) * PP + pp];
+                s[t][hh] += T.x * w.x - T.y * w.y;
               }
             }
           }
         }
       }
     }
-  } else {
-  for (int j = 0; j < G; ++j) {
-    for (int r = 0; r < K.R; ++r) {
-      __syncthreads();
-      const _Float16* cbp = a.kcb + ((((size_t)h * G + j) * K.R + r) * K.Nc) * GS;
-      for (int i = tid; i < NH * K.Nc * PP; i += kThreads) {
-        const int hh = i / (K.Nc * PP), rem = i % (K.Nc * PP), l = rem / PP, pp = rem % PP;
-        const float x = (float)cbp[l * GS + 2 * pp], y = (float)cbp[l * GS + 2 * pp + 1];
-        const float2 qv = qz[hh * P + j * PP + pp];
-        table[i] = make_float2(qv.x * x + qv.y * y, qv.x * y - qv.y * x);  // conj(q~) * z
-      }
-      __syncthreads();
-      const int f = r * G + j;
-#pragma unroll
-      for (int t = 0; t < TPT; ++t) {
-        const int m = m0 + tid + kThreads * t;
-        if (m < L) {
-          const int code = read_field(kbase + (size_t)m * K.bpt, f, K.bits);
-#pragma unroll
-          for (int pp = 0; pp < PP; ++pp) {
-            const int p = j * PP + pp;
-            const float2 w = phase_exact((uint32_t)m, ph.lo[p], ph.hi[p]);
-#pragma unroll
-            for (int hh = 0; hh < NH; ++hh) {
-              const float2 T = table[(hh * K.Nc + code) * PP + pp];
-              s[t][hh] += T.x * w.x - T.y * w.y;
-            }
-          }
-        }
-      }
     }
-  }
-  }
+
+  };
+  if (a.exact_phase)
+    scores(std::true_type{});
+  else
+    scores(std::false_type{});
 
   // softmax over the chunk
   float M[NH], lsum[NH];
