@@ -29,10 +29,13 @@
 namespace commvq {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kGenericTPT = 4;  // tokens per lane in the generic kernel
-constexpr int kHistShift = 20;  // fixed-point weights: w * 2^20 (chunk <= 1024 keeps sums < 2^31)
+constexpr int kGenericChunk = 1024;  // positions per workgroup of the generic kernel
 constexpr int kWideGroup = 32;  // group sizes from which keys are rebuilt per slice instead of tabled
+// lanes per workgroup: 1024 (one position each) for wide groups and up to 4
+// query heads per KV head, else 512 (two positions each; 8 query heads do not
+// fit 128 registers per lane, and the table path measured slower at 1024)
+__host__ __device__ constexpr int generic_threads(int nh, int gs) { return (gs >= kWideGroup && nh <= 4) ? 1024 : 512; }
+constexpr int kHistShift = 20;  // fixed-point weights: w * 2^20 (chunk <= 1024 keeps sums < 2^31)
 constexpr int kBitSub = 128;    // binary value codes: positions whose bit rows are staged in LDS at a time
 
 __device__ __forceinline__ int read_field(const uint8_t* rec, int f, int bits) {
@@ -43,9 +46,10 @@ __device__ __forceinline__ int read_field(const uint8_t* rec, int f, int bits) {
 }
 
 template <int NH, int GS, bool BITV>
-__global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, PhaseTable ph) {
+__global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel(DecodeArgs a, PhaseTable ph) {
+  constexpr int kThreads = generic_threads(NH, GS);
   constexpr int PP = GS / 2;
-  constexpr int TPT = kGenericTPT;
+  constexpr int TPT = kGenericChunk / kThreads;
   constexpr int NW = kThreads / 64;
   extern __shared__ float4 dec_smem4[];
   float* sm = reinterpret_cast<float*>(dec_smem4);
@@ -114,8 +118,8 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeArgs a, 
             reinterpret_cast<uint4*>(cbs)[i] = *reinterpret_cast<const uint4*>(src + (size_t)rl * GS + c8 * 8);
           }
           __syncthreads();
-  #pragma unroll 1
-          for (int t = 0; t < TPT; ++t) {
+#pragma unroll
+          for (int t = 0; t < TPT; ++t) {  // (unrolled: s[t] stays in registers)
             const int m = m0 + tid + kThreads * t;
             if (m < L) {
               float kx[SL];
@@ -358,7 +362,7 @@ hipError_t launch_generic(const DecodeArgs& a, const PhaseTable& ph, hipStream_t
   static std::atomic<uint64_t> configured{0};
   hipError_t e = allow_full_lds(reinterpret_cast<const void*>(&decode_generic_kernel<NH, GS, BITV>), configured);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_generic_kernel<NH, GS, BITV>), dim3(a.n_chunks * a.k.Hkv, a.B), dim3(kThreads), smem,
+  hipLaunchKernelGGL((decode_generic_kernel<NH, GS, BITV>), dim3(a.n_chunks * a.k.Hkv, a.B), dim3(generic_threads(NH, GS)), smem,
                      stream, a, ph);
   return hipGetLastError();
 }
@@ -394,9 +398,9 @@ size_t decode_bitv_smem(const CbShape& k, int nbits, int NH) {
   // the score phase's staging, or the weights [NH][chunk], u [NH][nbits] and
   // kBitSub positions' bit rows
   const size_t score = decode_generic_smem(k, k, NH);
-  const int P = k.D / 2, NW = kThreads / 64;
+  const int P = k.D / 2, NW = generic_threads(NH, k.g) / 64;
   const size_t fixed = (2 * NH * P + NH * k.D + ((NH * (NW > 2 ? NW : 2) + 2 * NH + 4) & ~3)) * sizeof(float);
-  const size_t bitv = fixed + ((size_t)NH * kThreads * kGenericTPT + (size_t)NH * nbits) * sizeof(float) +
+  const size_t bitv = fixed + ((size_t)NH * kGenericChunk + (size_t)NH * nbits) * sizeof(float) +
                       (size_t)kBitSub * (nbits / 8);
   return score > bitv ? score : bitv;
 }
@@ -404,7 +408,7 @@ size_t decode_bitv_smem(const CbShape& k, int nbits, int NH) {
 size_t decode_generic_smem(const CbShape& k, const CbShape& v, int NH) {
   // rotated queries (float2 per pair), output accumulators, reductions, then
   // the query x codebook table of one (group, round) or a value histogram
-  const int P = k.D / 2, NW = kThreads / 64;
+  const int P = k.D / 2, NW = generic_threads(NH, k.g) / 64;
   const size_t table_bytes = k.g >= kWideGroup ? (size_t)k.R * k.Nc * 32 * sizeof(_Float16)  // one slice, all rounds
                                                : (size_t)NH * k.Nc * (k.g / 2) * sizeof(float2);
   const size_t hist_bytes = (size_t)NH * v.Nc * sizeof(uint32_t);
@@ -418,7 +422,7 @@ bool decode_fast_path(const CbShape& k, const CbShape& v, int NH, int flags) {
 }
 
 int decode_chunk_len(const CbShape& k, const CbShape& v, int B, int Hq, int max_len, int flags) {
-  if (!decode_fast_path(k, v, Hq / k.Hkv, flags)) return kThreads * kGenericTPT;
+  if (!decode_fast_path(k, v, Hq / k.Hkv, flags)) return kGenericChunk;
   // the longest chunk that still gives every compute unit a workgroup
   for (int c : {4096, 2048}) {
     const long long wgs = (long long)B * k.Hkv * ((max_len + c - 1) / c);
@@ -444,7 +448,7 @@ hipError_t launch_decode_generic(const DecodeArgs& a, const PhaseTable& ph, hipS
 }
 
 hipError_t launch_decode_bitv(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream) {
-  if (a.nbits < 32 || a.nbits > 2048 || (a.nbits & (a.nbits - 1)) || a.chunk != kThreads * kGenericTPT)
+  if (a.nbits < 32 || a.nbits > 2048 || (a.nbits & (a.nbits - 1)) || a.chunk != kGenericChunk)
     return hipErrorInvalidValue;
   return launch_generic_all<true>(a, ph, stream);
 }
