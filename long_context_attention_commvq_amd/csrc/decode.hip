@@ -45,6 +45,13 @@ __device__ __forceinline__ int read_field(const uint8_t* rec, int f, int bits) {
   return (int)((v >> sh) & ((1u << bits) - 1u));
 }
 
+// Value rounds per histogram pass of the generic kernel: all R where NH x R x Nc'
+// bins fit in the LDS the key table (or slice) already takes, else 1.
+__host__ __device__ inline int generic_hist_rounds(const CbShape& k, const CbShape& v, int NH) {
+  const size_t table = k.g >= kWideGroup ? (size_t)k.R * k.Nc * 32 * 2 : (size_t)NH * k.Nc * (k.g / 2) * 8;
+  return (size_t)NH * v.R * v.Nc * 4 <= table ? v.R : 1;
+}
+
 template <int NH, int GS, bool BITV>
 __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel(DecodeArgs a, PhaseTable ph) {
   constexpr int kThreads = generic_threads(NH, GS);
@@ -294,28 +301,35 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
       oacc[hh * D + d] = o;
     }
   } else {
-  // value histograms and contraction with the value codebook
+  // value histograms and contraction with the value codebook: RB rounds of a
+  // group per pass (all of them where their histograms fit the table's LDS),
+  // bins [head][round][code]
+  const int RB = generic_hist_rounds(K, V, NH);
+  const int NBIN = RB * V.Nc;
   for (int j = 0; j < G; ++j) {
-    for (int r = 0; r < V.R; ++r) {
+    for (int r = 0; r < V.R; r += RB) {
       __syncthreads();
-      for (int i = tid; i < NH * V.Nc; i += kThreads) hist[i] = 0u;
+      for (int i = tid; i < NH * NBIN; i += kThreads) hist[i] = 0u;
       __syncthreads();
-      const int f = r * G + j;
 #pragma unroll
       for (int t = 0; t < TPT; ++t) {
         const int m = m0 + tid + kThreads * t;
         if (m < L) {
-          const int code = read_field(vbase + (size_t)m * V.bpt, f, V.bits);
+          uint32_t fx[NH];
 #pragma unroll
-          for (int hh = 0; hh < NH; ++hh) {
-            const uint32_t fx = (uint32_t)fmaf(s[t][hh], (float)(1 << kHistShift), 0.5f);
-            atomicAdd(&hist[hh * V.Nc + code], fx);
+          for (int hh = 0; hh < NH; ++hh) fx[hh] = (uint32_t)fmaf(s[t][hh], (float)(1 << kHistShift), 0.5f);
+          for (int rr = 0; rr < RB; ++rr) {
+            const int code = read_field(vbase + (size_t)m * V.bpt, (r + rr) * G + j, V.bits);
+#pragma unroll
+            for (int hh = 0; hh < NH; ++hh) atomicAdd(&hist[hh * NBIN + rr * V.Nc + code], fx[hh]);
           }
         }
       }
       __syncthreads();
+      // the pass's rounds of group j are consecutive in the codebook: bin b
+      // (round r + b / Nc, code b % Nc) at cvp[b * GS]
       const _Float16* cvp = a.vcb + ((((size_t)h * G + j) * V.R + r) * V.Nc) * GS;
-      // NO outputs (head, scalar), each a sum over the Nc bins split over PARTS
+      // NO outputs (head, scalar), each a sum over the NBIN bins split over PARTS
       // lanes of one wavefront and added with shuffles
       constexpr int NO = NH * GS;
       constexpr int PARTS = NO >= kThreads ? 1 : (kThreads / NO > 64 ? 64 : kThreads / NO);
@@ -323,7 +337,7 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
         for (int i = tid; i < NO; i += kThreads) {
           const int hh = i / GS, e = i % GS;
           float acc = 0.f;
-          for (int l = 0; l < V.Nc; ++l) acc = fmaf((float)hist[hh * V.Nc + l], (float)cvp[l * GS + e], acc);
+          for (int l = 0; l < NBIN; ++l) acc = fmaf((float)hist[hh * NBIN + l], (float)cvp[l * GS + e], acc);
           oacc[hh * D + j * GS + e] += acc * (1.0f / (float)(1 << kHistShift));
         }
       } else {
@@ -331,7 +345,7 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
         if (o < NO) {  // whole groups of PARTS lanes
           const int hh = o / GS, e = o % GS;
           float acc = 0.f;
-          for (int l = part; l < V.Nc; l += PARTS) acc = fmaf((float)hist[hh * V.Nc + l], (float)cvp[l * GS + e], acc);
+          for (int l = part; l < NBIN; l += PARTS) acc = fmaf((float)hist[hh * NBIN + l], (float)cvp[l * GS + e], acc);
 #pragma unroll
           for (int off = PARTS / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
           if (part == 0) oacc[hh * D + j * GS + e] += acc * (1.0f / (float)(1 << kHistShift));
@@ -411,7 +425,7 @@ size_t decode_generic_smem(const CbShape& k, const CbShape& v, int NH) {
   const int P = k.D / 2, NW = generic_threads(NH, k.g) / 64;
   const size_t table_bytes = k.g >= kWideGroup ? (size_t)k.R * k.Nc * 32 * sizeof(_Float16)  // one slice, all rounds
                                                : (size_t)NH * k.Nc * (k.g / 2) * sizeof(float2);
-  const size_t hist_bytes = (size_t)NH * v.Nc * sizeof(uint32_t);
+  const size_t hist_bytes = (size_t)NH * generic_hist_rounds(k, v, NH) * v.Nc * sizeof(uint32_t);
   return (2 * NH * P + NH * k.D + ((NH * (NW > 2 ? NW : 2) + 2 * NH + 4) & ~3)) * sizeof(float) +
          (table_bytes > hist_bytes ? table_bytes : hist_bytes);
 }
