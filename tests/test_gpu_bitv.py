@@ -149,3 +149,65 @@ def test_bit_value_decode_full_size_128k_sampled():
         err = row_errors(got[0, h * rep:(h + 1) * rep], ref)
         print(f"[bit values full size] head {h} max row rel err {err.max():.3e}", flush=True)
         assert err.max() <= ATTN_TOL
+
+
+def test_bit_value_fast_path_graph_replay():
+    """Fast-path binary-value calls recorded into one HIP graph give the eager
+    result bit for bit on every replay, with eager work between replays (its
+    three kernels use no atomics, no memset, and no initialised workspace)."""
+    B, Hq, Hkv, D, g, Nc, R, nb, L = 1, 32, 8, 128, 8, 256, 1, 1024, 5000
+    rng = np.random.default_rng(9400)
+    kcb = synth.codebook(9401, Hkv, D, g, Nc, R)
+    kp = dev(rng.integers(0, 256, size=(B, Hkv, L, 16), dtype=np.uint8))
+    vb = dev(rng.integers(0, 256, size=(B, L, nb // 8), dtype=np.uint8))
+    rows = dev(bit_rows(9402, nb, Hkv * D))
+    kq = api.Quantizer(dev(kcb), g)
+    qs = [dev(synth.queries(9403 + i, B, Hq, D)) for i in range(2)]
+    lens = dev(np.array([L - 3], dtype=np.int32))
+    qpos = lens - 1
+    ws = api.BitvWorkspace(kq, nb, Hkv * D, B, Hq, L, DEV)
+    outs = [torch.empty((B, Hq, D), dtype=torch.float32, device=DEV) for _ in range(2)]
+    for i in range(2):
+        api.decode_attention_bitv(kq, rows, qs[i], qpos, kp, vb, lens, L, 500000.0, out=outs[i], workspace=ws)
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(2):
+            api.decode_attention_bitv(kq, rows, qs[i], qpos, kp, vb, lens, L, 500000.0, out=outs[i], workspace=ws)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        other = api.decode_attention_bitv(kq, rows, qs[rep % 2], qpos, kp, vb, lens, L, 500000.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i], eager[i]), (rep, i)
+        assert torch.equal(other, eager[rep % 2])
+
+
+def test_bit_value_fast_path_batch_two_long():
+    """Two sequences of 40,000 and 33,001 positions on the fast path (chunks of
+    2048, a ragged last chunk each, 1024-bit codes): every query head of one
+    KV head per sequence against the oracle."""
+    B, Hq, Hkv, D, g, Nc, R, nb, Lmax = 2, 32, 8, 128, 8, 256, 1, 1024, 40000
+    rep = Hq // Hkv
+    rng = np.random.default_rng(9500)
+    kcb = synth.codebook(9501, Hkv, D, g, Nc, R)
+    kp = rng.integers(0, 256, size=(B, Hkv, Lmax, 16), dtype=np.uint8)
+    vbits = rng.integers(0, 256, size=(B, Lmax, nb // 8), dtype=np.uint8)
+    rows = bit_rows(9502, nb, Hkv * D)
+    q = synth.queries(9503, B, Hq, D)
+    lens = np.array([40000, 33001], dtype=np.int32)
+    kq = api.Quantizer(dev(kcb), g)
+    out = api.decode_attention_bitv(kq, dev(rows), dev(q), dev(lens - 1), dev(kp), dev(vbits), dev(lens), Lmax, 500000.0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b, h in ((0, 3), (1, 6)):
+        ref = O.decode_attention_bit_values(q[b:b + 1, h * rep:(h + 1) * rep], lens[b:b + 1] - 1, kp[b:b + 1, h:h + 1],
+                                            vbits[b:b + 1], lens[b:b + 1], kcb[h:h + 1], rows[:, h * D:(h + 1) * D],
+                                            500000.0)[0]
+        err = row_errors(got[b, h * rep:(h + 1) * rep], ref)
+        print(f"[bit values B2] sequence {b} head {h} max row rel err {err.max():.3e}", flush=True)
+        assert err.max() <= ATTN_TOL
