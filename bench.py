@@ -579,7 +579,7 @@ def bench_bitv(args):
                      "unit": "GB/s", "frac": bitv_bytes / (t_bitv * 1e-6) / 1e9 / HBM_PEAK_GBS, "traffic": None,
                      "bytes_per_launch": bitv_bytes, "avg_launch_us": t_bitv,
                      "kernel": "commvq_decode_attention_bitv call: fast decode kernel (scores, softmax, weights), "
-                               "bitv_values_kernel, chunk-merge kernel"},
+                               "bitv_values_kernel, bitv_merge_kernel"},
         "cpu_baseline": None if args.no_cpu else decode_cpu_baseline(args.cpu_seconds, w, np.full(B, Lmax),
                                                                      value_bits=nb),
     }

@@ -231,8 +231,9 @@ int64_t commvq_decode_bitv_workspace_bytes(int32_t batch, int32_t n_q_heads, int
  * Paths: on the fast kernel's key shapes (D 128, g 8, Nc' 256, R 1 or 2, four
  * query heads per KV head), n_bits >= 128, n_q_heads <= 32 and flags 0, the
  * fast kernel computes the scores and softmax and writes fp16 weights, and a
- * second kernel forms u on the matrix cores (fp16 weights times the 0/1 bits,
- * fp32 sums) and u^T C in fp32, per chunk and range of 128 bits. Otherwise
+ * second kernel forms u per chunk and range of 128 bits on the matrix cores
+ * (fp16 weights times the 0/1 bits, fp32 sums); a third combines the chunks
+ * on u and forms u^T C in fp32 per query head. Otherwise
  * the generic kernel runs (fp32 table or rebuilt keys, phases as above; shapes as
  * commvq_decode_attention's generic path). vcb->dim must equal Hkv * D (else
  * COMMVQ_ERR_INVALID_ARG). */

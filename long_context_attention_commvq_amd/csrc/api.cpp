@@ -701,10 +701,11 @@ int32_t commvq_decode_attention_bitv(const commvq_codebook* kcb, const commvq_bi
     a.n_chunks *= nb / 128;
     e = commvq::launch_decode_fast_bitv_scores(a, pc.ph, s);
     if (e == hipSuccess) e = commvq::launch_bitv_values(a, s);
+    if (e == hipSuccess) e = commvq::launch_bitv_merge(a, s);
   } else {
     e = commvq::launch_decode_bitv(a, pc.ph, s);
+    if (e == hipSuccess) e = commvq::launch_decode_merge(a, s);
   }
-  if (e == hipSuccess) e = commvq::launch_decode_merge(a, s);
   return hip_status(e, "commvq_decode_attention_bitv launch");
 }
 

@@ -147,13 +147,16 @@ hipError_t launch_decode_bitv(const DecodeArgs& a, const PhaseTable& ph, hipStre
 // Binary value codes on the fast kernel's shapes (and nbits a multiple of 128,
 // Hq <= 32): the fast kernel's scores and softmax write the weights a.pw and
 // each chunk's (M, l); bitv_values_kernel forms each (chunk, 128-bit range)'s
-// o on the matrix cores. a.n_chunks counts partial slots: chunks x nbits / 128.
+// u on the matrix cores; bitv_merge_kernel combines the chunks and forms u^T C.
+// a.n_chunks counts partial slots: chunks x nbits / 128.
 bool decode_bitv_fast_path(const CbShape& k, int nbits, int Hq, int flags);
 size_t decode_bitv_workspace_bytes(const CbShape& k, int nbits, int B, int Hq, int max_len);  // either path
 // byte offset of the weights in the fast path's workspace (after the partials)
 size_t decode_bitv_pw_offset(const CbShape& k, int nbits, int B, int Hq, int max_len, int chunk);
 hipError_t launch_decode_fast_bitv_scores(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream);
 hipError_t launch_bitv_values(const DecodeArgs& a, hipStream_t stream);
+// the fast path's merge: chunks combined on u per (query head, sequence), then u^T C into a.out
+hipError_t launch_bitv_merge(const DecodeArgs& a, hipStream_t stream);
 size_t decode_workspace_bytes(const CbShape& k, int B, int Hq, int max_len, int chunk);
 // Byte offset of the new-token area in the workspace (after the partials, 256-aligned).
 size_t decode_newtok_offset(const CbShape& k, int B, int Hq, int max_len, int chunk);

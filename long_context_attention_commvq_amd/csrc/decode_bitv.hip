@@ -20,14 +20,13 @@
 //     bytes: a rotate puts the lane's bit n of each half-word at bits 14 and
 //     30, and a byte permute plus a mask makes each fp16 pair 2.0 or 0, so one
 //     operand dword costs two instructions;
-//   - the eight wavefronts' u are added through LDS, then thread (KV head,
-//     dimension pair) forms o = u^T C over the range's 128 rows of C (fp32),
-//     for the KV head's query heads, into the range's partial slot;
+//   - the eight wavefronts' u are added through LDS and written to the
+//     (chunk, range) partial slot;
 //   - the grid puts range r of chunk c at r * chunks + c; workgroups go to the
 //     8 XCDs round-robin, so with a multiple of 8 chunks a chunk's ranges share
 //     one XCD and its L2 copy of the chunk's weights.
-// The merge kernel then combines the slots like any chunk partials (M equal
-// across a chunk's ranges, l in the first only).
+// bitv_merge_kernel then combines the chunks on u (per query head) and forms
+// o = u^T C once, in fp32.
 
 #include "decode_common.hpp"
 
@@ -38,7 +37,6 @@ constexpr int kBvThreads = 512;
 constexpr int kBvWaves = kBvThreads / 64;
 constexpr int kBvRange = 128;   // code bits per workgroup
 constexpr int kBvRow = 132;     // LDS row stride (floats) of the wavefront partials: 4 rows of a store hit 4 bank groups
-constexpr int kBvURow = 36;     // LDS row stride (floats) of u [bit][head], 16-byte aligned rows
 constexpr int kBvD = 128;       // head_dim of the fast path
 
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
@@ -48,12 +46,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 template <int NHT>
 __global__ __launch_bounds__(kBvThreads, 1) void bitv_values_kernel(DecodeArgs a) {
   constexpr int HP = 16 * NHT;
-  // region 0, in turn: the wavefront partials of u [w][head][bit]; the
-  // contraction's partial outputs [row quarter][head][dim]
-  constexpr int R0 = kBvWaves * 32 * kBvRow * 4;
-  static_assert(4 * 32 * kBvD * 4 <= R0, "region 0");
+  // the wavefront partials of u [w][head][bit]
+  constexpr int R0 = kBvWaves * HP * kBvRow * 4;
   __shared__ __attribute__((aligned(16))) char r0[R0];
-  __shared__ float ub[kBvRange * kBvURow];  // u [bit][head]
   float* usum = reinterpret_cast<float*>(r0);
   const int NR = a.nbits / kBvRange;
   const int npc = a.n_chunks / NR;
@@ -138,67 +133,118 @@ __global__ __launch_bounds__(kBvThreads, 1) void bitv_values_kernel(DecodeArgs a
       for (int i = 0; i < 4; ++i) usum[(wave * HP + 16 * ht + 4 * kg + i) * kBvRow + 16 * t + n] = acc[ht][t][i];
 
   __syncthreads();
-  // contraction operands, requested before the reduction (after the barrier,
-  // so they do not share registers with the partials): thread (KV head kv, row
-  // quarter qq, dimensions 8 d8 .. 8 d8 + 7) takes rows 32 qq .. 32 qq + 31 of
-  // the range
-  const int kv = tid >> 6, qq = (tid >> 4) & 3, d8 = tid & 15;
-  const int dimc = a.k.Hkv * kBvD;
-  const bool kv_ok = kv < a.k.Hkv;
-  const _Float16* crow = a.vrows + (size_t)(kBvRange * r + 32 * qq) * dimc + (kv_ok ? kv : 0) * kBvD + 8 * d8;
-  // four batches of 8 rows, each requested one batch ahead of its use (the
-  // first before the reduction)
-  h8_t cvb[2][8];
-  auto load_rows = [&](h8_t (&dst)[8], int i0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = *reinterpret_cast<const h8_t*>(crow + (size_t)(i0 + i) * dimc);
-  };
-  load_rows(cvb[0], 0);
-  for (int e = tid; e < HP * kBvRange; e += kBvThreads) {
+  // the slot's u (added over the wavefronts), bits in order
+  float* pr = a.part + (((size_t)b * a.Hq) * a.n_chunks + (size_t)c * NR + r) * (kBvD + 2) + 2;
+  for (int e = tid; e < a.Hq * kBvRange; e += kBvThreads) {
     const int head = e / kBvRange, bit = e % kBvRange;
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < kBvWaves; ++w) sum += usum[(w * HP + head) * kBvRow + bit];
-    ub[bit * kBvURow + head] = 0.5f * sum;  // the bits entered as 2.0
+    pr[(size_t)head * a.n_chunks * (kBvD + 2) + bit] = 0.5f * sum;  // the bits entered as 2.0
   }
-  __syncthreads();
+}
 
-  // o[4 kv + k][d] over the quarter's rows: sum_i u[4 kv + k][i] C[128 r + i][kv D + d]
-  float o[4][8];
+// Merge and contraction, one workgroup (1024 lanes) per (query head, sequence):
+//   M = max_c M_c, L = sum_c e^{M_c - M} l_c,
+//   U[128 r + i] = sum_c e^{M_c - M} u_{c,r}[i],   o = U^T C[:, kv D .. kv D + D) / L,
+// the chunks' softmax partials combined on u (linear in the weights), so the
+// rows of C meet one u per query head instead of one per chunk and range.
+constexpr int kBmThreads = 1024;
+__global__ __launch_bounds__(kBmThreads) void bitv_merge_kernel(DecodeArgs a) {
+  __shared__ float U[2048];
+  __shared__ float wsh[kBmThreads];
+  __shared__ float red[2][kBmThreads / 64];
+  __shared__ float2 osum[kBmThreads / 64][kBvD / 2];
+  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int NR = a.nbits / kBvRange, npc = a.n_chunks / NR;
+  constexpr size_t cs = kBvD + 2;
+  const float* pr = a.part + ((size_t)b * a.Hq + hq) * a.n_chunks * cs;
+  // the rows of C this lane contracts, requested first: lane (part p, pair dp)
+  // takes dimensions 2 dp, 2 dp + 1 of rows p * nbits / 16 ...
+  const int dp = tid % (kBvD / 2), p = tid / (kBvD / 2);
+  const int kv = hq / a.NH, dimc = a.k.Hkv * kBvD;
+  const int rows = a.nbits / (kBmThreads / (kBvD / 2));  // 8 .. 128 rows per part
+  const half2_t* col = reinterpret_cast<const half2_t*>(a.vrows + (size_t)(p * rows) * dimc + (size_t)kv * kBvD + 2 * dp);
+  // rows in batches of 64 (the first requested here; 2048-bit codes have two)
+  half2_t cv[64];
+  auto load_batch = [&](int i0) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[k][e] = 0.f;
-#pragma unroll
-  for (int bt = 0; bt < 4; ++bt) {
-    if (bt < 3) load_rows(cvb[(bt + 1) & 1], 8 * (bt + 1));
-    const h8_t (&cvh)[8] = cvb[bt & 1];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4_t u4 = *reinterpret_cast<const float4_t*>(ub + (32 * qq + 8 * bt + i) * kBvURow + 4 * (kv_ok ? kv : 0));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float cf = (float)cvh[i][e];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) o[k][e] = fmaf(u4[k], cf, o[k][e]);
-      }
-    }
-  }
-  float* osum = reinterpret_cast<float*>(r0);  // [quarter][head][dim] (u's partials are consumed)
-  if (kv_ok) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float* dst = osum + (qq * 32 + 4 * kv + k) * kBvD + 8 * d8;
-      *reinterpret_cast<float4_t*>(dst) = (float4_t){o[k][0], o[k][1], o[k][2], o[k][3]};
-      *reinterpret_cast<float4_t*>(dst + 4) = (float4_t){o[k][4], o[k][5], o[k][6], o[k][7]};
-    }
-  }
+    for (int i = 0; i < 64; ++i)
+      if (i0 + i < rows) cv[i] = col[(size_t)(i0 + i) * (dimc / 2)];
+  };
+  load_batch(0);
+  // M = max_c M_c; the lane's chunk of the first kBmThreads keeps its (M_c, l_c)
+  const float m_first = tid < npc ? pr[(size_t)tid * NR * cs] : -INFINITY;
+  const float l_first = tid < npc ? pr[(size_t)tid * NR * cs + 1] : 0.f;
+  float mx = m_first;
+  for (int c = tid + kBmThreads; c < npc; c += kBmThreads) mx = fmaxf(mx, pr[(size_t)c * NR * cs]);
+  mx = wave_max(mx);
+  if (lane == 0) red[0][wave] = mx;
   __syncthreads();
-  for (int e = tid; e < a.Hq * kBvD; e += kBvThreads) {
-    const int hq = e / kBvD, d = e % kBvD;
-    const float v = osum[hq * kBvD + d] + osum[(32 + hq) * kBvD + d] + osum[(64 + hq) * kBvD + d] +
-                    osum[(96 + hq) * kBvD + d];
-    a.part[(((size_t)b * a.Hq + hq) * a.n_chunks + (size_t)c * NR + r) * (kBvD + 2) + 2 + d] = v;
+  float M = red[0][0];
+#pragma unroll
+  for (int w = 1; w < kBmThreads / 64; ++w) M = fmaxf(M, red[0][w]);
+  // U[i] = sum_c w_c u_c[i], w_c = e^{M_c - M} (0 for an empty chunk, whose
+  // slots hold zeros), chunks taken kBmThreads at a time, their weights in LDS
+  float ls = 0.f, acc0 = 0.f, acc1 = 0.f;
+  const int i0 = tid, i1 = tid + kBmThreads;  // the lane's bits (nbits <= 2048)
+  for (int c0 = 0; c0 < npc; c0 += kBmThreads) {
+    __syncthreads();
+    {
+      const int c = c0 + tid;
+      float w = 0.f;
+      if (c < npc) {
+        const float mc = c0 == 0 ? m_first : pr[(size_t)c * NR * cs];
+        if (mc > -INFINITY) {
+          w = __expf(mc - M);
+          ls = fmaf(w, c0 == 0 ? l_first : pr[(size_t)c * NR * cs + 1], ls);
+        }
+      }
+      wsh[tid] = w;
+    }
+    __syncthreads();
+    const int nc = min(kBmThreads, npc - c0);
+    auto sweep = [&](int i, float& acc) {
+      const int r = i / kBvRange, bit = i % kBvRange;
+      const float* q = pr + ((size_t)c0 * NR + r) * cs + 2 + bit;
+      for (int k0 = 0; k0 < nc; k0 += 16) {
+        float uv[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) uv[k] = k0 + k < nc ? q[(size_t)(k0 + k) * NR * cs] : 0.f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) acc = fmaf(k0 + k < nc ? wsh[k0 + k] : 0.f, uv[k], acc);
+      }
+    };
+    if (i0 < a.nbits) sweep(i0, acc0);
+    if (i1 < a.nbits) sweep(i1, acc1);
+  }
+  if (i0 < a.nbits) U[i0] = acc0;
+  if (i1 < a.nbits) U[i1] = acc1;
+  ls = wave_sum(ls);
+  if (lane == 0) red[1][wave] = ls;
+  __syncthreads();
+  float Ls = 0.f;
+#pragma unroll
+  for (int w = 0; w < kBmThreads / 64; ++w) Ls += red[1][w];
+  // o = U^T C / L over this lane's rows, then the 16 parts added
+  float o0 = 0.f, o1 = 0.f;
+  for (int i0 = 0; i0 < rows; i0 += 64) {
+    if (i0 > 0) load_batch(i0);
+#pragma unroll
+    for (int i = 0; i < 64; ++i)
+      if (i0 + i < rows) {
+        const float u = U[p * rows + i0 + i];
+        o0 = fmaf(u, (float)cv[i].x, o0);
+        o1 = fmaf(u, (float)cv[i].y, o1);
+      }
+  }
+  osum[p][dp] = make_float2(o0, o1);
+  __syncthreads();
+  if (tid < kBvD) {
+    float o = 0.f;
+#pragma unroll
+    for (int q = 0; q < kBmThreads / 64; ++q) o += (tid & 1) ? osum[q][tid >> 1].y : osum[q][tid >> 1].x;
+    a.out[((size_t)b * a.Hq + hq) * kBvD + tid] = Ls > 0.f ? o / Ls : 0.f;
   }
 }
 
@@ -223,6 +269,13 @@ size_t decode_bitv_workspace_bytes(const CbShape& k, int nbits, int B, int Hq, i
   const size_t plen = (size_t)(max_len + chunk - 1) / chunk * chunk;
   const size_t fast = decode_bitv_pw_offset(k, nbits, B, Hq, max_len, chunk) + ((size_t)B * Hq * plen * 2 + 255) / 256 * 256;
   return fast > generic ? fast : generic;
+}
+
+hipError_t launch_bitv_merge(const DecodeArgs& a, hipStream_t stream) {
+  if (a.k.D != kBvD || a.nbits < kBvRange || a.nbits > 2048 || a.nbits % kBvRange || a.n_chunks % (a.nbits / kBvRange))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bitv_merge_kernel, dim3(a.Hq, a.B), dim3(kBmThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_bitv_values(const DecodeArgs& a, hipStream_t stream) {

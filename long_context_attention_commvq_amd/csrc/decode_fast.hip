@@ -189,8 +189,8 @@ __device__ __forceinline__ int search_row64_dot(const half2_t (&e2)[4], const h8
 // BV: binary value codes (a.vbits). The workgroup then stops after the
 // softmax: it writes its positions' weights e^{s - M} (fp16, a.pw) and the
 // chunk's (M, l) into each of its nbits / 128 partial slots (one per range of
-// value-code bits; l in the first only), and bitv_values_kernel adds each
-// range's o.
+// value-code bits; l in the first only); bitv_values_kernel adds each range's
+// u.
 template <int R, int TL, bool BV>
 __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseTable ph) {
   using Cfg = FastCfg<R>;
