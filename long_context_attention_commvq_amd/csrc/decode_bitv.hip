@@ -93,16 +93,12 @@ __global__ __launch_bounds__(kBvThreads, 1) void bitv_values_kernel(DecodeArgs a
   for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[ht][t] = (float4_t){0.f, 0.f, 0.f, 0.f};
-  auto step = [&](Ops& o, int ks) {
+  auto step = [&](const Ops& o) {
     uint32_t y[8][4];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) y[j][q] = __builtin_amdgcn_alignbit(o.x[j][q], o.x[j][q], rot);
-    h8_t acur[NHT];
-#pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) acur[ht] = o.a[ht];
-    if (ks + 2 * kBvWaves < nks) load(o, ks + 2 * kBvWaves);  // refill this slot two k-steps ahead
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int q = t >> 1;
@@ -113,15 +109,22 @@ __global__ __launch_bounds__(kBvThreads, 1) void bitv_values_kernel(DecodeArgs a
       const h8_t bop = __builtin_bit_cast(h8_t, bw);
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht)
-        acc[ht][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(acur[ht], bop, acc[ht][t], 0, 0, 0);
+        acc[ht][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(o.a[ht], bop, acc[ht][t], 0, 0, 0);
     }
   };
-  Ops o0, o1;
-  if (wave < nks) load(o0, wave);
-  if (wave + kBvWaves < nks) load(o1, wave + kBvWaves);
-  for (int ks = wave; ks < nks; ks += 2 * kBvWaves) {
-    step(o0, ks);
-    if (ks + kBvWaves < nks) step(o1, ks + kBvWaves);
+  // A wavefront has at most 4096 / 32 / 8 = 16 k-steps; the loop is unrolled so
+  // that the three operand slots are fixed registers (no copies between
+  // iterations): slot (kk + 2) % 3 is refilled while slot kk % 3 is used.
+  static_assert(4096 / 32 / kBvWaves == 16, "k-steps per wavefront");
+  Ops ring[3];
+  if (wave < nks) load(ring[0], wave);
+  if (wave + kBvWaves < nks) load(ring[1], wave + kBvWaves);
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk) {
+    const int ks = wave + kBvWaves * kk;
+    if (ks >= nks) break;  // (uniform in the wavefront)
+    if (ks + 2 * kBvWaves < nks) load(ring[(kk + 2) % 3], ks + 2 * kBvWaves);
+    step(ring[kk % 3]);
   }
 
   // lane holds u[16 ht + 4 kg + i][16 t + n] (times 2)
