@@ -147,7 +147,8 @@ __global__ __launch_bounds__(kBvThreads, 1) void bitv_values_kernel(DecodeArgs a
   }
 }
 
-// Merge and contraction, one workgroup (1024 lanes) per (query head, sequence):
+// Merge and contraction, one workgroup (1024 lanes) per (query head, sequence,
+// quarter of the output dimensions; each quarter's workgroup forms all of U):
 //   M = max_c M_c, L = sum_c e^{M_c - M} l_c,
 //   U[128 r + i] = sum_c e^{M_c - M} u_{c,r}[i],   o = U^T C[:, kv D .. kv D + D) / L,
 // the chunks' softmax partials combined on u (linear in the weights), so the
@@ -157,25 +158,24 @@ __global__ __launch_bounds__(kBmThreads) void bitv_merge_kernel(DecodeArgs a) {
   __shared__ float U[2048];
   __shared__ float wsh[kBmThreads];
   __shared__ float red[2][kBmThreads / 64];
-  __shared__ float2 osum[kBmThreads / 64][kBvD / 2];
-  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int DQ = kBvD / 4;             // output dimensions per workgroup
+  constexpr int NP = kBmThreads / (DQ / 2);  // parts of the rows (64)
+  __shared__ float2 osum[NP][DQ / 2];
+  const int hq = blockIdx.x, b = blockIdx.y, dq0 = blockIdx.z * DQ;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NR = a.nbits / kBvRange, npc = a.n_chunks / NR;
   constexpr size_t cs = kBvD + 2;
   const float* pr = a.part + ((size_t)b * a.Hq + hq) * a.n_chunks * cs;
   // the rows of C this lane contracts, requested first: lane (part p, pair dp)
-  // takes dimensions 2 dp, 2 dp + 1 of rows p * nbits / 16 ...
-  const int dp = tid % (kBvD / 2), p = tid / (kBvD / 2);
+  // takes dimensions dq0 + 2 dp, dq0 + 2 dp + 1 of rows p * nbits / 64 ...
+  const int dp = tid % (DQ / 2), p = tid / (DQ / 2);
   const int kv = hq / a.NH, dimc = a.k.Hkv * kBvD;
-  const int rows = a.nbits / (kBmThreads / (kBvD / 2));  // 8 .. 128 rows per part
-  const half2_t* col = reinterpret_cast<const half2_t*>(a.vrows + (size_t)(p * rows) * dimc + (size_t)kv * kBvD + 2 * dp);
-  // rows in batches of 64 (the first requested here; 2048-bit codes have two)
-  half2_t cv[64];
-  auto load_batch = [&](int i0) {
+  const int rows = a.nbits / NP;  // 2 .. 32 rows per part
+  const half2_t* col = reinterpret_cast<const half2_t*>(a.vrows + (size_t)(p * rows) * dimc + (size_t)kv * kBvD + dq0 + 2 * dp);
+  half2_t cv[32];
 #pragma unroll
-    for (int i = 0; i < 64; ++i)
-      if (i0 + i < rows) cv[i] = col[(size_t)(i0 + i) * (dimc / 2)];
-  };
-  load_batch(0);
+  for (int i = 0; i < 32; ++i)
+    if (i < rows) cv[i] = col[(size_t)i * (dimc / 2)];
   // M = max_c M_c; the lane's chunk of the first kBmThreads keeps its (M_c, l_c)
   const float m_first = tid < npc ? pr[(size_t)tid * NR * cs] : -INFINITY;
   const float l_first = tid < npc ? pr[(size_t)tid * NR * cs + 1] : 0.f;
@@ -229,25 +229,21 @@ __global__ __launch_bounds__(kBmThreads) void bitv_merge_kernel(DecodeArgs a) {
   float Ls = 0.f;
 #pragma unroll
   for (int w = 0; w < kBmThreads / 64; ++w) Ls += red[1][w];
-  // o = U^T C / L over this lane's rows, then the 16 parts added
+  // o = U^T C / L over this lane's rows, then the 64 parts added
   float o0 = 0.f, o1 = 0.f;
-  for (int i0 = 0; i0 < rows; i0 += 64) {
-    if (i0 > 0) load_batch(i0);
 #pragma unroll
-    for (int i = 0; i < 64; ++i)
-      if (i0 + i < rows) {
-        const float u = U[p * rows + i0 + i];
-        o0 = fmaf(u, (float)cv[i].x, o0);
-        o1 = fmaf(u, (float)cv[i].y, o1);
-      }
-  }
+  for (int i = 0; i < 32; ++i)
+    if (i < rows) {
+      const float u = U[p * rows + i];
+      o0 = fmaf(u, (float)cv[i].x, o0);
+      o1 = fmaf(u, (float)cv[i].y, o1);
+    }
   osum[p][dp] = make_float2(o0, o1);
   __syncthreads();
-  if (tid < kBvD) {
+  if (tid < DQ) {
     float o = 0.f;
-#pragma unroll
-    for (int q = 0; q < kBmThreads / 64; ++q) o += (tid & 1) ? osum[q][tid >> 1].y : osum[q][tid >> 1].x;
-    a.out[((size_t)b * a.Hq + hq) * kBvD + tid] = Ls > 0.f ? o / Ls : 0.f;
+    for (int q = 0; q < NP; ++q) o += (tid & 1) ? osum[q][tid >> 1].y : osum[q][tid >> 1].x;
+    a.out[((size_t)b * a.Hq + hq) * kBvD + dq0 + tid] = Ls > 0.f ? o / Ls : 0.f;
   }
 }
 
@@ -277,7 +273,7 @@ size_t decode_bitv_workspace_bytes(const CbShape& k, int nbits, int B, int Hq, i
 hipError_t launch_bitv_merge(const DecodeArgs& a, hipStream_t stream) {
   if (a.k.D != kBvD || a.nbits < kBvRange || a.nbits > 2048 || a.nbits % kBvRange || a.n_chunks % (a.nbits / kBvRange))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bitv_merge_kernel, dim3(a.Hq, a.B), dim3(kBmThreads), 0, stream, a);
+  hipLaunchKernelGGL(bitv_merge_kernel, dim3(a.Hq, a.B, 4), dim3(kBmThreads), 0, stream, a);
   return hipGetLastError();
 }
 
