@@ -71,9 +71,10 @@ def parse():
                     help="decode workload to time (default: the 128K 1-bit decode-step workload)")
     ap.add_argument("--encode", action="store_true",
                     help="time the prefill encoder instead (131072 tokens x 8 KV heads of K and V, 2-bit)")
-    ap.add_argument("--graph", action="store_true",
-                    help="capture the timed steps in one HIP graph and time its replay (the default issues each "
-                         "commvq_decode_step call from the host)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the steps issued from the host one call at a time (default: the timed steps are "
+                         "captured once in a HIP graph and its replay is timed; per-step eager event times are "
+                         "reported either way)")
     ap.add_argument("--naive", action="store_true",
                     help="time the comparison path (dequantise the codes to fp16, then dense attention) against "
                          "commvq_decode_attention on the same 128K 1-bit caches, instead of the headline step")
@@ -102,6 +103,18 @@ def copy_calibration(mib: int):
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "fp32 negate", "bytes_read_per_launch": n * 4,
                       "bytes_written_per_launch": n * 4, "launches": 5}), flush=True)
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(budget_s: float):
@@ -139,7 +152,7 @@ def cpu_baseline(budget_s: float):
             toks += L
     t_step = t_total / units * w.n_kv_heads
     L_mean = toks / units
-    return {"value": L_mean / t_step, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": L_mean / t_step, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{units} (KV head, step) units of the {WORKLOAD} workload, mean L={L_mean:.0f}, "
                       f"fp64 NumPy, BLAS threads={cores}; {t_total:.1f} s measured, "
                       f"mean unit time scaled x{w.n_kv_heads} to one 8-head step"}
@@ -185,7 +198,7 @@ def decode_cpu_baseline(budget_s: float, w, lens, value_bits: int = 0):
             units += 1
             toks += L
     kind = f"binary value codes ({value_bits} bits per token)" if value_bits else "residual value codebook"
-    return {"value": toks / t_total / w.n_kv_heads, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": toks / t_total / w.n_kv_heads, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{units} (sequence, KV head) units of the {w.name} shape ({kind}), {toks} cached positions, "
                       f"fp64 NumPy, BLAS threads={cores}; {t_total:.1f} s measured, scaled to all "
                       f"{w.n_kv_heads} KV heads of one call"}
@@ -211,7 +224,7 @@ def encode_cpu_baseline(budget_s: float, w):
             t_total += time.perf_counter() - t0
             slices += 1
     th = slices * n * w.n_kv_heads
-    return {"value": th / t_total, "unit": "token-heads/s", "cores": cores, "kind": "oracle",
+    return {"value": th / t_total, "unit": "token-heads/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{slices} slices of {n} tokens x {w.n_kv_heads} KV heads ({th} token-heads), fp64 NumPy, "
                       f"BLAS threads={cores}; {t_total:.1f} s measured"}
 
@@ -677,7 +690,7 @@ def em_cpu_baseline(budget_s: float, x, cb):
             t_total += time.perf_counter() - t0
             done += 1
     t_all = t_total / done * H * G
-    return {"value": N * H * G / t_all, "unit": "vector-groups/s", "cores": cores, "kind": "oracle",
+    return {"value": N * H * G / t_all, "unit": "vector-groups/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{done} of {H * G} (KV head, group) slices, {N} vectors each, em_step round 0 at "
                       f"temperature 0, fp64 NumPy, BLAS threads={cores}; {t_total:.1f} s measured, scaled to all slices"}
 
@@ -773,9 +786,26 @@ def main():
     for i in range(args.warmup):
         run_step(i)
     torch.cuda.synchronize()
+
+    # (1) per-step device times: every step bracketed by HIP events on its stream,
+    # all steps queued behind a spin kernel so that no host-issue gap falls inside
+    # an interval; median and p10/p90 over the K steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.0e6 + 6.0e4 * args.steps))  # ~1-2 ms of GPU time while the host queues the steps
+    evs[0].record(stream)
+    for k in range(args.steps):
+        run_step(args.warmup + k)
+        evs[k + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step_us = np.array([evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(args.steps)])
+    eager_ms_step = evs[0].elapsed_time(evs[-1]) / args.steps
+
+    # (2) the timed region: the K steps recorded once in a HIP graph (the library
+    # allocates nothing and records no memset, so a decode loop can be captured)
+    # and replayed as one launch, bracketed by events and synchronisations
     graph = None
-    if args.graph:
-        # the timed steps recorded once, replayed as one graph launch
+    if not args.eager:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             cap = torch.cuda.current_stream().cuda_stream
@@ -784,7 +814,8 @@ def main():
         torch.cuda.synchronize()
         graph.replay()  # one untimed replay
         torch.cuda.synchronize()
-    print(f"[bench] timing {args.steps} steps" + (" (one graph replay)" if graph else ""), file=sys.stderr, flush=True)
+    print(f"[bench] timing {args.steps} steps" + (" (one graph replay)" if graph else " (eager)"), file=sys.stderr,
+          flush=True)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
@@ -799,10 +830,8 @@ def main():
     t_wall = time.perf_counter() - t_wall
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
-    # one step is one commvq_decode_step call on `stream`: the fused append +
-    # attention kernel, then the chunk-merge kernel. HIP events cannot split the
-    # two inside one call, so the roofline is taken over the whole call (the
-    # merge kernel adds ~10 %; the rocprofv3 trace gives the split).
+    # one step is one commvq_decode_step call on `stream`; the roofline is taken
+    # over the whole call (the rocprofv3 trace gives its kernels' split)
     dec_avg_ms = ms_step
     # cached tokens per step and packed-code bytes per decode launch
     toks, code_bytes = 0, 0
@@ -814,8 +843,10 @@ def main():
     toks_per_step = toks / args.steps
     bytes_per_launch = code_bytes / args.steps
     achieved = bytes_per_launch / (dec_avg_ms * 1e-3) / 1e9
-    print(f"[bench] step {ms_step * 1e3:.1f} us (decode + merge kernels), host issue {t_wall / args.steps * 1e6:.1f} us/step",
-          file=sys.stderr, flush=True)
+    print(f"[bench] step {ms_step * 1e3:.2f} us ({'graph replay' if graph else 'eager'}); per-step events: median "
+          f"{np.median(per_step_us):.2f} us, p10 {np.percentile(per_step_us, 10):.2f}, p90 "
+          f"{np.percentile(per_step_us, 90):.2f}; eager queued {eager_ms_step * 1e3:.2f} us/step; host "
+          f"{t_wall / args.steps * 1e6:.1f} us/step", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu:
@@ -843,6 +874,12 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(), "traffic_unit": "bytes per launch",
                      "kernel": "commvq_decode_step call: fused append + attention kernel, then chunk-merge kernel", "bytes_per_launch": bytes_per_launch,
                      "avg_launch_us": dec_avg_ms * 1e3},
+        "step_us": {"timed": "graph replay" if graph is not None else "eager", "mean": ms_step * 1e3,
+                    "median": float(np.median(per_step_us)), "p10": float(np.percentile(per_step_us, 10)),
+                    "p90": float(np.percentile(per_step_us, 90)), "eager_queued_mean": eager_ms_step * 1e3,
+                    "per_step_source": "HIP events around each eager call, all calls queued behind a spin kernel",
+                    "cache": f"cold: {NL} layer slices rotated ({NL * 2 * B * H * Lmax * bpt_k / 2**20:.0f} MiB of "
+                             f"codes, beyond the 256 MB Infinity Cache)" if NL > 1 else "warm: one layer slice"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

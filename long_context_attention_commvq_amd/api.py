@@ -10,6 +10,34 @@ import torch
 from . import _lib
 
 
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, device, shape: tuple | None = None) -> torch.Tensor:
+    """The C ABI reads raw pointers: check what it cannot (dtype, device, shape)
+    and hand it a contiguous tensor."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != torch.device(device):
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.contiguous()
+
+
+def _need_cache(t: torch.Tensor, name: str, quant: "Quantizer", batch: int, device) -> torch.Tensor:
+    """A packed cache: uint8 [B, Hkv, Lmax, bytes_per_token], contiguous (written in place, so never copied)."""
+    if t.dtype != torch.uint8 or t.dim() != 4:
+        raise TypeError(f"{name} must be uint8 [B, Hkv, Lmax, bytes_per_token]")
+    if t.device != torch.device(device):
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.shape[0] != batch or t.shape[1] != quant.n_kv_heads or t.shape[3] != quant.bytes_per_token:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}; expected [{batch}, {quant.n_kv_heads}, Lmax, "
+                         f"{quant.bytes_per_token}]")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (it is read and written in place)")
+    return t
+
+
 class Quantizer:
     """One residual codebook (keys or values) living on the GPU.
 
@@ -59,7 +87,11 @@ def encode_into_cache(quant: Quantizer, x: torch.Tensor, cache: torch.Tensor, b:
 def append(quant: Quantizer, x: torch.Tensor, positions: torch.Tensor, cache: torch.Tensor) -> None:
     """x fp16 [B, Hkv, D], positions int32 [B] (device) -> cache[b, :, positions[b]]."""
     B = x.shape[0]
-    _lib.commvq_append(quant.desc, x.contiguous(), B, positions, cache, cache.shape[2])
+    dev = x.device
+    x = _need(x, "x", torch.float16, dev, (B, quant.n_kv_heads, quant.head_dim))
+    positions = _need(positions, "positions", torch.int32, dev, (B,))
+    cache = _need_cache(cache, "cache", quant, B, dev)
+    _lib.commvq_append(quant.desc, x, B, positions, cache, cache.shape[2])
 
 
 class DecodeWorkspace:
@@ -80,6 +112,16 @@ def decode_attention(kq: Quantizer, vq: Quantizer, q: torch.Tensor, q_pos: torch
                      workspace: DecodeWorkspace | None = None, exact: bool = False) -> torch.Tensor:
     """q fp32 [B, Hq, D] -> out fp32 [B, Hq, D] over packed caches [B, Hkv, Lmax, bpt]."""
     B, Hq, D = q.shape
+    dev = q.device
+    q = _need(q, "q", torch.float32, dev, (B, Hq, kq.head_dim))
+    q_pos = _need(q_pos, "q_pos", torch.int32, dev, (B,))
+    seq_lens = _need(seq_lens, "seq_lens", torch.int32, dev, (B,))
+    kcache = _need_cache(kcache, "kcache", kq, B, dev)
+    vcache = _need_cache(vcache, "vcache", vq, B, dev)
+    if out is not None:
+        _need(out, "out", torch.float32, dev, (B, Hq, D))
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -100,6 +142,19 @@ def decode_step(kq: Quantizer, vq: Quantizer, k_new: torch.Tensor, v_new: torch.
                 exact: bool = False) -> torch.Tensor:
     """Append k_new/v_new fp16 [B, Hkv, D] at positions[b], then attend (one call)."""
     B, Hq, D = q.shape
+    dev = q.device
+    q = _need(q, "q", torch.float32, dev, (B, Hq, kq.head_dim))
+    k_new = _need(k_new, "k_new", torch.float16, dev, (B, kq.n_kv_heads, kq.head_dim))
+    v_new = _need(v_new, "v_new", torch.float16, dev, (B, vq.n_kv_heads, vq.head_dim))
+    positions = _need(positions, "positions", torch.int32, dev, (B,))
+    q_pos = _need(q_pos, "q_pos", torch.int32, dev, (B,))
+    seq_lens = _need(seq_lens, "seq_lens", torch.int32, dev, (B,))
+    kcache = _need_cache(kcache, "kcache", kq, B, dev)
+    vcache = _need_cache(vcache, "vcache", vq, B, dev)
+    if out is not None:
+        _need(out, "out", torch.float32, dev, (B, Hq, D))
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -107,7 +162,7 @@ def decode_step(kq: Quantizer, vq: Quantizer, k_new: torch.Tensor, v_new: torch.
     if workspace is None:
         workspace = DecodeWorkspace(kq, vq, B, Hq, max_seq_len, q.device)
     rope = _lib.make_rope(theta_base)
-    _lib.commvq_decode_step(kq.desc, vq.desc, rope, k_new.contiguous(), v_new.contiguous(), positions, q, q_pos,
+    _lib.commvq_decode_step(kq.desc, vq.desc, rope, k_new, v_new, positions, q, q_pos,
                             kcache, vcache, seq_lens, B, Hq, kcache.shape[2], max_seq_len, sm_scale, out,
                             workspace.buf, workspace.nbytes, _lib.COMMVQ_DECODE_EXACT if exact else 0)
     return out

@@ -14,8 +14,8 @@
 //   4. the weights are scattered into per-code histograms (LDS integer atomics on
 //      fixed-point weights) and the histograms are multiplied by the value
 //      codebook (review, "If this is right", fourth bullet);
-//   5. the chunk's (max, sum, unnormalised output) go to the workspace and the
-//      last workgroup to finish for (b, h) merges the chunks.
+//   5. the chunk's (max, sum, unnormalised output) go to the workspace; a second
+//      kernel (decode_merge_kernel) combines the chunks of each (b, query head).
 // This kernel keeps the table in fp32; position phases come from the hardware
 // sine and cosine of the exact turn count, or from sincospi of it in the
 // exact-precision mode (a.exact_phase). It serves every supported shape.

@@ -1,8 +1,12 @@
-// Greedy residual search of one group by one wavefront, shared by every kernel
-// that encodes few tokens (append, fused decode step) so they all pick the same
-// entries as the bulk encoder: squared distance accumulated term by term in
-// float32 with fmaf, lowest index on ties ("Pith review of CommVQ", "What
-// carries the argument": one index shared by a group, R residual rounds).
+// Greedy residual search of one group by one wavefront, shared by the kernels
+// that encode few tokens (append, the generic and two-round decode steps):
+// squared distance accumulated term by term in float32 with fmaf, lowest index
+// on ties ("Pith review of CommVQ", "What carries the argument": one index
+// shared by a group, R residual rounds). This is the fp32 bulk encoder's
+// arithmetic; the matrix-core encoder and the one-round fused decode step rank
+// entries by |c|^2/2 - e.c instead, so the paths can differ at near ties only
+// (the tests accept a differing code only when its float64 distance is within
+// 1e-5 relative of the minimum).
 #pragma once
 
 #include "commvq_internal.hpp"
@@ -40,6 +44,7 @@ __device__ __forceinline__ void greedy_group_wave(float (&e)[GS], const _Float16
         bi = oi;
       }
     }
+    if (bi == 0x7fffffff) bi = 0;  // no distance below +inf (a NaN or infinite input): entry 0
 #pragma unroll
     for (int i = 0; i < GS; ++i) e[i] -= (float)c[bi * GS + i];
     if (lane == 0) out[r * out_stride] = (uint8_t)bi;
@@ -87,6 +92,7 @@ __device__ __forceinline__ void greedy_group_row16(float (&e)[8], const _Float16
         bi = oi;
       }
     }
+    if (bi == 0x7fffffff) bi = 0;  // no distance below +inf (a NaN or infinite input): entry 0
 #pragma unroll
     for (int i = 0; i < 8; ++i) e[i] -= (float)c[bi * 8 + i];
     if (lane16 == 0) out[r * out_stride] = (uint8_t)bi;

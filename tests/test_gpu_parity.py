@@ -367,6 +367,67 @@ def test_decode_step_appends_then_attends(R, exact):
     assert err.max() <= ATTN_TOL
 
 
+def _poison(x, cells):
+    """x [N, H, D] with one scalar of each listed (token, head, scalar) set non-finite."""
+    x = x.copy()
+    for (n, h, i), val in cells:
+        x[n, h, i] = val
+    return x
+
+
+@pytest.mark.parametrize("g,Nc,R", [(8, 256, 2), (8, 256, 1), (4, 16, 3)])
+def test_non_finite_inputs_encode_to_entry_zero(g, Nc, R):
+    """A group holding a NaN or an infinity has no finite distance to any entry:
+    every encoder (few-token, fp32 bulk, matrix-core bulk, append and the fused
+    decode step) writes entry 0 for it in every round, as the oracle's argmin does,
+    and the other groups of the same tokens are encoded as usual."""
+    H, D = 2, 64 if g == 4 else 128
+    G = D // g
+    cells = [((3, 1, 5 * g + 2), np.nan), ((7, 0, 2 * g), np.inf), ((7, 1, D - 1), -np.inf)]
+    poisoned = {(3, 1, 5), (7, 0, 2), (7, 1, G - 1)}
+    cb = synth.codebook(900 + g + R, H, D, g, Nc, R)
+    q = api.Quantizer(dev(cb), g)
+    for N in (20, 300):  # few-token kernel, then the bulk (matrix-core for g 8 / Nc' 256) encoder
+        x = _poison(synth.kv(901 + N, N, H, D), cells)
+        got = gpu_encode(x, cb, Nc)
+        codes = O.unpack_codes(got, R, G, Nc)  # [N, H, R, G]
+        for n, h, j in poisoned:
+            assert np.all(codes[n, h, :, j] == 0), (N, n, h, j, codes[n, h, :, j])
+        hard, ties = check_encoding(x, cb, got, Nc)
+        assert not hard, hard[:5]
+    # append: one token per sequence
+    x = _poison(synth.kv(950, 8, H, D), cells)
+    bpt = q.bytes_per_token
+    cache = torch.zeros((8, H, 4, bpt), dtype=torch.uint8, device=DEV)
+    api.append(q, dev(x), dev(np.full(8, 2, dtype=np.int32)), cache)
+    torch.cuda.synchronize()
+    codes = O.unpack_codes(cache[:, :, 2].cpu().numpy(), R, G, Nc)
+    for n, h, j in poisoned:
+        assert np.all(codes[n, h, :, j] == 0), ("append", n, h, j)
+    if g != 8 or Nc != 256:
+        return
+    # fused decode step (R = 1: searches spread over the chunk workgroups; R = 2:
+    # the owner workgroup's 16-lane search): sequence 3's key and 7's value poisoned
+    B, Hq, Lmax = 8, 8, 2048
+    kcb, vcb = cb, synth.codebook(960 + R, H, D, g, Nc, R)
+    kq, vq = q, api.Quantizer(dev(vcb), g)
+    rng = np.random.default_rng(961)
+    kp = _pack_cache(rng.integers(0, Nc, size=(B, Lmax, H, R, G)), Nc)
+    vp = _pack_cache(rng.integers(0, Nc, size=(B, Lmax, H, R, G)), Nc)
+    k_new = _poison(synth.kv(962, B, H, D), cells[:1])
+    v_new = _poison(synth.kv(963, B, H, D), cells[1:])
+    lens = np.full(B, Lmax, dtype=np.int32)
+    positions = lens - 1
+    kd, vd = dev(kp), dev(vp)
+    out = api.decode_step(kq, vq, dev(k_new), dev(v_new), dev(positions), dev(synth.queries(964, B, Hq, D)),
+                          dev(positions), kd, vd, dev(lens), Lmax, 500000.0)
+    torch.cuda.synchronize()
+    kcodes = O.unpack_codes(kd.cpu().numpy()[:, :, Lmax - 1], R, G, Nc)
+    vcodes = O.unpack_codes(vd.cpu().numpy()[:, :, Lmax - 1], R, G, Nc)
+    assert np.all(kcodes[3, 1, :, 5] == 0) and np.all(vcodes[7, 0, :, 2] == 0) and np.all(vcodes[7, 1, :, G - 1] == 0)
+    assert np.isfinite(out.cpu().numpy()).all()  # the cached entries are finite, so is the attention
+
+
 @pytest.mark.parametrize("Lmax", [600, 1500, 4100])
 def test_decode_step_search_spread_over_few_chunks(Lmax):
     """The 1-bit decode step spreads the new token's 32 group searches over the

@@ -177,3 +177,36 @@ def test_mutant_bit_values_wrong_head_slice(monkeypatch):
     real = O.binary_values
     monkeypatch.setattr(O, "binary_values", lambda packed, rows: real(packed, rows)[..., ::-1])  # columns reversed
     _expect_fail(P.test_bit_value_attention_matches_torch_sdpa)
+
+
+def test_mutant_em_double_temperature(monkeypatch):
+    real = O.em_step
+    monkeypatch.setattr(O, "em_step", lambda x, cb, r, T, min_mass=0.0: real(x, cb, r, 2 * T, min_mass))
+    _expect_fail(lambda: P.test_em_soft_step_equals_explicit_loops(0.3, 0))
+    _expect_fail(lambda: P.test_em_soft_step_equals_explicit_loops(2.0, 1))
+
+
+def test_mutant_em_soft_weights_without_min_shift_sign(monkeypatch):
+    """exp(+(d - min d) / T): weights that grow with distance."""
+    def bad(x, codebook, round_index, temperature, min_mass=0.0):
+        cb = np.asarray(codebook, dtype=np.float64)
+        e = O.em_round_residuals(x, cb, round_index)
+        entries = cb[:, :, round_index]
+        d = O.sq_distances(e, entries[None])
+        w = np.exp((d - d.max(axis=-1, keepdims=True)) / temperature)
+        w = w / w.sum(axis=-1, keepdims=True)
+        mass = w.sum(axis=0)
+        new = np.einsum("nhgl,nhgi->hgli", w, e) / mass[..., None]
+        return new, mass
+    monkeypatch.setattr(O, "em_step", bad)
+    _expect_fail(lambda: P.test_em_soft_step_equals_explicit_loops(0.3, 0))
+
+
+def test_mutant_encode_gap_absolute(monkeypatch):
+    real = O.encode
+
+    def bad(x, codebook, chunk=256):
+        codes, gaps = real(x, codebook, chunk)
+        return codes, gaps * 0.5  # a gap off by a factor (e.g. measured on distances, not squared)
+    monkeypatch.setattr(O, "encode", bad)
+    _expect_fail(P.test_encode_gaps_equal_brute_force_top2)

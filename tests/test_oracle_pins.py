@@ -383,6 +383,79 @@ def test_em_hard_step_equals_brute_force_lloyd_step():
                 assert np.allclose(new[h, j, l], want, rtol=0, atol=1e-12)
 
 
+def _explicit_soft_em(x, cb, r, T):
+    """One soft EM iteration written as plain loops over every (vector, entry):
+    residuals by an explicit nearest-entry search of each earlier round, then
+    weights exp(-(d_l - min d) / T) / sum, masses and weighted means."""
+    N, H, D = x.shape
+    _, G, R, Nc, g = cb.shape
+    new = cb[:, :, r].copy()
+    mass = np.zeros((H, G, Nc))
+    for h in range(H):
+        for j in range(G):
+            sums = np.zeros((Nc, g))
+            for n in range(N):
+                e = [float(v) for v in x[n, h, j * g:(j + 1) * g]]
+                for rr in range(r):
+                    best, bd = 0, None
+                    for l in range(Nc):
+                        d = sum((e[i] - cb[h, j, rr, l, i]) ** 2 for i in range(g))
+                        if bd is None or d < bd:
+                            best, bd = l, d
+                    e = [e[i] - cb[h, j, rr, best, i] for i in range(g)]
+                d = [sum((e[i] - cb[h, j, r, l, i]) ** 2 for i in range(g)) for l in range(Nc)]
+                dmin = min(d)
+                w = [math.exp(-(d[l] - dmin) / T) for l in range(Nc)]
+                tot = sum(w)
+                for l in range(Nc):
+                    mass[h, j, l] += w[l] / tot
+                    for i in range(g):
+                        sums[l, i] += w[l] / tot * e[i]
+            for l in range(Nc):
+                if mass[h, j, l] > 0:
+                    new[h, j, l] = sums[l] / mass[h, j, l]
+    return new, mass
+
+
+@pytest.mark.parametrize("T,r", [(0.3, 0), (2.0, 1), (0.3, 2)])
+def test_em_soft_step_equals_explicit_loops(T, r):
+    """Finite temperature: the annealed soft E-step and the weighted-mean M-step
+    (review, "Assumptions & free parameters": soft assignment and annealing;
+    "Referee Report", Significance: closed-form update), against plain loops.
+    Unit-scale data, so a temperature off by a factor moves the weights."""
+    x, cb = _em_data(17 + r, 40, 2, 2, 3, 5, 3)
+    new, mass = O.em_step(x, cb, r, T)
+    want, wmass = _explicit_soft_em(x, cb, r, T)
+    assert np.allclose(mass, wmass, rtol=1e-12, atol=1e-12)
+    assert np.allclose(mass.sum(axis=-1), 40.0, rtol=1e-12)  # each vector's weights sum to one
+    assert np.allclose(new, want, rtol=1e-10, atol=1e-12)
+
+
+def test_encode_gaps_equal_brute_force_top2():
+    """The near-tie diagnostic: for each decision, the two smallest distances found
+    by sorting every entry's distance (explicit loops), relative to max(d_best,
+    1e-12 |e|^2), with the residual of the greedy rounds before it."""
+    rng = np.random.default_rng(19)
+    N, H, G, g, Nc, R = 25, 2, 3, 2, 6, 3
+    x = rng.standard_normal((N, H, G * g))
+    cb = rng.standard_normal((H, G, R, Nc, g))
+    cb[1, 2, 1, 4] = cb[1, 2, 1, 1]  # an exact duplicate: gap 0 wherever either is nearest
+    codes, gaps = O.encode(x, cb)
+    for n in range(N):
+        for h in range(H):
+            for j in range(G):
+                e = [float(v) for v in x[n, h, j * g:(j + 1) * g]]
+                for r in range(R):
+                    d = sorted((sum((e[i] - cb[h, j, r, l, i]) ** 2 for i in range(g)), l) for l in range(Nc))
+                    (d1, l1), (d2, _) = d[0], d[1]
+                    norm2 = sum(v * v for v in e)
+                    want = (d2 - d1) / max(d1, 1e-12 * norm2, 1e-300)
+                    assert codes[n, h, r, j] == l1
+                    assert math.isclose(gaps[n, h, r, j], want, rel_tol=1e-9, abs_tol=1e-12)
+                    e = [e[i] - cb[h, j, r, l1, i] for i in range(g)]
+    assert (gaps[:, 1, 1, 2] == 0).any() or not (codes[:, 1, 1, 2] == 1).any()
+
+
 def test_em_infinite_temperature_gives_the_mean_of_all_residuals():
     """T -> infinity: uniform responsibilities, so every entry becomes the mean of
     all residuals (round 1: x minus the nearest round-0 entry) with mass N / Nc."""
