@@ -53,14 +53,22 @@ typedef enum commvq_dtype { COMMVQ_F16 = 1 } commvq_dtype;
 
 /* commvq_decode_attention flags. By default shapes with head_dim 128, g = 8,
  * Nc' = 256, R = 1 or 2 and four query heads per KV head run a kernel that keeps
- * the query x codebook table and the position phases in fp16 (products summed in
- * fp32): its score error is about 4e-4 of |q||k|/sqrt(D), which keeps outputs
- * within 1e-4 of an fp64 reference for unit-variance queries but grows with the
- * spread of the scores. COMMVQ_DECODE_EXACT keeps the table in fp32 and every
- * phase exact (slower), for strongly peaked attention. The kernel for the other
- * shapes (fp32 table or rebuilt keys) takes each position's phase from the
- * hardware sine and cosine of its exact turn count (within 2e-7), and from an
- * exact sincospi under COMMVQ_DECODE_EXACT. */
+ * the query (per block of 64 positions), the position phases and the rotated
+ * key entries in fp16 (products summed in fp32). Its score error is about 2^-11
+ * of the spread of the score's terms, and the softmax passes it on more strongly
+ * the more the scores spread. So the kernel measures, per wavefront (its 64 to
+ * 512 positions), the standard deviation of the scaled scores (valid positions,
+ * each of the four query heads); where it exceeds 2.0 the wavefront recomputes its
+ * scores in fp32 (exact fp16 products, fp16 hi + lo phases, fp32 matrix-core
+ * sums), at several times the cost of its score phase. Validated range (outputs
+ * against an fp64 reference, worst row error over max |ref|): queries at 1 and
+ * 2 times unit variance stay on the fp16 scores (1-bit: <= 8.9e-4, 2-bit:
+ * <= 1.6e-3); from 4 times up to 16 times (tested) the recomputed scores give
+ * <= 1e-4, at 4K to 128K positions. COMMVQ_DECODE_EXACT selects the fp32
+ * generic kernel instead (slower still). The kernel for the other shapes (fp32
+ * table or rebuilt keys) takes each position's phase from the hardware sine and
+ * cosine of its exact turn count (within 2e-7), and from an exact sincospi under
+ * COMMVQ_DECODE_EXACT. */
 #define COMMVQ_DECODE_EXACT 1u
 
 /* One codebook (keys or values) for all KV heads of one layer.

@@ -140,6 +140,20 @@ __device__ __forceinline__ half4_t as_h4(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(half4_t, (u32x2){lo, hi});
 }
 
+// Real and imaginary parts of z e + c for packed fp16 pairs z = (x, y) and
+// e = (c, s), in fp32: v_dot2_f32_f16 forms both products exactly and adds them
+// in fp32. The real part takes z as (x, -y), the imaginary part as (y, x).
+__device__ __forceinline__ float cdot(uint32_t zv, uint32_t e, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, zv), __builtin_bit_cast(half2_t, e), c, false);
+}
+__device__ __forceinline__ uint32_t conj_h2(uint32_t z) { return z ^ 0x80000000u; }       // (x, -y)
+__device__ __forceinline__ uint32_t swap_h2(uint32_t z) { return __builtin_amdgcn_alignbit(z, z, 16); }  // (y, x)
+
+// Largest standard deviation of the scaled scores over the valid positions of a
+// wavefront beyond which its scores are recomputed in fp32 (see the precision
+// guard in the kernel).
+constexpr float kFastSigmaMax = 2.0f;
+
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 
 // Decode step, R = 1: one group of the new token's key or value searched by a
@@ -509,6 +523,121 @@ __global__ __launch_bounds__(FT, 1) void decode_fast_kernel(DecodeArgs a, PhaseT
     for (int k = 0; k < FNH; ++k) s[t][k] = acc0[k] + acc1[k];
   });
   __builtin_amdgcn_s_setprio(0);
+
+  // ---- precision guard ----------------------------------------------------
+  // The fp16 roundings above (q', the lane phases, k') leave each score an error
+  // of about 2^-11 of the spread of its terms, and the softmax passes it on the
+  // more strongly the scores spread. When the standard deviation of a
+  // wavefront's scaled scores (valid positions, any of the four heads) exceeds
+  // kFastSigmaMax, the wavefront recomputes its scores: lane phases as fp16
+  // hi + lo parts, k' formed in fp32 (exact fp16 products), q' in fp32 from an
+  // exact block phase, and the dot products on v_mfma_f32_4x4x1f32.
+  bool precise = false;
+  {
+    // per head, one pass: the sums of s and s^2 over the valid positions, taken
+    // about one of the wavefront's scores (the spread does not depend on the
+    // shift, and the sums of squares stay small)
+    float wv[TL], nv = 0.f;
+#pragma unroll
+    for (int t = 0; t < TL; ++t) {
+      const int mt = m0 + tid + FT * t;
+      wv[t] = (mt < L && mt != skip_pos) ? 1.f : 0.f;
+      nv += wv[t];
+    }
+    const float n = wave_sum(nv);
+    if (n > 1.f) {
+      float vmax = 0.f;
+#pragma unroll
+      for (int k = 0; k < FNH; ++k) {
+        const float c0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, s[0][k])));
+        float a1 = 0.f, a2 = 0.f;
+#pragma unroll
+        for (int t = 0; t < TL; ++t) {
+          const float dv = wv[t] * (s[t][k] - c0);
+          a1 += dv;
+          a2 = fmaf(dv, dv, a2);
+        }
+        const float m1 = wave_sum(a1) / n;
+        vmax = fmaxf(vmax, wave_sum(a2) / n - m1 * m1);
+      }
+      precise = vmax * a.sm_scale * a.sm_scale > kFastSigmaMax * kFastSigmaMax;
+    }
+  }
+  if (precise) {
+    // low parts of the lane phases: e^{i lane theta_p} (hardware sine and cosine
+    // of the exact turn count) less its fp16 value el[p]
+    uint32_t elo[FPR];
+#pragma unroll
+    for (int p = 0; p < FPR; ++p) {
+      const float2 e = phase_hw((uint32_t)lane, ph.lo[p], ph.hi[p]);
+      const half2_t hi = __builtin_bit_cast(half2_t, el[p]);
+      elo[p] = pack_h2(e.x - (float)hi.x, e.y - (float)hi.y);
+    }
+    // MFMA A operand: instruction (pair p, part c) broadcasts block p % 16, whose
+    // lane (block j, row qi) holds head qi's q'_p, p = j + 16 r, as qa[2 r + c]
+    const int pj = lane >> 2;
+    static_for<TL>([&](auto tc) __attribute__((always_inline)) {
+      constexpr int t = decltype(tc)::value;
+      uint32_t cr[R][4];
+      load_rec(t, cr);
+      const uint32_t mb = (uint32_t)(m0 + 64 * wave + FT * t);
+      // (the rotated query and the turn counts are re-read per block, not kept
+      // in registers across blocks)
+      asm volatile("" ::: "memory");
+      float qa[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = pj + 16 * r;
+        const float2 q0 = qz[qi * FPR + p];
+        const float2 eb = phase_hw(mb, ph.lo[p], ph.hi[p]);
+        qa[2 * r] = fmaf(q0.x, eb.x, q0.y * eb.y);
+        qa[2 * r + 1] = fmaf(q0.y, eb.x, -q0.x * eb.y);
+      }
+      float4_t acc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = (float4_t){0.f, 0.f, 0.f, 0.f};
+      static_for<FG>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        u32x4 z[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const uint32_t off = byte_x16<j & 3>(cr[r][j >> 2]);  // code * 16
+          z[r] = *reinterpret_cast<const u32x4*>(lds + (size_t)(j * R + r) * FNC * 16 + off);
+        }
+        // two pairs' four k' components first, then their four products: a
+        // dot-product result must not reach the matrix core right after it is
+        // written (read too soon, the product took a stale operand)
+        static_for<2>([&](auto hc) __attribute__((always_inline)) {
+          constexpr int hh = decltype(hc)::value;
+          float kx[2], ky[2];
+          static_for<2>([&](auto uc) __attribute__((always_inline)) {
+            constexpr int u = 2 * hh + decltype(uc)::value, p = 4 * j + u, i = decltype(uc)::value;
+            if constexpr (R == 1) {
+              const uint32_t zc = conj_h2(z[0][u]), zw = swap_h2(z[0][u]);
+              kx[i] = cdot(zc, el[p], cdot(zc, elo[p], 0.f));
+              ky[i] = cdot(zw, el[p], cdot(zw, elo[p], 0.f));
+            } else {
+              // (z1 + z2) e: both rounds against the high part exactly, their
+              // fp16 sum against the low part (its rounding scaled by 2^-12)
+              const uint32_t zs = add_h2(z[0][u], z[1][u]);
+              kx[i] = cdot(conj_h2(z[0][u]), el[p], cdot(conj_h2(z[1][u]), el[p], cdot(conj_h2(zs), elo[p], 0.f)));
+              ky[i] = cdot(swap_h2(z[0][u]), el[p], cdot(swap_h2(z[1][u]), el[p], cdot(swap_h2(zs), elo[p], 0.f)));
+            }
+          });
+          // the wait takes the four values as operands, so every product is
+          // issued after it and at least eight wait states after the last write
+          asm volatile("s_nop 7" : "+v"(kx[0]), "+v"(ky[0]), "+v"(kx[1]), "+v"(ky[1]));
+          static_for<2>([&](auto uc) __attribute__((always_inline)) {
+            constexpr int u = 2 * hh + decltype(uc)::value, p = 4 * j + u, i = decltype(uc)::value;
+            acc[2 * i] = __builtin_amdgcn_mfma_f32_4x4x1f32(qa[2 * (p >> 4)], kx[i], acc[2 * i], 4, p & 15, 0);
+            acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(qa[2 * (p >> 4) + 1], ky[i], acc[2 * i + 1], 4, p & 15, 0);
+          });
+        });
+      });
+#pragma unroll
+      for (int k = 0; k < FNH; ++k) s[t][k] = (acc[0][k] + acc[1][k]) + (acc[2][k] + acc[3][k]);
+    });
+  }
 
   // value records of the lane's positions, requested now so they arrive during
   // the softmax; dword k of round r is taken from slot (k + q4) & 3 (the lane's

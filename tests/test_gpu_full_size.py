@@ -34,18 +34,18 @@ def oracle_unit(q, kp, vp, kcb, vcb, b, h, L, qpos, theta, rep):
         np.array([L]), kcb[h:h + 1], vcb[h:h + 1], theta)[0]
 
 
-def run_workload(name, units, lens=None, seed_shift=0):
+def run_workload(name, units, lens=None, seed_shift=0, q_scale=1.0, tol=ATTN_TOL):
     w = synth.WORKLOADS[name]
     B, Hq, H, D, Lmax = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.context
     rep = Hq // H
-    print(f"[full-size {name}] B={B} Hq={Hq} Hkv={H} Lmax={Lmax} R={w.n_rounds}", flush=True)
+    print(f"[full-size {name}] B={B} Hq={Hq} Hkv={H} Lmax={Lmax} R={w.n_rounds} q x{q_scale}", flush=True)
     kcb = synth.codebook(w.seed + 1, H, D, w.group_size, w.n_entries, w.n_rounds)
     vcb = synth.codebook(w.seed + 2, H, D, w.group_size, w.n_entries, w.n_rounds)
     kq, vq = api.Quantizer(dev(kcb), w.group_size), api.Quantizer(dev(vcb), w.group_size)
     bpt = kq.bytes_per_token
     kp = random_cache(w.seed + 40 + seed_shift, B, H, Lmax, bpt)
     vp = random_cache(w.seed + 41 + seed_shift, B, H, Lmax, bpt)
-    q = synth.queries(w.seed + 42 + seed_shift, B, Hq, D)
+    q = synth.queries(w.seed + 42 + seed_shift, B, Hq, D) * np.float32(q_scale)
     if lens is None:
         lens = np.full(B, Lmax, dtype=np.int32)
     lens = np.asarray(lens, dtype=np.int32)
@@ -59,12 +59,21 @@ def run_workload(name, units, lens=None, seed_shift=0):
         ref = oracle_unit(q, kp, vp, kcb, vcb, b, h, int(lens[b]), int(qpos[b]), w.theta_base, rep)
         err = row_errors(got[b, h * rep:(h + 1) * rep], ref)
         worst = max(worst, float(err.max()))
-        assert err.max() <= ATTN_TOL, (b, h, err)
+        assert err.max() <= tol, (b, h, err)
     print(f"[full-size {name}] {len(units)} units, max row rel err {worst:.3e}", flush=True)
 
 
 def test_full_size_32k_2bit_all_heads():
     run_workload("llama8b_ctx32k_2bit", [(0, h) for h in range(8)])
+
+
+@pytest.mark.parametrize("q_scale", [4.0, 8.0])
+@pytest.mark.parametrize("name", ["llama8b_ctx128k_1bit_64steps", "llama8b_ctx32k_2bit"])
+def test_full_size_peaked_queries_default_flags(name, q_scale):
+    """The 128K 1-bit and 32K 2-bit shapes with queries scaled by 4 and 8 under
+    the default flags: the fp16 path alone misses the bar here (about 2e-3 to
+    8e-3); the kernel's spread guard recomputes these scores in fp32."""
+    run_workload(name, [(0, 0), (0, 5)], q_scale=q_scale, tol=1e-4)
 
 
 def test_full_size_b16_ragged_32k_2bit_sampled():

@@ -265,14 +265,20 @@ def test_decode_peaked_queries_exact_mode(q_scale, R):
     assert err.max() <= ATTN_TOL
 
 
-@pytest.mark.parametrize("q_scale", [1.0, 2.0])
+@pytest.mark.parametrize("q_scale", [1.0, 2.0, 4.0, 8.0, 16.0])
 @pytest.mark.parametrize("R", [1, 2])
 def test_decode_fast_path_query_scales(q_scale, R):
-    """fp16-table kernel: unit-variance queries (the workloads' distribution) and twice that."""
+    """Default flags across query scales: unit-variance queries (the workloads'
+    distribution) up to 16 times that. Scores whose spread exceeds the fp16
+    path's bound are recomputed in fp32 inside the kernel; from q x 4 every
+    wavefront's spread is past it, and the error must then be far below what the
+    fp16 roundings alone leave (about 1.4e-3 to 8e-3 on these inputs)."""
     got, ref, err = run_decode_case(78 + R, B=2, Hq=8, Hkv=2, D=128, g=8, Nc=256, R=R, lens=[5000, 3001],
                                     Lmax=5120, q_scale=q_scale)
-    print(f"[decode fast x{q_scale} R{R}] max row rel err {err.max():.3e}", flush=True)
+    print(f"[decode flags 0 x{q_scale} R{R}] max row rel err {err.max():.3e}", flush=True)
     assert err.max() <= ATTN_TOL
+    if q_scale >= 4.0:
+        assert err.max() <= 1e-4
 
 
 @pytest.mark.parametrize("R", [1, 2])
