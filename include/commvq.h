@@ -15,7 +15,9 @@
  *
  * Conventions shared by every call:
  *  - Device pointers are HIP device allocations owned by the caller. The library
- *    allocates nothing and keeps no state besides a thread-local error string.
+ *    allocates nothing and keeps no state besides a thread-local error string,
+ *    and, for commvq_decode_step_noalloc, one static scratch array per GPU (with
+ *    its device address, looked up once per device).
  *  - Every compute call is asynchronous on `stream` (a hipStream_t passed as
  *    void*; NULL is the default stream) and returns before the GPU work ends.
  *  - Calls return COMMVQ_OK (0) or a negative commvq_status; on error nothing is
@@ -204,6 +206,27 @@ int32_t commvq_decode_step(const commvq_codebook* kcb, const commvq_codebook* vc
                            int32_t batch, int32_t n_q_heads, int32_t cache_len,
                            int32_t max_seq_len, float sm_scale, float* out, void* workspace,
                            size_t workspace_bytes, uint32_t flags, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): commvq_decode_step with
+ * no workspace argument. Its chunk partials and new-token terms live in a static
+ * device array of COMMVQ_NOALLOC_SCRATCH_BYTES (16 MiB), one per GPU, held until
+ * the process ends; the call allocates nothing. A shape whose
+ * commvq_decode_workspace_bytes exceeds that size is rejected with
+ * COMMVQ_ERR_WORKSPACE before any HIP call. The scratch is that of the device
+ * current when the call is made (the stream must belong to it); its address is
+ * looked up on the first call on each device. Nothing in it has to start at zero
+ * (every call writes all it reads). All calls on one GPU share the one array:
+ * calls that overlap in time on the same GPU (other streams, other host
+ * threads) race. Arguments, outputs and errors as commvq_decode_step. */
+#define COMMVQ_NOALLOC_SCRATCH_BYTES (16ull << 20)
+int32_t commvq_decode_step_noalloc(const commvq_codebook* kcb, const commvq_codebook* vcb,
+                                   const commvq_rope* rope, const void* k_new, const void* v_new,
+                                   const int32_t* positions, const float* q, const int32_t* q_pos,
+                                   uint8_t* kcodes, uint8_t* vcodes, const int32_t* seq_lens,
+                                   int32_t batch, int32_t n_q_heads, int32_t cache_len,
+                                   int32_t max_seq_len, float sm_scale, float* out, uint32_t flags,
+                                   void* stream);
 
 /* ---- binary value codes ------------------------------------------------------
  * The paper codes a value vector with a binary code s in {0,1}^Nc and decodes

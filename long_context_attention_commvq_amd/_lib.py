@@ -20,6 +20,7 @@ COMMVQ_ERR_INVALID_ARG = -1
 COMMVQ_ERR_UNSUPPORTED = -2
 COMMVQ_ERR_WORKSPACE = -3
 COMMVQ_ERR_HIP = -4
+COMMVQ_NOALLOC_SCRATCH_BYTES = 16 << 20
 COMMVQ_F16 = 1
 COMMVQ_DECODE_EXACT = 1
 
@@ -36,6 +37,7 @@ EXPORTED = [
     "commvq_code_bytes_per_token", "commvq_decode_workspace_bytes", "commvq_encode", "commvq_append",
     "commvq_decode_attention", "commvq_decode_step", "commvq_dequantize_kv", "commvq_dense_workspace_bytes",
     "commvq_dense_decode_attention", "commvq_em_work_bytes", "commvq_em_step", "commvq_decode_attention_bitv", "commvq_decode_bitv_workspace_bytes",
+    "commvq_decode_step_noalloc",
 ]
 
 
@@ -95,6 +97,10 @@ def lib():
         L.commvq_decode_step.argtypes = [CB, CB, POINTER(commvq_rope), c_void_p, c_void_p, c_void_p, c_void_p,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                          c_float, c_void_p, c_void_p, c_size_t, ctypes.c_uint32, c_void_p]
+        L.commvq_decode_step_noalloc.restype = c_int32
+        L.commvq_decode_step_noalloc.argtypes = [CB, CB, POINTER(commvq_rope), c_void_p, c_void_p, c_void_p, c_void_p,
+                                                 c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                                 c_int32, c_float, c_void_p, ctypes.c_uint32, c_void_p]
         L.commvq_dequantize_kv.restype = c_int32
         L.commvq_dequantize_kv.argtypes = [CB, CB, POINTER(commvq_rope), c_void_p, c_void_p, c_void_p, c_int32,
                                            c_int32, c_int32, c_void_p, c_void_p, c_void_p]
@@ -216,6 +222,16 @@ def commvq_decode_step(kcb: commvq_codebook, vcb: commvq_codebook, rope: commvq_
         ctypes.byref(kcb), ctypes.byref(vcb), ctypes.byref(rope), _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(q),
         _ptr(q_pos), _ptr(kcodes), _ptr(vcodes), _ptr(seq_lens), batch, n_q_heads, cache_len, max_seq_len,
         float(sm_scale), _ptr(out), _ptr(workspace), int(workspace_bytes), int(flags), _stream(stream, q, out)))
+
+
+def commvq_decode_step_noalloc(kcb: commvq_codebook, vcb: commvq_codebook, rope: commvq_rope, k_new, v_new,
+                               positions, q, q_pos, kcodes, vcodes, seq_lens, batch: int, n_q_heads: int,
+                               cache_len: int, max_seq_len: int, sm_scale: float, out, flags: int = 0,
+                               stream=None) -> int:
+    return _check(lib().commvq_decode_step_noalloc(
+        ctypes.byref(kcb), ctypes.byref(vcb), ctypes.byref(rope), _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(q),
+        _ptr(q_pos), _ptr(kcodes), _ptr(vcodes), _ptr(seq_lens), batch, n_q_heads, cache_len, max_seq_len,
+        float(sm_scale), _ptr(out), int(flags), _stream(stream, q, out)))
 
 
 def commvq_dequantize_kv(kcb: commvq_codebook, vcb: commvq_codebook, rope: commvq_rope, kcodes, vcodes, seq_lens,

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/commvq.h"
 #include "decode_common.hpp"
@@ -85,6 +86,34 @@ int32_t check_entries(const commvq_codebook* cb, const char* name) {
 int32_t hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return COMMVQ_OK;
   return fail(COMMVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Scratch of commvq_decode_step_noalloc: a static device array, one copy per
+// GPU, held until the process ends. In host code its name is only a stand-in:
+// the device address is looked up once per device (with that device current)
+// and that address is what kernels and copies receive.
+constexpr int kNoAllocMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[COMMVQ_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kNoAllocMaxDevices] = {};
+
+int32_t noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "commvq_decode_step_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kNoAllocMaxDevices)
+    return fail(COMMVQ_ERR_UNSUPPORTED, "commvq_decode_step_noalloc: device %d beyond the %d with a scratch address",
+                dev, kNoAllocMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "commvq_decode_step_noalloc: hipGetSymbolAddress");
+    if (!ptr) return fail(COMMVQ_ERR_HIP, "commvq_decode_step_noalloc: null scratch address");
+    g_scratch_addr[dev] = ptr;
+  }
+  *out = g_scratch_addr[dev];
+  return COMMVQ_OK;
 }
 
 int32_t decode_shapes(const commvq_codebook* kcb, const commvq_codebook* vcb, int32_t batch,
@@ -274,7 +303,7 @@ int32_t decode_impl(const commvq_codebook* kcb, const commvq_codebook* vcb, cons
                     const int32_t* q_pos, const uint8_t* kcodes, const uint8_t* vcodes, const int32_t* seq_lens,
                     int32_t batch, int32_t n_q_heads, int32_t cache_len, int32_t max_seq_len, float sm_scale,
                     float* out, void* workspace, size_t workspace_bytes, uint32_t flags, const StepArgs* step,
-                    void* stream) {
+                    void* stream, bool static_scratch = false) {
   g_err[0] = 0;
   commvq::CbShape k, v;
   int32_t st = decode_shapes(kcb, vcb, batch, n_q_heads, max_seq_len, &k, &v);
@@ -310,6 +339,16 @@ int32_t decode_impl(const commvq_codebook* kcb, const commvq_codebook* vcb, cons
   }
   const int64_t need = commvq_decode_workspace_bytes(batch, n_q_heads, max_seq_len, kcb, vcb);
   if (need < 0) return (int32_t)need;
+  if (static_scratch) {
+    // every argument is checked above, before the first HIP call
+    if ((uint64_t)need > (uint64_t)COMMVQ_NOALLOC_SCRATCH_BYTES)
+      return fail(COMMVQ_ERR_WORKSPACE,
+                  "commvq_decode_step_noalloc: this shape needs %lld bytes of scratch, beyond the static %llu",
+                  (long long)need, (unsigned long long)COMMVQ_NOALLOC_SCRATCH_BYTES);
+    st = noalloc_scratch(&workspace);
+    if (st) return st;
+    workspace_bytes = COMMVQ_NOALLOC_SCRATCH_BYTES;
+  }
   if (!workspace || workspace_bytes < (size_t)need)
     return fail(COMMVQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %lld required", workspace_bytes,
                 (long long)need);
@@ -399,6 +438,16 @@ int32_t commvq_decode_step(const commvq_codebook* kcb, const commvq_codebook* vc
   StepArgs st{k_new, v_new, positions};
   return decode_impl(kcb, vcb, rope, q, q_pos, kcodes, vcodes, seq_lens, batch, n_q_heads, cache_len, max_seq_len,
                      sm_scale, out, workspace, workspace_bytes, flags, &st, stream);
+}
+
+int32_t commvq_decode_step_noalloc(const commvq_codebook* kcb, const commvq_codebook* vcb, const commvq_rope* rope,
+                                   const void* k_new, const void* v_new, const int32_t* positions, const float* q,
+                                   const int32_t* q_pos, uint8_t* kcodes, uint8_t* vcodes, const int32_t* seq_lens,
+                                   int32_t batch, int32_t n_q_heads, int32_t cache_len, int32_t max_seq_len,
+                                   float sm_scale, float* out, uint32_t flags, void* stream) {
+  StepArgs st{k_new, v_new, positions};
+  return decode_impl(kcb, vcb, rope, q, q_pos, kcodes, vcodes, seq_lens, batch, n_q_heads, cache_len, max_seq_len,
+                     sm_scale, out, nullptr, 0, flags, &st, stream, true);
 }
 
 }  // extern "C"

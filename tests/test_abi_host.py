@@ -154,6 +154,25 @@ def test_decode_step_validation_without_launch():
     assert step(ws_bytes=16) == _lib.COMMVQ_ERR_WORKSPACE
 
 
+def test_decode_step_noalloc_validation_without_launch():
+    """The allocation-free step checks every argument, and its static scratch's
+    size against the shape's need, before any GPU call."""
+    k, rope = cb(R=1), _lib.make_rope(500000.0)
+    L = _lib.lib()
+
+    def step(k_new=FAKE, batch=1, lmax=1024, flags=0):
+        return L.commvq_decode_step_noalloc(ctypes.byref(k), ctypes.byref(k), ctypes.byref(rope), k_new, FAKE, FAKE,
+                                            FAKE, FAKE, FAKE, FAKE, FAKE, batch, 32, lmax, lmax, 0.088, FAKE, flags,
+                                            None)
+    assert step(k_new=None) == _lib.COMMVQ_ERR_INVALID_ARG
+    assert step(flags=2) == _lib.COMMVQ_ERR_INVALID_ARG
+    assert step(batch=0) == _lib.COMMVQ_ERR_INVALID_ARG
+    big = (64, 131072)
+    assert _lib.commvq_decode_workspace_bytes(big[0], 32, big[1], k, k) > _lib.COMMVQ_NOALLOC_SCRATCH_BYTES
+    assert step(batch=big[0], lmax=big[1]) == _lib.COMMVQ_ERR_WORKSPACE
+    assert "scratch" in _lib.commvq_last_error()
+
+
 def test_dense_workspace_query():
     E = _lib
     assert E.commvq_dense_workspace_bytes(1, 32, 8, 128, 131072) == 32 * 128 * 130 * 4  # chunks of 1024 positions
