@@ -38,6 +38,18 @@ __host__ __device__ constexpr int generic_threads(int nh, int gs) { return (gs >
 constexpr int kHistShift = 20;  // fixed-point weights: w * 2^20 (chunk <= 1024 keeps sums < 2^31)
 constexpr int kBitSub = 128;    // binary value codes: positions whose bit rows are staged in LDS at a time
 
+// acc + the fp16 in the low (high) half of w, in one v_fma_mix_f32 (the
+// conversion is exact and the product by 1 too: one rounding, as a convert
+// then an fp32 add)
+__device__ __forceinline__ float add_f16_lo(float acc, uint32_t w) {
+  asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel_hi:[1,0,0]" : "+v"(acc) : "v"(w));
+  return acc;
+}
+__device__ __forceinline__ float add_f16_hi(float acc, uint32_t w) {
+  asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(acc) : "v"(w));
+  return acc;
+}
+
 __device__ __forceinline__ int read_field(const uint8_t* rec, int f, int bits) {
   const int o = f * bits, byte = o >> 3, sh = o & 7;
   uint32_t v = rec[byte];
@@ -50,6 +62,52 @@ __device__ __forceinline__ int read_field(const uint8_t* rec, int f, int bits) {
 __host__ __device__ inline int generic_hist_rounds(const CbShape& k, const CbShape& v, int NH) {
   const size_t table = k.g >= kWideGroup ? (size_t)k.R * k.Nc * 32 * 2 : (size_t)NH * k.Nc * (k.g / 2) * 8;
   return (size_t)NH * v.R * v.Nc * 4 <= table ? v.R : 1;
+}
+
+// Bytes of the region that holds the query x codebook table (or one slice of
+// every round's entries, for wide groups) and, later, the value histograms.
+__host__ __device__ inline size_t generic_uni_bytes(const CbShape& k, const CbShape& v, int NH) {
+  const size_t table_bytes = k.g >= kWideGroup ? (size_t)k.R * k.Nc * 32 * sizeof(_Float16)  // one slice, all rounds
+                                               : (size_t)NH * k.Nc * (k.g / 2) * sizeof(float2);
+  const size_t hist_bytes = (size_t)NH * generic_hist_rounds(k, v, NH) * v.Nc * sizeof(uint32_t);
+  return ((table_bytes > hist_bytes ? table_bytes : hist_bytes) + 15) / 16 * 16;
+}
+
+// Wide groups re-read every position's record once per (group, slice) and per
+// value pass, one field per round: with records of at most 32 bytes the chunk's
+// key and value records are copied to LDS once, so those reads wait on LDS
+// instead of on memory.
+// (only where they fit the LDS beside the rest)
+__host__ __device__ inline size_t generic_fixed_bytes(const CbShape& k, int NH) {
+  // rotated queries (float2 per pair), output accumulators, reductions
+  const int P = k.D / 2, NW = generic_threads(NH, k.g) / 64;
+  return (2 * NH * P + NH * k.D + ((NH * (NW > 2 ? NW : 2) + 2 * NH + 4) & ~3)) * sizeof(float);
+}
+__host__ __device__ inline bool generic_stage_records(const CbShape& k, const CbShape& v, int NH) {
+  return k.g >= kWideGroup && k.bpt <= 32 && v.bpt <= 32 &&
+         generic_fixed_bytes(k, NH) + generic_uni_bytes(k, v, NH) + (size_t)kGenericChunk * (k.bpt + v.bpt) <=
+             160 * 1024;
+}
+__host__ __device__ inline size_t generic_rec_bytes(const CbShape& k, const CbShape& v, int NH) {
+  return generic_stage_records(k, v, NH) ? (size_t)kGenericChunk * (k.bpt + v.bpt) : 0;
+}
+
+// n bytes from global memory to LDS, eight loads in flight per lane
+template <int T>
+__device__ __forceinline__ void copy_bytes(uint8_t* dst, const uint8_t* src, int n, int tid) {
+  for (int i0 = 0; i0 < n; i0 += T * 8) {
+    uint8_t tmp[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * T + tid;
+      tmp[u] = i < n ? src[i] : (uint8_t)0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * T + tid;
+      if (i < n) dst[i] = tmp[u];
+    }
+  }
 }
 
 template <int NH, int GS, bool BITV>
@@ -103,6 +161,22 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
 
   const uint8_t* kbase = a.kcodes + ((size_t)b * K.Hkv + h) * (size_t)a.cache_len * K.bpt;
   const uint8_t* vbase = a.vcodes + ((size_t)b * V.Hkv + h) * (size_t)a.cache_len * V.bpt;
+  // the chunk's records in LDS (positions present in the cache only), after
+  // the table region; the scores' first staging barrier orders these writes
+  const bool staged = GS >= kWideGroup && generic_stage_records(K, V, NH);
+  uint8_t* krl = reinterpret_cast<uint8_t*>(uni) + generic_uni_bytes(K, V, NH);
+  uint8_t* vrl = krl + (size_t)kGenericChunk * K.bpt;
+  if (staged) {
+    const int n = min(a.chunk, a.cache_len - m0);
+    copy_bytes<kThreads>(krl, kbase + (size_t)m0 * K.bpt, n * K.bpt, tid);
+    if constexpr (!BITV) copy_bytes<kThreads>(vrl, vbase + (size_t)m0 * V.bpt, n * V.bpt, tid);
+  }
+  auto kfield = [&](int m, int f) {
+    return staged ? read_field(krl + (size_t)(m - m0) * K.bpt, f, K.bits) : read_field(kbase + (size_t)m * K.bpt, f, K.bits);
+  };
+  auto vfield = [&](int m, int f) {
+    return staged ? read_field(vrl + (size_t)(m - m0) * V.bpt, f, V.bits) : read_field(vbase + (size_t)m * V.bpt, f, V.bits);
+  };
 
   // scores; the position phases are exact (sincospi of the exact turn count)
   // under COMMVQ_DECODE_EXACT, else from the hardware sine and cosine (turns)
@@ -115,14 +189,30 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
       // and dotted with the rotated queries. A query x codebook table per (group,
       // round) would cost a phase and NH products per pair and round instead.
       constexpr int SL = 32, SP = SL / 2;
-      _Float16* cbs = reinterpret_cast<_Float16*>(uni);  // [R][Nc][SL]
+      // [R][Nc][SL]: entry e's 16-byte chunk v at chunk slot 4 e + ((v + e / 4) & 3),
+      // so that lanes reading chunk v of different entries spread over the banks
+      _Float16* cbs = reinterpret_cast<_Float16*>(uni);
       for (int j = 0; j < G; ++j) {
         for (int sl = 0; sl < GS / SL; ++sl) {
           __syncthreads();
           const _Float16* src = a.kcb + ((size_t)h * G + j) * K.R * K.Nc * GS + sl * SL;  // entry (r, l) at (r Nc + l) GS
-          for (int i = tid; i < K.R * K.Nc * (SL / 8); i += kThreads) {
-            const int rl = i / (SL / 8), c8 = i % (SL / 8);
-            reinterpret_cast<uint4*>(cbs)[i] = *reinterpret_cast<const uint4*>(src + (size_t)rl * GS + c8 * 8);
+          {
+            // four 16-byte loads in flight per lane
+            const int nv = K.R * K.Nc * (SL / 8);
+            for (int i0 = 0; i0 < nv; i0 += 4 * kThreads) {
+              uint4 w[4];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u * kThreads + tid;
+                w[u] = i < nv ? *reinterpret_cast<const uint4*>(src + (size_t)(i / (SL / 8)) * GS + (i % (SL / 8)) * 8)
+                              : make_uint4(0u, 0u, 0u, 0u);
+              }
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u * kThreads + tid, e = i / (SL / 8);
+                if (i < nv) reinterpret_cast<uint4*>(cbs)[e * 4 + ((i + (e >> 2)) & 3)] = w[u];
+              }
+            }
           }
           __syncthreads();
 #pragma unroll
@@ -133,17 +223,17 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
   #pragma unroll
               for (int i = 0; i < SL; ++i) kx[i] = 0.f;
               for (int r = 0; r < K.R; ++r) {
-                const int code = read_field(kbase + (size_t)m * K.bpt, r * G + j, K.bits);
-                const uint4* e = reinterpret_cast<const uint4*>(cbs + ((size_t)r * K.Nc + code) * SL);
+                const int code = kfield(m, r * G + j);
+                const int ei = r * K.Nc + code;
+                const uint4* e = reinterpret_cast<const uint4*>(cbs) + ei * 4;
   #pragma unroll
                 for (int v = 0; v < SL / 8; ++v) {
-                  const uint4 w = e[v];
+                  const uint4 w = e[(v + (ei >> 2)) & 3];
                   const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
   #pragma unroll
                   for (int u = 0; u < 4; ++u) {
-                    const half2_t xy = __builtin_bit_cast(half2_t, wd[u]);
-                    kx[8 * v + 2 * u] += (float)xy.x;
-                    kx[8 * v + 2 * u + 1] += (float)xy.y;
+                    kx[8 * v + 2 * u] = add_f16_lo(kx[8 * v + 2 * u], wd[u]);
+                    kx[8 * v + 2 * u + 1] = add_f16_hi(kx[8 * v + 2 * u + 1], wd[u]);
                   }
                 }
               }
@@ -319,7 +409,7 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
 #pragma unroll
           for (int hh = 0; hh < NH; ++hh) fx[hh] = (uint32_t)fmaf(s[t][hh], (float)(1 << kHistShift), 0.5f);
           for (int rr = 0; rr < RB; ++rr) {
-            const int code = read_field(vbase + (size_t)m * V.bpt, (r + rr) * G + j, V.bits);
+            const int code = vfield(m, (r + rr) * G + j);
 #pragma unroll
             for (int hh = 0; hh < NH; ++hh) atomicAdd(&hist[hh * NBIN + rr * V.Nc + code], fx[hh]);
           }
@@ -333,7 +423,39 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
       // lanes of one wavefront and added with shuffles
       constexpr int NO = NH * GS;
       constexpr int PARTS = NO >= kThreads ? 1 : (kThreads / NO > 64 ? 64 : kThreads / NO);
-      if constexpr (PARTS == 1) {
+      // groups of 8 scalars: a lane takes 8 consecutive outputs of one head
+      // (one 16-byte codebook read per bin) over every PV-th bin, and the PV
+      // lanes of those outputs (adjacent, in one wavefront) are added with shuffles
+      constexpr int NOV = NH * GS / 8;
+      constexpr int PV = GS % 8 != 0 ? 0 : (kThreads / NOV > 64 ? 64 : kThreads / NOV);
+      if constexpr (PV >= 2) {
+        const int o = tid / PV, part = tid % PV;
+        if (o < NOV) {
+          const int hh = o / (GS / 8), ev = o % (GS / 8);
+          float acc[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+#pragma unroll 4
+          for (int l = part; l < NBIN; l += PV) {
+            const uint4 w = *reinterpret_cast<const uint4*>(cvp + (size_t)l * GS + 8 * ev);
+            const float hv = (float)hist[hh * NBIN + l];
+            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const half2_t xy = __builtin_bit_cast(half2_t, wd[u]);
+              acc[2 * u] = fmaf(hv, (float)xy.x, acc[2 * u]);
+              acc[2 * u + 1] = fmaf(hv, (float)xy.y, acc[2 * u + 1]);
+            }
+          }
+#pragma unroll
+          for (int off = PV / 2; off > 0; off >>= 1)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] += __shfl_xor(acc[k], off, 64);
+          if (part == 0)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) oacc[hh * D + j * GS + 8 * ev + k] += acc[k] * (1.0f / (float)(1 << kHistShift));
+        }
+      } else if constexpr (PARTS == 1) {
         for (int i = tid; i < NO; i += kThreads) {
           const int hh = i / GS, e = i % GS;
           float acc = 0.f;
@@ -421,13 +543,9 @@ size_t decode_bitv_smem(const CbShape& k, int nbits, int NH) {
 
 size_t decode_generic_smem(const CbShape& k, const CbShape& v, int NH) {
   // rotated queries (float2 per pair), output accumulators, reductions, then
-  // the query x codebook table of one (group, round) or a value histogram
-  const int P = k.D / 2, NW = generic_threads(NH, k.g) / 64;
-  const size_t table_bytes = k.g >= kWideGroup ? (size_t)k.R * k.Nc * 32 * sizeof(_Float16)  // one slice, all rounds
-                                               : (size_t)NH * k.Nc * (k.g / 2) * sizeof(float2);
-  const size_t hist_bytes = (size_t)NH * generic_hist_rounds(k, v, NH) * v.Nc * sizeof(uint32_t);
-  return (2 * NH * P + NH * k.D + ((NH * (NW > 2 ? NW : 2) + 2 * NH + 4) & ~3)) * sizeof(float) +
-         (table_bytes > hist_bytes ? table_bytes : hist_bytes);
+  // the query x codebook table of one (group, round) or a value histogram,
+  // then (wide groups, short records) the chunk's key and value records
+  return generic_fixed_bytes(k, NH) + generic_uni_bytes(k, v, NH) + generic_rec_bytes(k, v, NH);
 }
 
 bool decode_fast_path(const CbShape& k, const CbShape& v, int NH, int flags) {
