@@ -259,8 +259,8 @@ def bench_encode(args):
     sid = stream.cuda_stream
 
     def step():
-        _lib.commvq_encode(kq.desc, kx.data_ptr(), N, H * D, kc.data_ptr(), H * bpt, bpt, sid)
-        _lib.commvq_encode(vq.desc, vx.data_ptr(), N, H * D, vc.data_ptr(), H * bpt, bpt, sid)
+        _lib.commvq_encode(kq.desc, kx.data_ptr(), N, H * D, kc.data_ptr(), H * bpt, bpt, stream=sid)
+        _lib.commvq_encode(vq.desc, vx.data_ptr(), N, H * D, vc.data_ptr(), H * bpt, bpt, stream=sid)
 
     for _ in range(args.warmup):
         step()

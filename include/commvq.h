@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define COMMVQ_ABI_VERSION 1
+#define COMMVQ_ABI_VERSION 2
 
 typedef enum commvq_status {
   COMMVQ_OK = 0,
@@ -136,11 +136,20 @@ int64_t commvq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t 
  * n_tokens == 0 launches nothing. One round of one group's codebook (Nc' * g
  * fp32) plus 64 tokens' codes (64 * R * D/g bytes) must fit 160 KiB of LDS
  * (otherwise COMMVQ_ERR_UNSUPPORTED; commvq_append and commvq_decode_step
- * share the rule). Pages: "What carries the argument" (shared index per
- * group, R residual rounds). */
+ * share the rule).
+ *   gap_out  nullable device fp32 [n_tokens][Hkv][R][G], 4-byte aligned: when
+ *          given, a second kernel (after the encoder, same stream) writes each
+ *          field's near-tie diagnostic (d2 - d1) / max(d1, 1e-12 |e|^2), the
+ *          relative margin between the two smallest squared distances of the
+ *          round's residual e to the group's entries (fp32; +inf when Nc' = 1),
+ *          with each round's residual taken after the encoder's own earlier
+ *          picks. A field whose margin is below ~1e-5 is a near tie: another
+ *          implementation may choose the other entry.
+ * Pages: "What carries the argument" (shared index per group, R residual
+ * rounds). */
 int32_t commvq_encode(const commvq_codebook* cb, const void* x, int64_t n_tokens,
                       int64_t x_token_stride, uint8_t* codes, int64_t code_token_stride,
-                      int64_t code_head_stride, void* stream);
+                      int64_t code_head_stride, float* gap_out, void* stream);
 
 /* Encode one new token per sequence and write it into a contiguous cache at a
  * per-sequence position held on the device.

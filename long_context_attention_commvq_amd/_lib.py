@@ -86,7 +86,7 @@ def lib():
         L.commvq_decode_workspace_bytes.restype = c_int64
         L.commvq_decode_workspace_bytes.argtypes = [c_int32, c_int32, c_int32, CB, CB]
         L.commvq_encode.restype = c_int32
-        L.commvq_encode.argtypes = [CB, c_void_p, c_int64, c_int64, c_void_p, c_int64, c_int64, c_void_p]
+        L.commvq_encode.argtypes = [CB, c_void_p, c_int64, c_int64, c_void_p, c_int64, c_int64, c_void_p, c_void_p]
         L.commvq_append.restype = c_int32
         L.commvq_append.argtypes = [CB, c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_void_p]
         L.commvq_decode_attention.restype = c_int32
@@ -195,9 +195,9 @@ def commvq_decode_workspace_bytes(batch: int, n_q_heads: int, max_seq_len: int, 
 
 
 def commvq_encode(cb: commvq_codebook, x, n_tokens: int, x_token_stride: int, codes, code_token_stride: int,
-                  code_head_stride: int, stream=None) -> int:
+                  code_head_stride: int, gap_out=None, stream=None) -> int:
     return _check(lib().commvq_encode(ctypes.byref(cb), _ptr(x), n_tokens, x_token_stride, _ptr(codes),
-                                      code_token_stride, code_head_stride, _stream(stream, x, codes)))
+                                      code_token_stride, code_head_stride, _ptr(gap_out), _stream(stream, x, codes)))
 
 
 def commvq_append(cb: commvq_codebook, x, batch: int, positions, cache, cache_len: int, stream=None) -> int:

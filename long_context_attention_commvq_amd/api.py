@@ -65,14 +65,20 @@ class Quantizer:
         return _lib.commvq_bits_per_scalar(self.desc)
 
 
-def encode(quant: Quantizer, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """x fp16 [N, Hkv, D] -> packed codes uint8 [N, Hkv, bytes_per_token]."""
+def encode(quant: Quantizer, x: torch.Tensor, out: torch.Tensor | None = None,
+           gaps: torch.Tensor | None = None) -> torch.Tensor:
+    """x fp16 [N, Hkv, D] -> packed codes uint8 [N, Hkv, bytes_per_token]; with
+    gaps (fp32 [N, Hkv, R, G], contiguous) also each field's near-tie margin."""
     N, H, D = x.shape
     x = x.contiguous()
     bpt = quant.bytes_per_token
     if out is None:
         out = torch.empty((N, H, bpt), dtype=torch.uint8, device=x.device)
-    _lib.commvq_encode(quant.desc, x, N, H * D, out, out.stride(0), out.stride(1))
+    if gaps is not None:
+        _need(gaps, "gaps", torch.float32, x.device, (N, H, quant.n_rounds, quant.head_dim // quant.group_size))
+        if not gaps.is_contiguous():
+            raise ValueError("gaps must be contiguous")
+    _lib.commvq_encode(quant.desc, x, N, H * D, out, out.stride(0), out.stride(1), gaps)
     return out
 
 

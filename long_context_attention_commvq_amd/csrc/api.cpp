@@ -218,7 +218,8 @@ int64_t commvq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t 
 }
 
 int32_t commvq_encode(const commvq_codebook* cb, const void* x, int64_t n_tokens, int64_t x_token_stride,
-                      uint8_t* codes, int64_t code_token_stride, int64_t code_head_stride, void* stream) {
+                      uint8_t* codes, int64_t code_token_stride, int64_t code_head_stride, float* gap_out,
+                      void* stream) {
   g_err[0] = 0;
   commvq::CbShape s;
   int32_t st = check_shape(cb, "codebook", &s);
@@ -231,6 +232,7 @@ int32_t commvq_encode(const commvq_codebook* cb, const void* x, int64_t n_tokens
   if (st) return st;
   if (!x || !codes) return fail(COMMVQ_ERR_INVALID_ARG, "null x or codes pointer");
   if (reinterpret_cast<uintptr_t>(x) & 3) return fail(COMMVQ_ERR_INVALID_ARG, "x must be 4-byte aligned");
+  if (reinterpret_cast<uintptr_t>(gap_out) & 3) return fail(COMMVQ_ERR_INVALID_ARG, "gap_out must be 4-byte aligned");
   if (x_token_stride < (int64_t)s.Hkv * s.D || (x_token_stride & 1))
     return fail(COMMVQ_ERR_INVALID_ARG, "x_token_stride %lld must be even and >= n_kv_heads*head_dim",
                 (long long)x_token_stride);
@@ -257,7 +259,9 @@ int32_t commvq_encode(const commvq_codebook* cb, const void* x, int64_t n_tokens
   a.positions = nullptr;
   a.cache_len = 0;
   a.s = s;
-  return hip_status(commvq::launch_encode(a, static_cast<hipStream_t>(stream)), "commvq_encode launch");
+  hipError_t e = commvq::launch_encode(a, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && gap_out) e = commvq::launch_encode_gaps(a, gap_out, static_cast<hipStream_t>(stream));
+  return hip_status(e, "commvq_encode launch");
 }
 
 int32_t commvq_append(const commvq_codebook* cb, const void* x, int32_t batch, const int32_t* positions,

@@ -163,6 +163,8 @@ size_t decode_newtok_offset(const CbShape& k, int B, int Hq, int max_len, int ch
 hipError_t launch_decode_fast(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream);
 
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t stream);
+// The near-tie diagnostic of an encoding already written (gap per field, [n][Hkv][R][G] fp32).
+hipError_t launch_encode_gaps(const EncodeArgs& a, float* gap, hipStream_t stream);
 // Whether launch_encode searches this shape on the matrix cores (more than 64 tokens).
 bool encode_uses_matrix_cores(const CbShape& s);
 hipError_t launch_decode_generic(const DecodeArgs& a, const PhaseTable& ph, hipStream_t stream);

@@ -312,6 +312,68 @@ bool encode_uses_matrix_cores(const CbShape& s) {
   return s.g == 8 && s.Nc == 256 && s.R <= 2 && (size_t)MF_TOKENS * s.R * s.G <= 64 * 1024;
 }
 
+// Near-tie diagnostic of an encoding already written: per (token, head, round,
+// group) field, the relative margin between the two smallest squared distances
+// of the round's residual to the group's entries,
+//   gap = (d2 - d1) / max(d1, 1e-12 |e|^2)   (+inf when Nc' = 1),
+// each round's residual taken after the encoder's own picks of the earlier
+// rounds (read back from the record). Distances in fp32. One lane per
+// (token, head, group); its residual lives in LDS (g <= 128 floats).
+constexpr int kGapThreads = 64;
+
+__device__ __forceinline__ int gap_read_field(const uint8_t* rec, int f, int bits) {
+  const int o = f * bits, byte = o >> 3, sh = o & 7;
+  uint32_t v = rec[byte];
+  if (sh + bits > 8) v |= (uint32_t)rec[byte + 1] << 8;
+  return (int)((v >> sh) & ((1u << bits) - 1u));
+}
+
+__global__ __launch_bounds__(kGapThreads) void encode_gaps_kernel(EncodeArgs a, float* gap) {
+  extern __shared__ float gap_e[];
+  const CbShape s = a.s;
+  const int G = s.G, g = s.g, R = s.R, Nc = s.Nc, H = s.Hkv;
+  const int64_t i = (int64_t)blockIdx.x * kGapThreads + threadIdx.x;  // (token, head, group)
+  if (i >= a.n_tokens * H * G) return;
+  const int j = (int)(i % G), h = (int)((i / G) % H);
+  const int64_t t = i / ((int64_t)G * H);
+  float* e = gap_e + threadIdx.x * g;
+  const _Float16* xs = a.x + t * a.x_token_stride + (int64_t)h * s.D + (int64_t)j * g;
+  for (int k = 0; k < g; ++k) e[k] = (float)xs[k];
+  const uint8_t* rec = a.codes + t * a.code_token_stride + (int64_t)h * a.code_head_stride;
+  for (int r = 0; r < R; ++r) {
+    const _Float16* ent = a.cb + (((size_t)h * G + j) * R + r) * (size_t)Nc * g;
+    float n2 = 0.f;
+    for (int k = 0; k < g; ++k) n2 = fmaf(e[k], e[k], n2);
+    float d1 = INFINITY, d2 = INFINITY;
+    for (int l = 0; l < Nc; ++l) {
+      float d = 0.f;
+      for (int k = 0; k < g; ++k) {
+        const float df = e[k] - (float)ent[(size_t)l * g + k];
+        d = fmaf(df, df, d);
+      }
+      if (d < d1) {
+        d2 = d1;
+        d1 = d;
+      } else if (d < d2) {
+        d2 = d;
+      }
+    }
+    gap[((t * H + h) * R + r) * G + j] = Nc > 1 ? (d2 - d1) / fmaxf(fmaxf(d1, 1e-12f * n2), 1e-30f) : INFINITY;
+    const int code = gap_read_field(rec, r * G + j, s.bits);
+    for (int k = 0; k < g; ++k) e[k] -= (float)ent[(size_t)code * g + k];
+  }
+}
+
+hipError_t launch_encode_gaps(const EncodeArgs& a, float* gap, hipStream_t stream) {
+  const int64_t n = a.n_tokens * a.s.Hkv * a.s.G;
+  if (n <= 0) return hipSuccess;
+  const int64_t nblk = (n + kGapThreads - 1) / kGapThreads;
+  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(encode_gaps_kernel, dim3((unsigned)nblk), dim3(kGapThreads), kGapThreads * a.s.g * sizeof(float),
+                     stream, a, gap);
+  return hipGetLastError();
+}
+
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t stream) {
   switch (a.s.g) {
     case 2: return launch_encode_g<2>(a, stream);

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert _lib.commvq_abi_version() == 1
+    assert _lib.commvq_abi_version() == 2
 
 
 def test_size_queries_match_the_oracle():
@@ -72,8 +72,8 @@ def test_null_descriptor():
     assert "null" in _lib.commvq_last_error()
 
 
-def _raw_encode(c, x, n, xs, codes, ts, hs):
-    return _lib.lib().commvq_encode(ctypes.byref(c), x, n, xs, codes, ts, hs, None)
+def _raw_encode(c, x, n, xs, codes, ts, hs, gap=None):
+    return _lib.lib().commvq_encode(ctypes.byref(c), x, n, xs, codes, ts, hs, gap, None)
 
 
 def test_encode_validation_without_launch():
@@ -89,6 +89,8 @@ def test_encode_validation_without_launch():
     assert _raw_encode(c, FAKE, 4, 256, FAKE, -64, 32) == _lib.COMMVQ_ERR_INVALID_ARG
     assert _raw_encode(cb(H=2, entries=None), FAKE, 4, 256, FAKE, 64, 32) == _lib.COMMVQ_ERR_INVALID_ARG
     assert _raw_encode(cb(H=2, entries=FAKE + 8), FAKE, 4, 256, FAKE, 64, 32) == _lib.COMMVQ_ERR_INVALID_ARG
+    assert _raw_encode(c, FAKE, 4, 256, FAKE, 64, 32, gap=FAKE + 2) == _lib.COMMVQ_ERR_INVALID_ARG  # misaligned gap_out
+    assert "gap_out" in _lib.commvq_last_error()
 
 
 def test_append_validation_without_launch():
@@ -279,7 +281,7 @@ def test_wide_groups_and_many_rounds():
     rope = _lib.make_rope(500000.0)
 
     def enc(c):
-        return L.commvq_encode(ctypes.byref(c), FAKE, 4, c.n_kv_heads * c.head_dim, FAKE, 4096, 512, None)
+        return L.commvq_encode(ctypes.byref(c), FAKE, 4, c.n_kv_heads * c.head_dim, FAKE, 4096, 512, None, None)
     assert enc(cb(D=96, g=24, Nc=16, R=1)) == E.COMMVQ_ERR_UNSUPPORTED          # no kernel for g = 24
     assert enc(cb(D=256, g=2, Nc=256, R=32)) == E.COMMVQ_ERR_UNSUPPORTED        # 4096 fields per record
     k = cb(D=128, g=64, Nc=256, R=16)

@@ -48,6 +48,39 @@ def test_encode_tiny_workload():
     assert not hard, hard[:5]
 
 
+@pytest.mark.parametrize("D,g,Nc,R,H,N,heavy", [
+    (128, 8, 256, 2, 2, 300, True),    # matrix-core search
+    (128, 8, 256, 2, 2, 5, False),     # few-token search
+    (128, 64, 64, 11, 1, 40, False),   # the paper's 1-bit quantizer (6-bit fields)
+    (64, 16, 64, 2, 3, 37, False),     # 6-bit fields straddle bytes
+])
+def test_encode_gap_diagnostic_matches_oracle(D, g, Nc, R, H, N, heavy):
+    """commvq_encode's gap_out against the oracle's gaps: where the GPU took the
+    oracle's codes so far (same residual), margins that are not near ties agree
+    to 1 %; every field whose code differs from the oracle's is a near tie in
+    the GPU's own diagnostic (< 1e-4)."""
+    x = synth.kv(4400 + N + R, N, H, D, heavy_tail=heavy)
+    cb = synth.codebook(4401 + N, H, D, g, Nc, R)
+    q = api.Quantizer(dev(cb), g)
+    G = D // g
+    gaps = torch.full((N, H, R, G), -1.0, dtype=torch.float32, device="cuda:0")
+    out = api.encode(q, dev(x), gaps=gaps)
+    torch.cuda.synchronize()
+    got_codes = O.unpack_codes(out.cpu().numpy(), R, G, Nc)  # [N, H, R, G]
+    ref_codes, ref_gaps = O.encode(x, cb)
+    gg = gaps.cpu().numpy().astype(np.float64)
+    assert np.all(gg >= 0)
+    same = np.cumprod(got_codes == ref_codes, axis=2).astype(bool)  # this and every earlier round agree
+    prev_same = np.concatenate([np.ones_like(same[:, :, :1]), same[:, :, :-1]], axis=2)
+    differ = prev_same & ~same
+    assert np.all(gg[differ] < 1e-4), gg[differ]
+    clear = same & (ref_gaps >= 1e-3)
+    rel = np.abs(gg[clear] - ref_gaps[clear]) / ref_gaps[clear]
+    print(f"[encode gaps N={N} g={g} R={R}] {clear.sum()} clear fields, max rel diff {rel.max():.2e}; "
+          f"{differ.sum()} differing codes, {(gg < 1e-5).sum()} fields under 1e-5", flush=True)
+    assert rel.max() <= 1e-2
+
+
 @pytest.mark.parametrize("D,g,Nc,R,H,N", [
     (128, 8, 256, 1, 2, 300),
     (128, 8, 256, 3, 1, 257),
