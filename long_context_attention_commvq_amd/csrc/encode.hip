@@ -14,8 +14,10 @@
 //    One v_mfma_f32_16x16x32_f16 gives the scores of 16 entries for 16 tokens:
 //    K = 32 holds [-c, -c, |c|^2/2 as three fp16 parts, 0...] against
 //    [e_hi, e_lo, 1, 1, 1, 0...], where e = e_hi + e_lo splits the fp32
-//    residual into two fp16 values (products are exact, sums fp32). The argmin
-//    compares the fp32 scores, lowest index on ties.
+//    residual into two fp16 values (products are exact, sums fp32). A per-token
+//    constant makes the scores non-negative, so the argmin runs on integer
+//    min3 over their bit patterns; the winner within a quad of four entries is
+//    settled by rescoring the four in fp32.
 //  * encode_kernel (any shape): distances accumulated term by term in fp32
 //    with fmaf against the codebook of one (group, round) staged in LDS.
 //  * encode_few_kernel (n <= 64 tokens, the decode-time append): one wavefront
@@ -144,32 +146,92 @@ __global__ __launch_bounds__(256) void encode_few_kernel(EncodeArgs a) {
 constexpr int MF_THREADS = 256;  // four wavefronts
 constexpr int MF_TOKENS = 256;   // tokens per workgroup (16 MFMA columns of 16)
 
+constexpr int MF_WAVES = MF_THREADS / 64;
+constexpr float kMfCScale = 4096.f;  // the per-token constant enters the scores as kMfCScale * C_h
+
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
+
+// Lexicographic minimum of (v, i) over lanes l and l ^ S (S = 16 or 32): one
+// v_permlane{16,32}_swap per operand leaves both lanes' pairs in every lane
+// (in some order), so every lane keeps the same winner.
+template <int S, typename T>
+__device__ __forceinline__ void lex_min_lanes(T& v, int& i) {
+  static_assert(S == 16 || S == 32, "lane distance");
+  const uint32_t vb = __builtin_bit_cast(uint32_t, v), ib = (uint32_t)i;
+  uint32_t v0, v1, i0, i1;
+  if constexpr (S == 16) {
+    const auto pv = __builtin_amdgcn_permlane16_swap(vb, vb, false, false);
+    const auto pi = __builtin_amdgcn_permlane16_swap(ib, ib, false, false);
+    v0 = pv[0], v1 = pv[1], i0 = pi[0], i1 = pi[1];
+  } else {
+    const auto pv = __builtin_amdgcn_permlane32_swap(vb, vb, false, false);
+    const auto pi = __builtin_amdgcn_permlane32_swap(ib, ib, false, false);
+    v0 = pv[0], v1 = pv[1], i0 = pi[0], i1 = pi[1];
+  }
+  const T a = __builtin_bit_cast(T, v0), b = __builtin_bit_cast(T, v1);
+  const bool second = b < a || (b == a && (int)i1 < (int)i0);
+  v = second ? b : a;
+  i = second ? (int)i1 : (int)i0;
+}
+
+// LDS of encode_mfma_kernel: four codebook slots of R x 256 entries (16 bytes
+// each), then the tile's R * G one-byte codes per token
+size_t encode_mfma_smem(const CbShape& s) {
+  return (size_t)MF_WAVES * s.R * 256 * 16 + (size_t)MF_TOKENS * s.R * s.G;
+}
+
+// sum of the eight fp16 products a_i b_i (each exact in fp32) onto acc
+__device__ __forceinline__ float mf_dot8(const uint4 a, const uint4 b, float acc) {
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a.x), __builtin_bit_cast(h2_t, b.x), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a.y), __builtin_bit_cast(h2_t, b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a.z), __builtin_bit_cast(h2_t, b.z), acc, false);
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a.w), __builtin_bit_cast(h2_t, b.w), acc, false);
+}
 
 // Workgroup = (tile of 256 tokens, KV head). Wavefront w takes groups w, w+4,
 // ...; for a group it keeps the A operands of all R rounds (16 blocks of 16
-// entries each) in registers and streams the tile's tokens through them, 16 at
-// a time: lane (q = lane / 16, n = lane % 16) feeds K slice q of token n and
-// receives the scores of entries 16 b + 4 q + i (i < 4) of block b for token n.
+// entries each) in registers, stages the group's codebook in its own LDS slot
+// and streams the tile's tokens through the A operands, 16 at a time: lane
+// (q = lane / 16, n = lane % 16) feeds K slice q of token n and receives the
+// scores of entries 16 b + 4 q + i (i < 4) of block b for token n.
+//
+// The scores carry a per-token constant C >= |e|^2 / 2 (K slice 2 holds
+// 4096 * C_h, C_h an fp16 rounded upward), which makes every score a
+// non-negative half squared distance, |e - c|^2 / 2 + (C - |e|^2 / 2): fp32
+// values >= 0 compare like their bit patterns as signed integers, so the
+// search runs on integer min3. Per lane it keeps the smallest score and the
+// block holding it; the four lanes of a token then agree on the quad of four
+// entries (block, q) with the smallest score, lowest first on equal scores.
+// Which entry of the quad won is settled by the four lanes rescoring one
+// entry each in fp32 (fp16 products, exact, summed in fp32): the two
+// evaluations can disagree only where two entries' scores agree to within
+// fp32 rounding (a near tie).
 template <int R>
 __global__ __launch_bounds__(MF_THREADS, 2) void encode_mfma_kernel(EncodeArgs a) {
-  extern __shared__ uint8_t mf_rec[];  // [MF_TOKENS][R * G] codes of the tile
+  extern __shared__ uint4 mf_smem[];  // [waves][R][256] codebook slots, then [MF_TOKENS][R * G] codes
   const CbShape s = a.s;
   const int G = s.G, RG = R * s.G;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, n = lane & 15;
+  uint4* cbw = mf_smem + wave * (R * 256);
+  uint8_t* mf_rec = reinterpret_cast<uint8_t*>(mf_smem + MF_WAVES * R * 256);
   const int h = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * MF_TOKENS;
+  const uint4 zero4 = {0u, 0u, 0u, 0u};
 
-  for (int j = wave; j < G; j += MF_THREADS / 64) {
-    const _Float16* cbj = a.cb + ((int64_t)h * G + j) * R * 256 * 8;
-    // A operands: rows = 16 entries of a block, K = [-c (q 0), -c (q 1), |c|^2/2 (q 2), 0 (q 3)]
+  for (int j = wave; j < G; j += MF_WAVES) {
+    // the slot is written and read by this wavefront only, in program order
+    const uint4* cbj = reinterpret_cast<const uint4*>(a.cb + ((int64_t)h * G + j) * R * 256 * 8);
+    for (int i = lane; i < R * 256; i += 64) cbw[i] = cbj[i];
+    // A operands: rows = 16 entries of a block,
+    // K = [-c (q 0), -c (q 1), |c|^2/2 as three parts and 4096 (q 2), 0 (q 3)]
     h8_t A[R][16];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int b = 0; b < 16; ++b) {
-        const h8_t c = *reinterpret_cast<const h8_t*>(cbj + ((size_t)r * 256 + 16 * b + n) * 8);
+        const h8_t c = __builtin_bit_cast(h8_t, cbw[r * 256 + 16 * b + n]);
         float v = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) v = fmaf((float)c[i], (float)c[i], v);
@@ -178,71 +240,97 @@ __global__ __launch_bounds__(MF_THREADS, 2) void encode_mfma_kernel(EncodeArgs a
         const float r1 = v - (float)v0;
         const _Float16 v1 = (_Float16)r1;
         const _Float16 v2 = (_Float16)(r1 - (float)v1);
-        const h8_t nrm = {v0, v1, v2, 0, 0, 0, 0, 0};
+        const h8_t nrm = {v0, v1, v2, (_Float16)kMfCScale, 0, 0, 0, 0};
         A[r][b] = q < 2 ? -c : (q == 2 ? nrm : h8_t{});
       }
-    const h8_t ones = {1, 1, 1, 0, 0, 0, 0, 0};
-#pragma unroll 1
-    for (int tb = 0; tb < MF_TOKENS / 16; ++tb) {
-      const int tl = 16 * tb + n;
-      const int64_t t = t0 + tl;
-      bool valid = t < a.n_tokens;
-      const _Float16* xp = nullptr;
-      if (valid) {
+    // group j of token n of batch tb (zero for tokens past the end or skipped)
+    auto fetch = [&a, &s, t0, n, h, j](int tb) -> uint4 {
+      const int64_t t = t0 + 16 * tb + n;
+      bool ok = t < a.n_tokens;
+      const _Float16* xp = a.x;
+      if (ok) {
         if (a.positions) {
           const int pos = a.positions[t];
-          valid = pos >= 0 && pos < a.cache_len;
+          ok = pos >= 0 && pos < a.cache_len;
           xp = a.x + (t * s.Hkv + h) * (int64_t)s.D;
         } else {
           xp = a.x + t * a.x_token_stride + (int64_t)h * s.D;
         }
       }
-      float e[8];
-      if (valid) {
-        const h8_t xv = *reinterpret_cast<const h8_t*>(xp + 8 * j);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = (float)xv[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = 0.f;
-      }
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (ok) v = *reinterpret_cast<const uint4*>(xp + 8 * j);
+      return v;
+    };
+    uint4 xnext = fetch(0);
+#pragma unroll 1
+    for (int tb = 0; tb < MF_TOKENS / 16; ++tb) {
+      const int tl = 16 * tb + n;
+      const uint4 xw = xnext;
+      if (tb + 1 < MF_TOKENS / 16) xnext = fetch(tb + 1);  // in flight during this batch
+      // |x|^2 of finite fp16 values stays below 2^36; a NaN or an infinity in
+      // the group makes it NaN or infinite, and such a group takes entry 0 in
+      // every round (it has no finite distance to any entry)
+      const bool non_finite = !(mf_dot8(xw, xw, 0.f) <= 0x1p36f);
+      float e[8];  // residual of the later rounds, fp32
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        h8_t hi, lo;
+        uint4 hw, lw;  // e = hi + lo in fp16
+        float ee;      // |e|^2
+        if (r == 0) {  // the input itself is fp16: hi = x, lo = 0
+          hw = xw;
+          lw = zero4;
+          ee = mf_dot8(xw, xw, 0.f);
+        } else {
+          h8_t hi, lo;
+          ee = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          hi[i] = (_Float16)e[i];
-          lo[i] = (_Float16)(e[i] - (float)hi[i]);
+          for (int i = 0; i < 8; ++i) {
+            hi[i] = (_Float16)e[i];
+            lo[i] = (_Float16)(e[i] - (float)hi[i]);
+            ee = fmaf(e[i], e[i], ee);
+          }
+          hw = __builtin_bit_cast(uint4, hi);
+          lw = __builtin_bit_cast(uint4, lo);
         }
-        const h8_t bv = q == 0 ? hi : (q == 1 ? lo : (q == 2 ? ones : h8_t{}));
-        float best = INFINITY;
-        int bi = 0x7fffffff;
+        // C_h >= |e|^2 / 8192: the 2^-10 factor covers the rounding of ee and
+        // of the conversion (normal range), the 2^-24 term the subnormal range
+        const _Float16 ch = (_Float16)fmaf(ee, 0x1.004p-13f, 0x1p-24f);
+        const h2_t one_c = {(_Float16)1.f, ch};
+        const uint4 cw = make_uint4(0x3C003C00u, __builtin_bit_cast(uint32_t, one_c), 0u, 0u);
+        const uint4 bw = q == 0 ? hw : (q == 1 ? lw : (q == 2 ? cw : zero4));
+        const h8_t bv = __builtin_bit_cast(h8_t, bw);
+        int best = 0x7fffffff, bb = 0;
 #pragma unroll
         for (int b = 0; b < 16; ++b) {
           const f4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][b], bv, (f4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (d[i] < best) {
-              best = d[i];
-              bi = 16 * b + 4 * q + i;
-            }
+          const int m3 = min(min(__float_as_int(d[0]), __float_as_int(d[1])), __float_as_int(d[2]));
+          const int nb = min(min(best, m3), __float_as_int(d[3]));
+          bb = nb < best ? b : bb;
+          best = nb;
         }
-        // the four lanes of token n hold disjoint entry sets
-#pragma unroll
-        for (int o = 16; o < 64; o <<= 1) {
-          const float od = __shfl_xor(best, o, 64);
-          const int oi = __shfl_xor(bi, o, 64);
-          if (od < best || (od == best && oi < bi)) {
-            best = od;
-            bi = oi;
-          }
-        }
-        if (bi == 0x7fffffff) bi = 0;  // no score compared below +inf (NaN input)
+        // the four lanes of token n: smallest (score, quad), quad = 4 block + q
+        int quad = 4 * bb + q;
+        lex_min_lanes<16>(best, quad);
+        lex_min_lanes<32>(best, quad);
+        // entries 16 (quad / 4) + 4 (quad % 4) + i, i < 4: lane q rescoring entry i = q
+        const int k0 = 16 * (quad >> 2) + 4 * (quad & 3);
+        const uint4 cq = cbw[r * 256 + k0 + q];
+        float sc = 0.5f * mf_dot8(cq, cq, 0.f) - mf_dot8(cq, lw, mf_dot8(cq, hw, 0.f));
+        int ki = q;
+        lex_min_lanes<16>(sc, ki);
+        lex_min_lanes<32>(sc, ki);
+        const int bi = non_finite ? 0 : k0 + ki;
         if (q == 0) mf_rec[tl * RG + r * G + j] = (uint8_t)bi;
         if (r + 1 < R) {
-          const h8_t c = *reinterpret_cast<const h8_t*>(cbj + ((size_t)r * 256 + bi) * 8);
+          const h8_t c = __builtin_bit_cast(h8_t, cbw[r * 256 + bi]);
+          if (r == 0) {
+            const h8_t x8 = __builtin_bit_cast(h8_t, xw);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) e[i] -= (float)c[i];
+            for (int i = 0; i < 8; ++i) e[i] = (float)x8[i] - (float)c[i];
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) e[i] -= (float)c[i];
+          }
         }
       }
     }
@@ -270,7 +358,6 @@ __global__ __launch_bounds__(MF_THREADS, 2) void encode_mfma_kernel(EncodeArgs a
   }
 }
 
-
 template <int GS>
 hipError_t launch_encode_g(const EncodeArgs& a, hipStream_t stream) {
   if (a.n_tokens <= 64 && a.s.R * a.s.G <= 512) {
@@ -281,7 +368,14 @@ hipError_t launch_encode_g(const EncodeArgs& a, hipStream_t stream) {
     if (encode_uses_matrix_cores(a.s)) {
       const int64_t nblk = (a.n_tokens + MF_TOKENS - 1) / MF_TOKENS;
       if (nblk > 0x7fffffff) return hipErrorInvalidValue;
-      const size_t smem = (size_t)MF_TOKENS * a.s.R * a.s.G;
+      const size_t smem = encode_mfma_smem(a.s);
+      static std::atomic<uint64_t> configured1{0}, configured2{0};
+      const void* fn = a.s.R == 1 ? reinterpret_cast<const void*>(&encode_mfma_kernel<1>)
+                                  : reinterpret_cast<const void*>(&encode_mfma_kernel<2>);
+      if (smem > 64 * 1024) {
+        const hipError_t e = allow_full_lds(fn, a.s.R == 1 ? configured1 : configured2);
+        if (e != hipSuccess) return e;
+      }
       if (a.s.R == 1)
         hipLaunchKernelGGL(encode_mfma_kernel<1>, dim3((unsigned)nblk, a.s.Hkv), dim3(MF_THREADS), smem, stream, a);
       else
@@ -307,9 +401,9 @@ hipError_t launch_encode_g(const EncodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 // The MFMA search covers g = 8, Nc' = 256 (8-bit fields) and R <= 2 when the
-// tile's codes fit the workgroup's LDS.
+// wavefronts' codebook slots and the tile's codes fit the workgroup's LDS.
 bool encode_uses_matrix_cores(const CbShape& s) {
-  return s.g == 8 && s.Nc == 256 && s.R <= 2 && (size_t)MF_TOKENS * s.R * s.G <= 64 * 1024;
+  return s.g == 8 && s.Nc == 256 && s.R <= 2 && encode_mfma_smem(s) <= 160 * 1024;
 }
 
 // Near-tie diagnostic of an encoding already written: per (token, head, round,
