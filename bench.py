@@ -275,7 +275,7 @@ def bench_encode(args):
     launch_s = ms_step * 1e-3 / 2  # two equal launches per step (K, V)
     token_heads = N * H
     candidates = token_heads * G * w.n_rounds * w.n_entries  # per launch
-    ops = 3 * candidates  # compare + two selects per candidate score
+    ops = candidates  # the argmin consumes every candidate score in at least one vector operation
     rec = {
         "metric": "prefill encode token-heads/s (K and V, 131072 tokens x 8 KV heads, 2-bit)",
         "value": 2 * token_heads / (ms_step * 1e-3),
@@ -289,7 +289,7 @@ def bench_encode(args):
                      "unit": "T lane-ops/s", "frac": ops / launch_s / VALU_PEAK_LANE_OPS,
                      "hbm_GBps": (N * H * D * 2 + N * H * bpt) / launch_s / 1e9,
                      "avg_launch_us": launch_s * 1e6,
-                     "work": "3 vector ops per (token, head, group, round, entry) candidate score"},
+                     "work": "1 vector op per (token, head, group, round, entry) candidate score"},
         "cpu_baseline": None if args.no_cpu else encode_cpu_baseline(args.cpu_seconds, w),
     }
     print(json.dumps(rec), flush=True)
@@ -636,11 +636,11 @@ def bench_em(args):
         torch.cuda.synchronize()
         ms = start.elapsed_time(stop) / args.steps
         # vector-ALU work per (vector, group, entry): at temperature 0 the step runs the matrix-core encoder
-        # (distances on MFMA; a compare and two selects per candidate, every round of the codebook searched) and
+        # (distances on MFMA; one vector op per candidate score, every round of the codebook searched) and
         # adds each vector to its entry's sums; at temperature > 0 the fitting kernel spends g subtractions, g FMAs
         # and a compare-select per candidate of each round searched, and two exponentials and g + 1 FMAs per entry
         # of the fitted round
-        per_entry = 3 * q.n_rounds if T == 0 else (r + 1) * (2 * g + 1) + (2 + g + 1)
+        per_entry = q.n_rounds if T == 0 else (r + 1) * (2 * g + 1) + (2 + g + 1)
         ops = N * H * G * Nc * per_entry
         out[label] = {"ms": ms, "vectors_per_s": N * H * G / (ms * 1e-3),
                       "achieved_T_lane_ops": ops / (ms * 1e-3) / 1e12,
@@ -660,7 +660,7 @@ def bench_em(args):
                    "group_size": g, "n_entries": Nc, "step": "commvq_em_step, round 0, temperature 0"},
         "roofline": {"bound": "alu", "achieved": main_rec["achieved_T_lane_ops"], "peak": VALU_PEAK_LANE_OPS / 1e12,
                      "unit": "T lane-ops/s", "frac": main_rec["frac_valu"],
-                     "work": "3 vector ops (compare, two selects) per (vector, group, entry, codebook round) of the "
+                     "work": "1 vector op per (vector, group, entry, codebook round) candidate score of the "
                              "matrix-core encoder that makes the nearest-entry choices"},
         "variants": out,
         "cpu_baseline": cpu,

@@ -12,12 +12,13 @@
 //    distance search is a GEMM on the matrix cores. For an entry c and residual
 //    e, score(c) = |c|^2 / 2 - e.c orders entries exactly as |e - c|^2 does.
 //    One v_mfma_f32_16x16x32_f16 gives the scores of 16 entries for 16 tokens:
-//    K = 32 holds [-c, -c, |c|^2/2 as three fp16 parts, 0...] against
-//    [e_hi, e_lo, 1, 1, 1, 0...], where e = e_hi + e_lo splits the fp32
-//    residual into two fp16 values (products are exact, sums fp32). A per-token
-//    constant makes the scores non-negative, so the argmin runs on integer
-//    min3 over their bit patterns; the winner within a quad of four entries is
-//    settled by rescoring the four in fp32.
+//    K = 32 holds [-c, -c, |c|^2/2 as three fp16 parts, 4096, 0...] against
+//    [x, y, 1, 1, 1, C_h, 0...], where the residual is e = x + y with x the
+//    fp16 input and y = 0 (round 0) or minus the round-0 entry (round 1), so
+//    every product is exact and the sums are fp32. The per-token constant
+//    4096 C_h >= |e|^2 / 2 makes the scores non-negative, so the argmin runs
+//    on integer min3 over their bit patterns; the winner within a quad of four
+//    entries is settled by rescoring the four in fp32.
 //  * encode_kernel (any shape): distances accumulated term by term in fp32
 //    with fmaf against the codebook of one (group, round) staged in LDS.
 //  * encode_few_kernel (n <= 64 tokens, the decode-time append): one wavefront
@@ -147,39 +148,76 @@ constexpr int MF_THREADS = 256;  // four wavefronts
 constexpr int MF_TOKENS = 256;   // tokens per workgroup (16 MFMA columns of 16)
 
 constexpr int MF_WAVES = MF_THREADS / 64;
+constexpr int MF_NB = 2;  // token batches of 16 interleaved per iteration
 constexpr float kMfCScale = 4096.f;  // the per-token constant enters the scores as kMfCScale * C_h
 
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
-// Lexicographic minimum of (v, i) over lanes l and l ^ S (S = 16 or 32): one
-// v_permlane{16,32}_swap per operand leaves both lanes' pairs in every lane
-// (in some order), so every lane keeps the same winner.
+// Minimum of (v, i) over lanes l and l ^ S (S = 16 or 32), the lower lane's
+// pair kept on equal v. A v_permlane{16,32}_swap of a register with itself
+// leaves, in every lane, the lower lane's (l & ~S) value in its first result
+// and the upper lane's (l | S) in its second, so both lanes keep the same
+// pair. With i_pair set, the two lanes' indices are given instead of swapped.
 template <int S, typename T>
-__device__ __forceinline__ void lex_min_lanes(T& v, int& i) {
+__device__ __forceinline__ void min_lanes(T& v, int& i, bool i_pair = false, int i_lo = 0, int i_hi = 0) {
   static_assert(S == 16 || S == 32, "lane distance");
-  const uint32_t vb = __builtin_bit_cast(uint32_t, v), ib = (uint32_t)i;
-  uint32_t v0, v1, i0, i1;
+  const uint32_t vb = __builtin_bit_cast(uint32_t, v);
+  uint32_t v0, v1;
   if constexpr (S == 16) {
     const auto pv = __builtin_amdgcn_permlane16_swap(vb, vb, false, false);
-    const auto pi = __builtin_amdgcn_permlane16_swap(ib, ib, false, false);
-    v0 = pv[0], v1 = pv[1], i0 = pi[0], i1 = pi[1];
+    v0 = pv[0], v1 = pv[1];
   } else {
     const auto pv = __builtin_amdgcn_permlane32_swap(vb, vb, false, false);
-    const auto pi = __builtin_amdgcn_permlane32_swap(ib, ib, false, false);
-    v0 = pv[0], v1 = pv[1], i0 = pi[0], i1 = pi[1];
+    v0 = pv[0], v1 = pv[1];
+  }
+  int i0 = i_lo, i1 = i_hi;
+  if (!i_pair) {
+    if constexpr (S == 16) {
+      const auto pi = __builtin_amdgcn_permlane16_swap((uint32_t)i, (uint32_t)i, false, false);
+      i0 = (int)pi[0], i1 = (int)pi[1];
+    } else {
+      const auto pi = __builtin_amdgcn_permlane32_swap((uint32_t)i, (uint32_t)i, false, false);
+      i0 = (int)pi[0], i1 = (int)pi[1];
+    }
   }
   const T a = __builtin_bit_cast(T, v0), b = __builtin_bit_cast(T, v1);
-  const bool second = b < a || (b == a && (int)i1 < (int)i0);
-  v = second ? b : a;
-  i = second ? (int)i1 : (int)i0;
+  const bool upper = b < a;
+  v = upper ? b : a;
+  i = upper ? i1 : i0;
 }
 
-// LDS of encode_mfma_kernel: four codebook slots of R x 256 entries (16 bytes
-// each), then the tile's R * G one-byte codes per token
+// K slice q of a token's B operand: x (q 0), y (q 1), the constants (q 2), 0
+// (q 3); m[k] is all ones in the lanes of slice k. Combined with bit masks, so
+// that nothing moves into per-slice branches.
+__device__ __forceinline__ h8_t b_operand(const uint32_t (&m)[3], const uint4 x, const uint4 y, const uint4 c) {
+  auto pick = [&m](uint32_t xv, uint32_t yv, uint32_t cv) -> uint32_t {
+    return (xv & m[0]) | (yv & m[1]) | (cv & m[2]);
+  };
+  typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+  const u4_t w = {pick(x.x, y.x, c.x), pick(x.y, y.y, c.y), pick(x.z, y.z, c.z), pick(x.w, y.w, c.w)};
+  return __builtin_bit_cast(h8_t, w);
+}
+
+// A wavefront's LDS slot, in 16-byte units: its group's R x 256 negated
+// entries, their fp32 |c|^2 / 2, and for R = 2 round 1's K-slice-2 operands
+__host__ __device__ constexpr int mf_slot(int R) { return R * 256 + R * 64 + (R - 1) * 256; }
+
+// |c|^2 / 2 in three fp16 parts, then the constant's scale: K slice 2 of an
+// entry's A operand
+__device__ __forceinline__ h8_t k_slice2(float v) {
+  const _Float16 v0 = (_Float16)v;
+  const float r1 = v - (float)v0;
+  const _Float16 v1 = (_Float16)r1;
+  const _Float16 v2 = (_Float16)(r1 - (float)v1);
+  return h8_t{v0, v1, v2, (_Float16)kMfCScale, 0, 0, 0, 0};
+}
+
+// LDS of encode_mfma_kernel: four wavefront slots, then the tile's R * G
+// one-byte codes per token
 size_t encode_mfma_smem(const CbShape& s) {
-  return (size_t)MF_WAVES * s.R * 256 * 16 + (size_t)MF_TOKENS * s.R * s.G;
+  return (size_t)MF_WAVES * mf_slot(s.R) * 16 + (size_t)MF_TOKENS * s.R * s.G;
 }
 
 // sum of the eight fp16 products a_i b_i (each exact in fp32) onto acc
@@ -191,11 +229,12 @@ __device__ __forceinline__ float mf_dot8(const uint4 a, const uint4 b, float acc
 }
 
 // Workgroup = (tile of 256 tokens, KV head). Wavefront w takes groups w, w+4,
-// ...; for a group it keeps the A operands of all R rounds (16 blocks of 16
-// entries each) in registers, stages the group's codebook in its own LDS slot
-// and streams the tile's tokens through the A operands, 16 at a time: lane
-// (q = lane / 16, n = lane % 16) feeds K slice q of token n and receives the
-// scores of entries 16 b + 4 q + i (i < 4) of block b for token n.
+// ...; for a group it stages the negated entries, their |c|^2 / 2 and round
+// 1's K-slice-2 operands in its own LDS slot, keeps round 0's A operands (16
+// blocks of 16 entries) in registers, reads round 1's from the slot per use,
+// and streams the tile's tokens through them, two batches of 16 interleaved:
+// lane (q = lane / 16, n = lane % 16) feeds K slice q of token n and receives
+// the scores of entries 16 b + 4 q + i (i < 4) of block b for token n.
 //
 // The scores carry a per-token constant C >= |e|^2 / 2 (K slice 2 holds
 // 4096 * C_h, C_h an fp16 rounded upward), which makes every score a
@@ -203,133 +242,145 @@ __device__ __forceinline__ float mf_dot8(const uint4 a, const uint4 b, float acc
 // values >= 0 compare like their bit patterns as signed integers, so the
 // search runs on integer min3. Per lane it keeps the smallest score and the
 // block holding it; the four lanes of a token then agree on the quad of four
-// entries (block, q) with the smallest score, lowest first on equal scores.
+// entries (block, q) with the smallest score.
 // Which entry of the quad won is settled by the four lanes rescoring one
 // entry each in fp32 (fp16 products, exact, summed in fp32): the two
 // evaluations can disagree only where two entries' scores agree to within
 // fp32 rounding (a near tie).
-template <int R>
+template <int R, bool POS>
 __global__ __launch_bounds__(MF_THREADS, 2) void encode_mfma_kernel(EncodeArgs a) {
-  extern __shared__ uint4 mf_smem[];  // [waves][R][256] codebook slots, then [MF_TOKENS][R * G] codes
+  static_assert(R == 1 || R == 2, "one or two rounds");
+  extern __shared__ uint4 mf_smem[];  // [waves] slots, then [MF_TOKENS][R * G] codes
   const CbShape s = a.s;
   const int G = s.G, RG = R * s.G;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, n = lane & 15;
-  uint4* cbw = mf_smem + wave * (R * 256);
-  uint8_t* mf_rec = reinterpret_cast<uint8_t*>(mf_smem + MF_WAVES * R * 256);
+  uint4* ncw = mf_smem + wave * mf_slot(R);  // [R][256] negated entries
+  float* nrw = reinterpret_cast<float*>(ncw + R * 256);  // [R][256] |c|^2 / 2
+  uint4* k2w = ncw + R * 256 + R * 64;  // [R - 1][256] K slice 2 of round 1's A operands
+  uint8_t* mf_rec = reinterpret_cast<uint8_t*>(mf_smem + MF_WAVES * mf_slot(R));
   const int h = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * MF_TOKENS;
   const uint4 zero4 = {0u, 0u, 0u, 0u};
+  const uint32_t qm[3] = {q == 0 ? ~0u : 0u, q == 1 ? ~0u : 0u, q == 2 ? ~0u : 0u};
 
   for (int j = wave; j < G; j += MF_WAVES) {
     // the slot is written and read by this wavefront only, in program order
     const uint4* cbj = reinterpret_cast<const uint4*>(a.cb + ((int64_t)h * G + j) * R * 256 * 8);
-    for (int i = lane; i < R * 256; i += 64) cbw[i] = cbj[i];
+    for (int i = lane; i < R * 256; i += 64) {
+      const h8_t c = __builtin_bit_cast(h8_t, cbj[i]);
+      float v = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v = fmaf((float)c[k], (float)c[k], v);
+      v *= 0.5f;
+      ncw[i] = __builtin_bit_cast(uint4, -c);
+      nrw[i] = v;
+      if (R == 2 && i >= 256) k2w[i - 256] = __builtin_bit_cast(uint4, k_slice2(v));
+    }
     // A operands: rows = 16 entries of a block,
-    // K = [-c (q 0), -c (q 1), |c|^2/2 as three parts and 4096 (q 2), 0 (q 3)]
-    h8_t A[R][16];
+    // K = [-c (q 0), -c (q 1), |c|^2/2 as three parts and 4096 (q 2), 0 (q 3)];
+    // round 0's in registers, round 1's read from the slot per use (the
+    // lanes of K slice 3 read entries there: B is 0 in that slice)
+    h8_t A0[16];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int b = 0; b < 16; ++b) {
-        const h8_t c = __builtin_bit_cast(h8_t, cbw[r * 256 + 16 * b + n]);
-        float v = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v = fmaf((float)c[i], (float)c[i], v);
-        v *= 0.5f;
-        const _Float16 v0 = (_Float16)v;
-        const float r1 = v - (float)v0;
-        const _Float16 v1 = (_Float16)r1;
-        const _Float16 v2 = (_Float16)(r1 - (float)v1);
-        const h8_t nrm = {v0, v1, v2, (_Float16)kMfCScale, 0, 0, 0, 0};
-        A[r][b] = q < 2 ? -c : (q == 2 ? nrm : h8_t{});
+    for (int b = 0; b < 16; ++b) {
+      const int en = 16 * b + n;
+      A0[b] = q < 2 ? __builtin_bit_cast(h8_t, ncw[en]) : (q == 2 ? k_slice2(nrw[en]) : h8_t{});
+    }
+    const uint4* a1 = (q == 2 ? k2w : ncw + 256) + n;
+    // group j of token n of batch tb (zero for tokens past the end or
+    // skipped); the input pointer advances by a fixed stride per batch. The
+    // loads are unconditional (clamped to token 0) so that the batches'
+    // instruction streams can interleave.
+    const int64_t tok_stride = POS ? (int64_t)s.Hkv * s.D : a.x_token_stride;
+    const _Float16* xg = a.x + (t0 + n) * tok_stride + (int64_t)h * s.D + 8 * j;
+    const int64_t left = a.n_tokens - t0 - n;
+    // (the raw load and its validity: the zeroing waits for the use)
+    auto fetch = [&](int tb, bool& ok) -> uint4 {
+      ok = 16 * tb < left;
+      if constexpr (POS) {
+        const int pos = a.positions[ok ? t0 + n + 16 * tb : 0];
+        ok = ok && pos >= 0 && pos < a.cache_len;
       }
-    // group j of token n of batch tb (zero for tokens past the end or skipped)
-    auto fetch = [&a, &s, t0, n, h, j](int tb) -> uint4 {
-      const int64_t t = t0 + 16 * tb + n;
-      bool ok = t < a.n_tokens;
-      const _Float16* xp = a.x;
-      if (ok) {
-        if (a.positions) {
-          const int pos = a.positions[t];
-          ok = pos >= 0 && pos < a.cache_len;
-          xp = a.x + (t * s.Hkv + h) * (int64_t)s.D;
-        } else {
-          xp = a.x + t * a.x_token_stride + (int64_t)h * s.D;
-        }
-      }
-      uint4 v = {0u, 0u, 0u, 0u};
-      if (ok) v = *reinterpret_cast<const uint4*>(xp + 8 * j);
-      return v;
+      return *reinterpret_cast<const uint4*>(ok ? xg + 16 * tb * tok_stride : a.x + 8 * j);
     };
-    uint4 xnext = fetch(0);
+    uint4 xnext[MF_NB];
+    bool oknext[MF_NB];
+#pragma unroll
+    for (int u = 0; u < MF_NB; ++u) xnext[u] = fetch(u, oknext[u]);
 #pragma unroll 1
-    for (int tb = 0; tb < MF_TOKENS / 16; ++tb) {
-      const int tl = 16 * tb + n;
-      const uint4 xw = xnext;
-      if (tb + 1 < MF_TOKENS / 16) xnext = fetch(tb + 1);  // in flight during this batch
-      // |x|^2 of finite fp16 values stays below 2^36; a NaN or an infinity in
-      // the group makes it NaN or infinite, and such a group takes entry 0 in
-      // every round (it has no finite distance to any entry)
-      const bool non_finite = !(mf_dot8(xw, xw, 0.f) <= 0x1p36f);
-      float e[8];  // residual of the later rounds, fp32
+    for (int tb = 0; tb < MF_TOKENS / 16; tb += MF_NB) {
+      uint4 xw[MF_NB], yw[MF_NB];
+      float xx[MF_NB], ee[MF_NB], slack[MF_NB];  // ee ~ |e|^2, slack >= its rounding error
+      bool non_finite[MF_NB];
+#pragma unroll
+      for (int u = 0; u < MF_NB; ++u) {
+        const uint32_t keep = oknext[u] ? ~0u : 0u;
+        xw[u] = make_uint4(xnext[u].x & keep, xnext[u].y & keep, xnext[u].z & keep, xnext[u].w & keep);
+        if (tb + MF_NB < MF_TOKENS / 16) xnext[u] = fetch(tb + MF_NB + u, oknext[u]);  // in flight during these batches
+        // |x|^2 of finite fp16 values stays below 2^36; a NaN or an infinity
+        // in the group makes it NaN or infinite, and such a group takes
+        // entry 0 in every round (it has no finite distance to any entry)
+        xx[u] = mf_dot8(xw[u], xw[u], 0.f);
+        non_finite[u] = !(xx[u] <= 0x1p36f);
+        // Round r's residual is e = x + y with y = 0 (round 0) or -c0
+        // (round 1, c0 the round-0 entry): both fp16, so the products with an
+        // entry are exact and e needs no splitting.
+        yw[u] = zero4;
+        ee[u] = xx[u];
+        slack[u] = 0.f;
+      }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        uint4 hw, lw;  // e = hi + lo in fp16
-        float ee;      // |e|^2
-        if (r == 0) {  // the input itself is fp16: hi = x, lo = 0
-          hw = xw;
-          lw = zero4;
-          ee = mf_dot8(xw, xw, 0.f);
-        } else {
-          h8_t hi, lo;
-          ee = 0.f;
+        h8_t bv[MF_NB];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            hi[i] = (_Float16)e[i];
-            lo[i] = (_Float16)(e[i] - (float)hi[i]);
-            ee = fmaf(e[i], e[i], ee);
-          }
-          hw = __builtin_bit_cast(uint4, hi);
-          lw = __builtin_bit_cast(uint4, lo);
+        for (int u = 0; u < MF_NB; ++u) {
+          // C_h >= |e|^2 / 8192: the 2^-8 factor covers the rounding of the
+          // conversion, slack the cancellation in |x|^2 - 2 x.c0 + |c0|^2,
+          // and the 2^-24 term the subnormal range
+          const _Float16 ch = (_Float16)fmaf(ee[u], 0x1.01p-13f, slack[u] + 0x1p-24f);
+          const h2_t one_c = {(_Float16)1.f, ch};
+          const uint4 cw = make_uint4(0x3C003C00u, __builtin_bit_cast(uint32_t, one_c), 0u, 0u);
+          bv[u] = b_operand(qm, xw[u], yw[u], cw);
         }
-        // C_h >= |e|^2 / 8192: the 2^-10 factor covers the rounding of ee and
-        // of the conversion (normal range), the 2^-24 term the subnormal range
-        const _Float16 ch = (_Float16)fmaf(ee, 0x1.004p-13f, 0x1p-24f);
-        const h2_t one_c = {(_Float16)1.f, ch};
-        const uint4 cw = make_uint4(0x3C003C00u, __builtin_bit_cast(uint32_t, one_c), 0u, 0u);
-        const uint4 bw = q == 0 ? hw : (q == 1 ? lw : (q == 2 ? cw : zero4));
-        const h8_t bv = __builtin_bit_cast(h8_t, bw);
-        int best = 0x7fffffff, bb = 0;
+        int best[MF_NB], bb[MF_NB];
+#pragma unroll
+        for (int u = 0; u < MF_NB; ++u) best[u] = 0x7fffffff, bb[u] = 0;
 #pragma unroll
         for (int b = 0; b < 16; ++b) {
-          const f4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[r][b], bv, (f4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          const int m3 = min(min(__float_as_int(d[0]), __float_as_int(d[1])), __float_as_int(d[2]));
-          const int nb = min(min(best, m3), __float_as_int(d[3]));
-          bb = nb < best ? b : bb;
-          best = nb;
+          const h8_t Ab = r == 0 ? A0[b] : __builtin_bit_cast(h8_t, a1[16 * b]);
+#pragma unroll
+          for (int u = 0; u < MF_NB; ++u) {
+            const f4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ab, bv[u], (f4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            const int m3 = min(min(__float_as_int(d[0]), __float_as_int(d[1])), __float_as_int(d[2]));
+            const int nb = min(min(best[u], m3), __float_as_int(d[3]));
+            bb[u] = nb < best[u] ? b : bb[u];
+            best[u] = nb;
+          }
         }
-        // the four lanes of token n: smallest (score, quad), quad = 4 block + q
-        int quad = 4 * bb + q;
-        lex_min_lanes<16>(best, quad);
-        lex_min_lanes<32>(best, quad);
-        // entries 16 (quad / 4) + 4 (quad % 4) + i, i < 4: lane q rescoring entry i = q
-        const int k0 = 16 * (quad >> 2) + 4 * (quad & 3);
-        const uint4 cq = cbw[r * 256 + k0 + q];
-        float sc = 0.5f * mf_dot8(cq, cq, 0.f) - mf_dot8(cq, lw, mf_dot8(cq, hw, 0.f));
-        int ki = q;
-        lex_min_lanes<16>(sc, ki);
-        lex_min_lanes<32>(sc, ki);
-        const int bi = non_finite ? 0 : k0 + ki;
-        if (q == 0) mf_rec[tl * RG + r * G + j] = (uint8_t)bi;
-        if (r + 1 < R) {
-          const h8_t c = __builtin_bit_cast(h8_t, cbw[r * 256 + bi]);
-          if (r == 0) {
-            const h8_t x8 = __builtin_bit_cast(h8_t, xw);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) e[i] = (float)x8[i] - (float)c[i];
-          } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) e[i] -= (float)c[i];
+        for (int u = 0; u < MF_NB; ++u) {
+          // the four lanes of token n agree on the quad (4 block + q) with
+          // the smallest score
+          int quad = 4 * bb[u] + q;
+          min_lanes<16>(best[u], quad);
+          min_lanes<32>(best[u], quad);
+          // entries 16 (quad / 4) + 4 (quad % 4) + i, i < 4: lane q rescoring entry i = q
+          const int k0 = 16 * (quad >> 2) + 4 * (quad & 3);
+          const uint4 cq = ncw[r * 256 + k0 + q];  // -c
+          float dot = mf_dot8(cq, xw[u], 0.f);
+          if (r > 0) dot = mf_dot8(cq, yw[u], dot);
+          float sc = nrw[r * 256 + k0 + q] + dot;
+          int ki = q;
+          min_lanes<16>(sc, ki, true, q & 2, q | 1);
+          min_lanes<32>(sc, ki);
+          const int bi = non_finite[u] ? 0 : k0 + ki;
+          // the token's four lanes store the same byte
+          mf_rec[(16 * (tb + u) + n) * RG + r * G + j] = (uint8_t)bi;
+          if (r + 1 < R) {
+            yw[u] = ncw[bi];
+            const float cc = 2.f * nrw[bi];
+            ee[u] = fmaf(2.f, mf_dot8(xw[u], yw[u], 0.f), xx[u] + cc);
+            slack[u] = (xx[u] + cc) * 0x1p-30f;
           }
         }
       }
@@ -341,7 +392,7 @@ __global__ __launch_bounds__(MF_THREADS, 2) void encode_mfma_kernel(EncodeArgs a
     const int64_t t = t0 + tl;
     if (t >= a.n_tokens) break;
     uint8_t* rec;
-    if (a.positions) {
+    if (POS) {
       const int pos = a.positions[t];
       if (pos < 0 || pos >= a.cache_len) continue;
       rec = a.codes + t * a.code_token_stride + h * a.code_head_stride + (int64_t)pos * s.bpt;
@@ -369,17 +420,23 @@ hipError_t launch_encode_g(const EncodeArgs& a, hipStream_t stream) {
       const int64_t nblk = (a.n_tokens + MF_TOKENS - 1) / MF_TOKENS;
       if (nblk > 0x7fffffff) return hipErrorInvalidValue;
       const size_t smem = encode_mfma_smem(a.s);
-      static std::atomic<uint64_t> configured1{0}, configured2{0};
-      const void* fn = a.s.R == 1 ? reinterpret_cast<const void*>(&encode_mfma_kernel<1>)
-                                  : reinterpret_cast<const void*>(&encode_mfma_kernel<2>);
+      static std::atomic<uint64_t> configured[4];
+      const int v = (a.s.R == 2 ? 2 : 0) + (a.positions ? 1 : 0);
+      const void* fns[4] = {reinterpret_cast<const void*>(&encode_mfma_kernel<1, false>),
+                            reinterpret_cast<const void*>(&encode_mfma_kernel<1, true>),
+                            reinterpret_cast<const void*>(&encode_mfma_kernel<2, false>),
+                            reinterpret_cast<const void*>(&encode_mfma_kernel<2, true>)};
       if (smem > 64 * 1024) {
-        const hipError_t e = allow_full_lds(fn, a.s.R == 1 ? configured1 : configured2);
+        const hipError_t e = allow_full_lds(fns[v], configured[v]);
         if (e != hipSuccess) return e;
       }
-      if (a.s.R == 1)
-        hipLaunchKernelGGL(encode_mfma_kernel<1>, dim3((unsigned)nblk, a.s.Hkv), dim3(MF_THREADS), smem, stream, a);
-      else
-        hipLaunchKernelGGL(encode_mfma_kernel<2>, dim3((unsigned)nblk, a.s.Hkv), dim3(MF_THREADS), smem, stream, a);
+      const dim3 grid((unsigned)nblk, a.s.Hkv), block(MF_THREADS);
+      switch (v) {
+        case 0: hipLaunchKernelGGL((encode_mfma_kernel<1, false>), grid, block, smem, stream, a); break;
+        case 1: hipLaunchKernelGGL((encode_mfma_kernel<1, true>), grid, block, smem, stream, a); break;
+        case 2: hipLaunchKernelGGL((encode_mfma_kernel<2, false>), grid, block, smem, stream, a); break;
+        default: hipLaunchKernelGGL((encode_mfma_kernel<2, true>), grid, block, smem, stream, a); break;
+      }
       return hipGetLastError();
     }
   }
