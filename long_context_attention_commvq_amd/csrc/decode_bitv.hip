@@ -17,9 +17,11 @@
 //     A = 16 query heads x 32 positions of weights (one 16-byte load per lane),
 //     B = 32 positions x 16 bits, for the 8 bit tiles of the range;
 //   - the B operand is built in registers from the lane's 8 positions' 16 code
-//     bytes: a rotate puts the lane's bit n of each half-word at bits 14 and
-//     30, and a byte permute plus a mask makes each fp16 pair 2.0 or 0, so one
-//     operand dword costs two instructions;
+//     bytes (staged in LDS by direct copies, six k-steps ahead): a byte
+//     permute moves the byte holding the lane's bit n of two positions'
+//     half-words to the low bytes and a mask keeps that bit, which makes each
+//     fp16 the subnormal 2^((n & 7) - 24) or 0 (exact in the products; the
+//     scale is undone in fp32), so one operand dword costs two instructions;
 //   - the eight wavefronts' u are added through LDS and written to the
 //     (chunk, range) partial slot;
 //   - the grid puts range r of chunk c at r * chunks + c; workgroups go to the
@@ -41,6 +43,7 @@ constexpr int kBvD = 128;       // head_dim of the fast path
 
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // NHT tiles of 16 query heads (Hq <= 16 NHT)
 template <int NHT>
@@ -59,73 +62,90 @@ __global__ __launch_bounds__(kBvThreads, 1) void bitv_values_kernel(DecodeArgs a
   const int m0 = c * a.chunk;
   if (m0 >= L) return;  // the score kernel wrote this chunk's empty partials
   const int nks = (min(m0 + a.chunk, L) - m0 + 31) / 32;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the k-step branches stay scalar
   const int n = lane & 15, kg = lane >> 4;
-  const uint32_t rot = (uint32_t)((n + 18) & 31);  // bit n -> 14, bit 16 + n -> 30
+  // B operand half-words: the byte holding the lane's bit n of a code
+  // half-word, moved to the low byte and masked to that bit, is the fp16
+  // 2^((n & 7) - 24) (a subnormal, exact in the products) or 0
+  const uint32_t jn = (uint32_t)(n >> 3);
+  const uint32_t selh[2] = {0x0C040C00u + jn * 0x00010001u, 0x0C060C02u + jn * 0x00010001u};
+  const uint32_t bmask = (1u << (n & 7)) * 0x00010001u;
   const int nby = a.nbits / 8;
   const size_t plen = (size_t)npc * a.chunk;
   const uint8_t* vb = a.vbits + (size_t)b * a.cache_len * nby + 16 * r;
   const _Float16* pwb = a.pw + (size_t)b * a.Hq * plen;
 
-  // operands of k-step ks (32 positions): the weights of heads 16 ht + n at
-  // positions kb..kb+7 (a head past Hq reads row 0 and is zeroed by a select),
-  // and the range's 16 code bytes of those 8 positions (clamped into the cache;
-  // positions past the sequence have weight 0). Two k-steps are in flight ahead
-  // of the one in use.
-  struct Ops {
-    h8_t a[NHT];
-    u32x4 x[8];
-  };
-  auto load = [&](Ops& o, int ks) {
-    const int kb = m0 + 32 * ks + 8 * kg;
+  // operands of the wavefront's k-step kk (ks = wave + 8 kk, 32 positions):
+  // the range's 16 code bytes of each position, copied straight into an LDS
+  // slot of the wavefront's ring (lane l and l + 32 copy position l; clamped
+  // into the cache, positions past the sequence have weight 0), and the
+  // weights of heads 16 ht + n at positions kb..kb+7 into a register slot (a
+  // head past Hq reads row 0; its rows of u are never stored). Every load is
+  // unconditional, so the wait counts below are exact. kBvAhead k-steps are in
+  // flight ahead of the one in use.
+  constexpr int kBvAhead = 6;
+  constexpr int kBvSlots = kBvAhead + 1;
+  static_assert(kBvWaves * kBvSlots * 1024 <= R0, "bit rings fit the partials' LDS");
+  char* ring = r0 + wave * (kBvSlots * 1024);
+  h8_t wa[kBvSlots][NHT];
+  auto issue = [&](int kk) {
+    const int slot = kk % kBvSlots;
+    const int kb0 = m0 + 32 * (wave + kBvWaves * kk);
+    __builtin_amdgcn_global_load_lds(vb + (size_t)min(kb0 + (lane & 31), a.cache_len - 1) * nby,
+                                     (lds_void_t*)(ring + slot * 1024), 16, 0, 0);
+    const int kb = kb0 + 8 * kg;
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       const int head = 16 * ht + n;
-      const h8_t v = *reinterpret_cast<const h8_t*>(pwb + (size_t)(head < a.Hq ? head : 0) * plen + kb);
-      o.a[ht] = head < a.Hq ? v : (h8_t){0, 0, 0, 0, 0, 0, 0, 0};
+      wa[slot][ht] = *reinterpret_cast<const h8_t*>(pwb + (size_t)(head < a.Hq ? head : 0) * plen + kb);
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      o.x[j] = *reinterpret_cast<const u32x4*>(vb + (size_t)min(kb + j, a.cache_len - 1) * nby);
   };
   float4_t acc[NHT][8];
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[ht][t] = (float4_t){0.f, 0.f, 0.f, 0.f};
-  auto step = [&](const Ops& o) {
-    uint32_t y[8][4];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) y[j][q] = __builtin_amdgcn_alignbit(o.x[j][q], o.x[j][q], rot);
+  auto step = [&](const h8_t (&w)[NHT], const u32x4 (&x)[8]) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int q = t >> 1;
-      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;  // high or low half-words
+      const uint32_t sel = selh[t & 1];  // the low or high half-words of positions 2e, 2e + 1
       u32x4 bw;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bw[e] = __builtin_amdgcn_perm(y[2 * e + 1][q], y[2 * e][q], sel) & 0x40004000u;
+      for (int e = 0; e < 4; ++e) bw[e] = __builtin_amdgcn_perm(x[2 * e + 1][q], x[2 * e][q], sel) & bmask;
       const h8_t bop = __builtin_bit_cast(h8_t, bw);
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht)
-        acc[ht][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(o.a[ht], bop, acc[ht][t], 0, 0, 0);
+        acc[ht][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w[ht], bop, acc[ht][t], 0, 0, 0);
     }
   };
   // A wavefront has at most 4096 / 32 / 8 = 16 k-steps; the loop is unrolled so
-  // that the three operand slots are fixed registers (no copies between
-  // iterations): slot (kk + 2) % 3 is refilled while slot kk % 3 is used.
+  // that the slots are fixed registers and LDS offsets.
   static_assert(4096 / 32 / kBvWaves == 16, "k-steps per wavefront");
-  Ops ring[3];
-  if (wave < nks) load(ring[0], wave);
-  if (wave + kBvWaves < nks) load(ring[1], wave + kBvWaves);
+#pragma unroll
+  for (int kk = 0; kk < kBvAhead; ++kk)
+    if (wave + kBvWaves * kk < nks) issue(kk);
 #pragma unroll
   for (int kk = 0; kk < 16; ++kk) {
     const int ks = wave + kBvWaves * kk;
     if (ks >= nks) break;  // (uniform in the wavefront)
-    if (ks + 2 * kBvWaves < nks) load(ring[(kk + 2) % 3], ks + 2 * kBvWaves);
-    step(ring[kk % 3]);
+    const bool more = ks + kBvWaves * kBvAhead < nks;
+    if (more) issue(kk + kBvAhead);
+    // k-step kk's copy has landed once at most the later k-steps' loads (one
+    // copy and NHT weight loads each) are outstanding; the compiler does not
+    // track the copy's LDS writes, so the wait is explicit
+    if (more)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kBvAhead * (1 + NHT)) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const char* sl = ring + (kk % kBvSlots) * 1024;
+    u32x4 x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = *reinterpret_cast<const u32x4*>(sl + (8 * kg + j) * 16);
+    step(wa[kk % kBvSlots], x);
   }
+  __syncthreads();  // the rings share LDS with the partials
 
   // lane holds u[16 ht + 4 kg + i][16 t + n] (times 2)
 #pragma unroll
@@ -143,7 +163,7 @@ __global__ __launch_bounds__(kBvThreads, 1) void bitv_values_kernel(DecodeArgs a
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < kBvWaves; ++w) sum += usum[(w * HP + head) * kBvRow + bit];
-    pr[(size_t)head * a.n_chunks * (kBvD + 2) + bit] = 0.5f * sum;  // the bits entered as 2.0
+    pr[(size_t)head * a.n_chunks * (kBvD + 2) + bit] = ldexpf(sum, 24 - (bit & 7));  // the bits entered as 2^((bit & 7) - 24)
   }
 }
 
@@ -176,6 +196,16 @@ __global__ __launch_bounds__(kBmThreads) void bitv_merge_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < 32; ++i)
     if (i < rows) cv[i] = col[(size_t)i * (dimc / 2)];
+  // the lane's bit i0 in the first kBmU chunks, requested before the chunk
+  // statistics are reduced (the values do not depend on them)
+  constexpr int kBmU = 32;
+  const int i0 = tid, i1 = tid + kBmThreads;  // the lane's bits (nbits <= 2048)
+  float u_first[kBmU];
+  {
+    const float* q = pr + (size_t)(i0 / kBvRange) * cs + 2 + i0 % kBvRange;
+#pragma unroll
+    for (int k = 0; k < kBmU; ++k) u_first[k] = i0 < a.nbits && k < npc ? q[(size_t)k * NR * cs] : 0.f;
+  }
   // M = max_c M_c; the lane's chunk of the first kBmThreads keeps its (M_c, l_c)
   const float m_first = tid < npc ? pr[(size_t)tid * NR * cs] : -INFINITY;
   const float l_first = tid < npc ? pr[(size_t)tid * NR * cs + 1] : 0.f;
@@ -190,7 +220,6 @@ __global__ __launch_bounds__(kBmThreads) void bitv_merge_kernel(DecodeArgs a) {
   // U[i] = sum_c w_c u_c[i], w_c = e^{M_c - M} (0 for an empty chunk, whose
   // slots hold zeros), chunks taken kBmThreads at a time, their weights in LDS
   float ls = 0.f, acc0 = 0.f, acc1 = 0.f;
-  const int i0 = tid, i1 = tid + kBmThreads;  // the lane's bits (nbits <= 2048)
   for (int c0 = 0; c0 < npc; c0 += kBmThreads) {
     __syncthreads();
     {
@@ -207,10 +236,10 @@ __global__ __launch_bounds__(kBmThreads) void bitv_merge_kernel(DecodeArgs a) {
     }
     __syncthreads();
     const int nc = min(kBmThreads, npc - c0);
-    auto sweep = [&](int i, float& acc) {
+    auto sweep = [&](int i, float& acc, int kfrom) {
       const int r = i / kBvRange, bit = i % kBvRange;
       const float* q = pr + ((size_t)c0 * NR + r) * cs + 2 + bit;
-      for (int k0 = 0; k0 < nc; k0 += 16) {
+      for (int k0 = kfrom; k0 < nc; k0 += 16) {
         float uv[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) uv[k] = k0 + k < nc ? q[(size_t)(k0 + k) * NR * cs] : 0.f;
@@ -218,8 +247,14 @@ __global__ __launch_bounds__(kBmThreads) void bitv_merge_kernel(DecodeArgs a) {
         for (int k = 0; k < 16; ++k) acc = fmaf(k0 + k < nc ? wsh[k0 + k] : 0.f, uv[k], acc);
       }
     };
-    if (i0 < a.nbits) sweep(i0, acc0);
-    if (i1 < a.nbits) sweep(i1, acc1);
+    int kfrom = 0;
+    if (c0 == 0) {  // the preloaded chunks (wsh is 0 past nc)
+#pragma unroll
+      for (int k = 0; k < kBmU; ++k) acc0 = fmaf(wsh[k], u_first[k], acc0);
+      kfrom = kBmU;
+    }
+    if (i0 < a.nbits) sweep(i0, acc0, kfrom);
+    if (i1 < a.nbits) sweep(i1, acc1, 0);
   }
   if (i0 < a.nbits) U[i0] = acc0;
   if (i1 < a.nbits) U[i1] = acc1;
@@ -240,10 +275,14 @@ __global__ __launch_bounds__(kBmThreads) void bitv_merge_kernel(DecodeArgs a) {
     }
   osum[p][dp] = make_float2(o0, o1);
   __syncthreads();
-  if (tid < DQ) {
-    float o = 0.f;
-    for (int q = 0; q < NP; ++q) o += (tid & 1) ? osum[q][tid >> 1].y : osum[q][tid >> 1].x;
-    a.out[((size_t)b * a.Hq + hq) * kBvD + dq0 + tid] = Ls > 0.f ? o / Ls : 0.f;
+  // wavefront w adds the 64 parts of dimensions 2 w and 2 w + 1, a part per lane
+  static_assert(NP == 64 && DQ == 2 * (kBmThreads / 64), "a lane per part, two dimensions per wavefront");
+  const float2 v = osum[lane][wave];
+  const float ox = wave_sum(v.x), oy = wave_sum(v.y);
+  if (lane == 0) {
+    float* o = a.out + ((size_t)b * a.Hq + hq) * kBvD + dq0 + 2 * wave;
+    o[0] = Ls > 0.f ? ox / Ls : 0.f;
+    o[1] = Ls > 0.f ? oy / Ls : 0.f;
   }
 }
 
