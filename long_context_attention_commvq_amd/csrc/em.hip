@@ -17,16 +17,17 @@
 // encoder (codes of a batch into the work buffer) and em_scatter_kernel per
 // batch; then em_update_kernel.
 //
-// em_accumulate_kernel<g>: a workgroup per (256 vectors, KV head) walks the
-// groups; per group it stages rounds 0..r of the codebook (fp32) and the 256
-// vectors' residuals in LDS. For 16 vectors at a time, thread l computes the
+// em_accumulate_kernel<g>: a workgroup per (1024 vectors, KV head) walks the
+// groups; per group it stages rounds 0..r of the codebook (fp32), then for
+// each tile of 256 vectors their residuals, in LDS. For 16 vectors at a time, thread l computes the
 // distances to entry l; each wavefront reduces four vectors' rows (minimum
 // and its lowest index). For an earlier round the residuals are then reduced
 // by their nearest entries; for the fitted round at temperature 0 the
 // wavefront adds the vector and a count of 1 to its nearest entry's sums in
 // LDS (fp32 LDS atomics), and at temperature > 0 it also sums the row's soft
 // weights, after which thread l adds w_nl e_n and w_nl in registers. The
-// workgroup's sums go to the accumulators with fp32 atomics.
+// workgroup's sums go to the accumulators with fp32 atomics, once per group
+// after its four tiles.
 
 #include "commvq_internal.hpp"
 
@@ -34,6 +35,7 @@ namespace commvq {
 namespace {
 
 constexpr int kEmThreads = 256, kEmTokens = 256, kEmSub = 16;
+constexpr int kEmTiles = 4;  // tiles of kEmTokens vectors per workgroup, one flush of the sums per group
 constexpr size_t kEmCodeScratch = size_t(4) << 20;  // codes of one encoder batch (nearest-entry path)
 
 __device__ __forceinline__ float em_wave_sum(float v) {
@@ -52,8 +54,7 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
   const CbShape s = a.s;
   const int Nc = s.Nc, G = s.G, r = a.round;
   const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t0 = (int64_t)blockIdx.x * kEmTokens;
-  const int nt = (int)min((int64_t)kEmTokens, a.n_tokens - t0);
+  const int64_t tw = (int64_t)blockIdx.x * kEmTokens * kEmTiles;
   float* cbf = em_smem;                          // [r + 1][Nc][GS]
   float* res = cbf + (size_t)(r + 1) * Nc * GS;  // [kEmTokens][GS]
   float* dist = res + kEmTokens * GS;            // [kEmSub][Nc]
@@ -67,85 +68,91 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
     __syncthreads();  // the previous group's reads of LDS are done
     const _Float16* cbj = a.cb + ((size_t)h * G + j) * s.R * Nc * GS;
     for (int i = tid; i < (r + 1) * Nc * GS; i += kEmThreads) cbf[i] = (float)cbj[i];
-    for (int i = tid; i < kEmTokens * GS; i += kEmThreads) {
-      const int n = i / GS, k = i - n * GS;
-      res[i] = n < nt ? (float)a.x[(t0 + n) * a.x_token_stride + (int64_t)h * s.D + j * GS + k] : 0.f;
-    }
     if (!soft)
       for (int i = tid; i < Nc * (GS + 1); i += kEmThreads) hacc[i] = 0.f;
-    __syncthreads();
     float acc[GS + 1];
 #pragma unroll
     for (int k = 0; k <= GS; ++k) acc[k] = 0.f;
-    for (int n0 = 0; n0 < nt; n0 += kEmSub) {
-      const int ns = min(kEmSub, nt - n0);
-      for (int rr = 0; rr <= r; ++rr) {
-        const float* cr = cbf + (size_t)rr * Nc * GS;
-        const bool fitted = rr == r;
-        // distances: thread l to entry l, for the sub-tile's vectors
-        float dl[kEmSub];
-        if (tid < Nc) {
-          float c[GS];
+    for (int tile = 0; tile < kEmTiles; ++tile) {
+      const int64_t t0 = tw + (int64_t)tile * kEmTokens;
+      if (t0 >= a.n_tokens) break;  // (uniform)
+      const int nt = (int)min((int64_t)kEmTokens, a.n_tokens - t0);
+      __syncthreads();  // the previous tile's reads of the residuals are done
+      for (int i = tid; i < kEmTokens * GS; i += kEmThreads) {
+        const int n = i / GS, k = i - n * GS;
+        res[i] = n < nt ? (float)a.x[(t0 + n) * a.x_token_stride + (int64_t)h * s.D + j * GS + k] : 0.f;
+      }
+      __syncthreads();
+      for (int n0 = 0; n0 < nt; n0 += kEmSub) {
+        const int ns = min(kEmSub, nt - n0);
+        for (int rr = 0; rr <= r; ++rr) {
+          const float* cr = cbf + (size_t)rr * Nc * GS;
+          const bool fitted = rr == r;
+          // distances: thread l to entry l, for the sub-tile's vectors
+          float dl[kEmSub];
+          if (tid < Nc) {
+            float c[GS];
 #pragma unroll
-          for (int k = 0; k < GS; ++k) c[k] = cr[tid * GS + k];
+            for (int k = 0; k < GS; ++k) c[k] = cr[tid * GS + k];
 #pragma unroll
-          for (int n = 0; n < kEmSub; ++n) {
-            float d = 0.f;
+            for (int n = 0; n < kEmSub; ++n) {
+              float d = 0.f;
 #pragma unroll
-            for (int k = 0; k < GS; ++k) {
-              const float df = res[(n0 + n) * GS + k] - c[k];
-              d = fmaf(df, df, d);
+              for (int k = 0; k < GS; ++k) {
+                const float df = res[(n0 + n) * GS + k] - c[k];
+                d = fmaf(df, df, d);
+              }
+              dl[n] = d;
+              dist[n * Nc + tid] = d;
             }
-            dl[n] = d;
-            dist[n * Nc + tid] = d;
-          }
-        }
-        __syncthreads();
-        // rows: minimum and its lowest index; for the fitted round the soft
-        // weights' sum, or (nearest entry) the vector added to its entry's sums
-        for (int n = wave; n < kEmSub; n += kEmThreads / 64) {
-          float m = INFINITY;
-          int mi = 0;  // (a valid index even if every distance is infinite or NaN)
-          for (int l = lane; l < Nc; l += 64) {
-            const float v = dist[n * Nc + l];
-            if (v < m) m = v, mi = l;  // a lane's entries ascend: the first of equal ones is kept
-          }
-#pragma unroll
-          for (int o = 32; o > 0; o >>= 1) {
-            const float om = __shfl_xor(m, o, 64);
-            const int oi = __shfl_xor(mi, o, 64);
-            if (om < m || (om == m && oi < mi)) m = om, mi = oi;
-          }
-          if (fitted && soft) {
-            float sm = 0.f;
-            for (int l = lane; l < Nc; l += 64) sm += __expf((m - dist[n * Nc + l]) * invT);
-            sm = em_wave_sum(sm);
-            if (lane == 0) {
-              rmin[n] = m;
-              rsum[n] = sm;
-            }
-          } else if (fitted) {
-            if (n < ns && lane <= GS) atomicAdd(&hacc[mi * (GS + 1) + lane], lane < GS ? res[(n0 + n) * GS + lane] : 1.f);
-          } else if (lane == 0) {
-            rarg[n] = mi;
-          }
-        }
-        __syncthreads();
-        if (!fitted) {
-          for (int i = tid; i < ns * GS; i += kEmThreads) {
-            const int n = i / GS, k = i - n * GS;
-            res[(n0 + n) * GS + k] -= cr[rarg[n] * GS + k];
           }
           __syncthreads();
-        } else if (soft && tid < Nc) {
+          // rows: minimum and its lowest index; for the fitted round the soft
+          // weights' sum, or (nearest entry) the vector added to its entry's sums
+          for (int n = wave; n < kEmSub; n += kEmThreads / 64) {
+            float m = INFINITY;
+            int mi = 0;  // (a valid index even if every distance is infinite or NaN)
+            for (int l = lane; l < Nc; l += 64) {
+              const float v = dist[n * Nc + l];
+              if (v < m) m = v, mi = l;  // a lane's entries ascend: the first of equal ones is kept
+            }
 #pragma unroll
-          for (int n = 0; n < kEmSub; ++n) {
-            if (n < ns) {
-              const float w = __expf((rmin[n] - dl[n]) * invT) / rsum[n];
-              if (w != 0.f) {
+            for (int o = 32; o > 0; o >>= 1) {
+              const float om = __shfl_xor(m, o, 64);
+              const int oi = __shfl_xor(mi, o, 64);
+              if (om < m || (om == m && oi < mi)) m = om, mi = oi;
+            }
+            if (fitted && soft) {
+              float sm = 0.f;
+              for (int l = lane; l < Nc; l += 64) sm += __expf((m - dist[n * Nc + l]) * invT);
+              sm = em_wave_sum(sm);
+              if (lane == 0) {
+                rmin[n] = m;
+                rsum[n] = 1.f / sm;  // (sm >= 1: the nearest entry's term is 1)
+              }
+            } else if (fitted) {
+              if (n < ns && lane <= GS) atomicAdd(&hacc[mi * (GS + 1) + lane], lane < GS ? res[(n0 + n) * GS + lane] : 1.f);
+            } else if (lane == 0) {
+              rarg[n] = mi;
+            }
+          }
+          __syncthreads();
+          if (!fitted) {
+            for (int i = tid; i < ns * GS; i += kEmThreads) {
+              const int n = i / GS, k = i - n * GS;
+              res[(n0 + n) * GS + k] -= cr[rarg[n] * GS + k];
+            }
+            __syncthreads();
+          } else if (soft && tid < Nc) {
 #pragma unroll
-                for (int k = 0; k < GS; ++k) acc[k] = fmaf(w, res[(n0 + n) * GS + k], acc[k]);
-                acc[GS] += w;
+            for (int n = 0; n < kEmSub; ++n) {
+              if (n < ns) {
+                const float w = __expf((rmin[n] - dl[n]) * invT) * rsum[n];
+                if (w != 0.f) {
+#pragma unroll
+                  for (int k = 0; k < GS; ++k) acc[k] = fmaf(w, res[(n0 + n) * GS + k], acc[k]);
+                  acc[GS] += w;
+                }
               }
             }
           }
@@ -272,7 +279,7 @@ hipError_t launch_em_g(const EmArgs& a, hipStream_t stream) {
   static std::atomic<uint64_t> configured{0};
   e = allow_full_lds(reinterpret_cast<const void*>(&em_accumulate_kernel<GS>), configured);
   if (e != hipSuccess) return e;
-  const int64_t blocks = (a.n_tokens + kEmTokens - 1) / kEmTokens;
+  const int64_t blocks = (a.n_tokens + kEmTokens * kEmTiles - 1) / (kEmTokens * kEmTiles);
   if (blocks > INT32_MAX || s.Hkv > 65535) return hipErrorInvalidValue;
   hipLaunchKernelGGL((em_accumulate_kernel<GS>), dim3((unsigned)blocks, s.Hkv), dim3(kEmThreads), smem, stream, a);
   e = hipGetLastError();
