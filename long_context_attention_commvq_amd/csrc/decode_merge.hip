@@ -27,7 +27,10 @@ __global__ __launch_bounds__(T) void decode_merge_kernel(DecodeArgs a) {
   __shared__ float sc_new;
   const float* __restrict__ part = a.part;
   const int n_chunks = a.n_chunks, D = a.k.D, Hq = a.Hq;
-  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  // Workgroups go to the XCDs round-robin in launch order, and the decode
+  // kernels put KV head h's chunks on XCD h mod 8 (KV head fastest). Workgroup
+  // k Hkv + h merges query head h NH + k, on the XCD that wrote its partials.
+  const int hq = (blockIdx.x % a.k.Hkv) * a.NH + blockIdx.x / a.k.Hkv, b = blockIdx.y, tid = threadIdx.x;
   const size_t cs = (size_t)D + 2;
   const float* pr = part + ((size_t)b * Hq + hq) * (size_t)n_chunks * cs;
   const int lpd = kMergeThreads / D;  // lanes per dimension (D <= 256)
@@ -114,6 +117,7 @@ __global__ __launch_bounds__(T) void decode_merge_kernel(DecodeArgs a) {
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
   if (a.k.D > 256) return hipErrorInvalidValue;
+  if (a.k.Hkv < 1 || a.NH * a.k.Hkv != a.Hq) return hipErrorInvalidValue;  // (the head remap is a bijection)
   if (a.fold_new && (a.k.D != 128 || a.NH != 4)) return hipErrorInvalidValue;  // the fast kernel's shape
   if (a.n_chunks > 64)
     hipLaunchKernelGGL(decode_merge_kernel<1024>, dim3(a.Hq, a.B), dim3(1024), 0, stream, a);
