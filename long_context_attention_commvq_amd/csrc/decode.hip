@@ -50,6 +50,17 @@ __device__ __forceinline__ float add_f16_hi(float acc, uint32_t w) {
   return acc;
 }
 
+// acc + x * (the fp16 in the low / high half of w), one v_fma_mix_f32 (exact
+// conversion, one rounding: the same result as fmaf(x, (float)half, acc))
+__device__ __forceinline__ float fma_f16_lo(float acc, uint32_t w, float x) {
+  asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel_hi:[1,0,0]" : "+v"(acc) : "v"(w), "v"(x));
+  return acc;
+}
+__device__ __forceinline__ float fma_f16_hi(float acc, uint32_t w, float x) {
+  asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(acc) : "v"(w), "v"(x));
+  return acc;
+}
+
 __device__ __forceinline__ int read_field(const uint8_t* rec, int f, int bits) {
   const int o = f * bits, byte = o >> 3, sh = o & 7;
   uint32_t v = rec[byte];
@@ -78,14 +89,29 @@ __host__ __device__ inline size_t generic_uni_bytes(const CbShape& k, const CbSh
 // key and value records are copied to LDS once, so those reads wait on LDS
 // instead of on memory.
 // (only where they fit the LDS beside the rest)
-__host__ __device__ inline size_t generic_fixed_bytes(const CbShape& k, int NH) {
+__host__ __device__ inline size_t generic_base_fixed_bytes(const CbShape& k, int NH) {
   // rotated queries (float2 per pair), output accumulators, reductions
   const int P = k.D / 2, NW = generic_threads(NH, k.g) / 64;
   return (2 * NH * P + NH * k.D + ((NH * (NW > 2 ? NW : 2) + 2 * NH + 4) & ~3)) * sizeof(float);
 }
+// Wide groups with four query heads per KV head and D = 128 take their dot
+// products on the matrix cores (phase split: the wavefront's block phase in the
+// query, a lane-constant phase on the rebuilt key), with a table of the lane
+// phases e^{i d theta_p}, d < 64, in LDS beside the staged slice, where it fits.
+constexpr int kLanePhaseBytes = 64 * 64 * 8;  // [64 offsets][64 pairs] float2
+// (never at the cost of the record staging below: that measured the larger gain)
+__host__ __device__ inline bool generic_wide_mfma(const CbShape& k, const CbShape& v, int NH) {
+  const size_t base = generic_base_fixed_bytes(k, NH) + generic_uni_bytes(k, v, NH);
+  const bool stageable = k.bpt <= 32 && v.bpt <= 32 && base + (size_t)kGenericChunk * (k.bpt + v.bpt) <= 160 * 1024;
+  return k.g >= kWideGroup && NH == 4 && k.D == 128 &&
+         base + kLanePhaseBytes + (stageable ? (size_t)kGenericChunk * (k.bpt + v.bpt) : 0) <= 160 * 1024;
+}
+__host__ __device__ inline size_t generic_fixed_bytes(const CbShape& k, const CbShape& v, int NH) {
+  return generic_base_fixed_bytes(k, NH) + (generic_wide_mfma(k, v, NH) ? kLanePhaseBytes : 0);
+}
 __host__ __device__ inline bool generic_stage_records(const CbShape& k, const CbShape& v, int NH) {
   return k.g >= kWideGroup && k.bpt <= 32 && v.bpt <= 32 &&
-         generic_fixed_bytes(k, NH) + generic_uni_bytes(k, v, NH) + (size_t)kGenericChunk * (k.bpt + v.bpt) <=
+         generic_fixed_bytes(k, v, NH) + generic_uni_bytes(k, v, NH) + (size_t)kGenericChunk * (k.bpt + v.bpt) <=
              160 * 1024;
 }
 __host__ __device__ inline size_t generic_rec_bytes(const CbShape& k, const CbShape& v, int NH) {
@@ -139,7 +165,9 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
   float2* qz = reinterpret_cast<float2*>(sm);  // [NH][P]
   float* oacc = sm + 2 * NH * P;               // [NH][D]
   float* red = oacc + NH * D;                  // [NH][NW]
-  float* uni = red + red_floats;  // table or histogram
+  const bool wide_mfma = GS >= kWideGroup && NH == 4 && generic_wide_mfma(K, V, NH);
+  float2* lph = reinterpret_cast<float2*>(red + red_floats);  // lane phases (wide_mfma)
+  float* uni = red + red_floats + (wide_mfma ? kLanePhaseBytes / 4 : 0);  // table or histogram
   float2* table = reinterpret_cast<float2*>(uni);
   uint32_t* hist = reinterpret_cast<uint32_t*>(uni);
 
@@ -192,29 +220,114 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
       // [R][Nc][SL]: entry e's 16-byte chunk v at chunk slot 4 e + ((v + e / 4) & 3),
       // so that lanes reading chunk v of different entries spread over the banks
       _Float16* cbs = reinterpret_cast<_Float16*>(uni);
-      for (int j = 0; j < G; ++j) {
-        for (int sl = 0; sl < GS / SL; ++sl) {
-          __syncthreads();
-          const _Float16* src = a.kcb + ((size_t)h * G + j) * K.R * K.Nc * GS + sl * SL;  // entry (r, l) at (r Nc + l) GS
-          {
-            // four 16-byte loads in flight per lane
-            const int nv = K.R * K.Nc * (SL / 8);
-            for (int i0 = 0; i0 < nv; i0 += 4 * kThreads) {
-              uint4 w[4];
+      auto stage_slice = [&](int j, int sl) {
+        __syncthreads();
+        const _Float16* src = a.kcb + ((size_t)h * G + j) * K.R * K.Nc * GS + sl * SL;  // entry (r, l) at (r Nc + l) GS
+        // four 16-byte loads in flight per lane
+        const int nv = K.R * K.Nc * (SL / 8);
+        for (int i0 = 0; i0 < nv; i0 += 4 * kThreads) {
+          uint4 w[4];
 #pragma unroll
-              for (int u = 0; u < 4; ++u) {
-                const int i = i0 + u * kThreads + tid;
-                w[u] = i < nv ? *reinterpret_cast<const uint4*>(src + (size_t)(i / (SL / 8)) * GS + (i % (SL / 8)) * 8)
-                              : make_uint4(0u, 0u, 0u, 0u);
-              }
+          for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * kThreads + tid;
+            w[u] = i < nv ? *reinterpret_cast<const uint4*>(src + (size_t)(i / (SL / 8)) * GS + (i % (SL / 8)) * 8)
+                          : make_uint4(0u, 0u, 0u, 0u);
+          }
 #pragma unroll
-              for (int u = 0; u < 4; ++u) {
-                const int i = i0 + u * kThreads + tid, e = i / (SL / 8);
-                if (i < nv) reinterpret_cast<uint4*>(cbs)[e * 4 + ((i + (e >> 2)) & 3)] = w[u];
-              }
+          for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * kThreads + tid, e = i / (SL / 8);
+            if (i < nv) reinterpret_cast<uint4*>(cbs)[e * 4 + ((i + (e >> 2)) & 3)] = w[u];
+          }
+        }
+        __syncthreads();
+      };
+      // kx[0 .. SL) += every round's entry of group j's staged slice at m's codes
+      auto rebuild = [&](int m, int j, float (&kx)[SL]) {
+        for (int r = 0; r < K.R; ++r) {
+          const int code = kfield(m, r * G + j);
+          const int ei = r * K.Nc + code;
+          const uint4* e = reinterpret_cast<const uint4*>(cbs) + ei * 4;
+#pragma unroll
+          for (int v = 0; v < SL / 8; ++v) {
+            const uint4 w = e[(v + (ei >> 2)) & 3];
+            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              kx[8 * v + 2 * u] = add_f16_lo(kx[8 * v + 2 * u], wd[u]);
+              kx[8 * v + 2 * u + 1] = add_f16_hi(kx[8 * v + 2 * u + 1], wd[u]);
             }
           }
-          __syncthreads();
+        }
+      };
+      if constexpr (NH == 4 && !EX) {
+        if (wide_mfma) {
+          // Phase split (D = 128, one position per lane, m = m_b + d with m_b =
+          // m0 + 64 w): s_m = Re sum_p conj(q~_p e^{-i m_b theta_p}) (k_p e^{i d theta_p}),
+          // a real dot product over D between the wavefront's block-rotated query q'
+          // and the rebuilt key rotated by lane-constant phases, on
+          // v_mfma_f32_4x4x1f32: block b takes positions 4b..4b+3 of the wavefront
+          // as columns and the four query heads as rows; K-step k (dimension k)
+          // broadcasts block k % 16's A, so lane (block bq, row qi) holds head qi's
+          // q' for dimensions bq + 16 t only. fp32 operands and sums throughout.
+          // Lane phase table: chunk c (pairs 2c, 2c + 1) of row d at slot (c + d) & 31,
+          // so that the 64 lanes reading chunk c of their own rows spread over the banks.
+          for (int i = tid; i < 64 * 64; i += kThreads) {
+            const int d = i >> 6, p = i & 63;
+            lph[d * 64 + ((((p >> 1) + d) & 31) << 1) + (p & 1)] = phase_hw((uint32_t)d, ph.lo[p], ph.hi[p]);
+          }
+          __syncthreads();  // (the rotated query too)
+          const int qi = lane & 3, bq = lane >> 2;
+          const uint32_t mb = (uint32_t)(m0 + 64 * wave);
+          float qa[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int k = bq + 16 * t, p = k >> 1;
+            const float2 q0 = qz[qi * P + p];
+            const float2 eb = phase_hw(mb, ph.lo[p], ph.hi[p]);
+            qa[t] = (k & 1) ? fmaf(q0.y, eb.x, -q0.x * eb.y) : fmaf(q0.x, eb.x, q0.y * eb.y);
+          }
+          // every lane takes part in the products (a lane past the cache reads the
+          // last record; positions past the sequence are masked after the scores)
+          const int mr = min(m0 + tid, a.cache_len - 1);
+          const float4* lph4 = reinterpret_cast<const float4*>(lph) + lane * 32;
+          float4_t acc = {0.f, 0.f, 0.f, 0.f};
+          constexpr int SPG = GS / SL;  // slices per group
+          static_assert(GS % SL == 0 && (128 / GS) * SPG == 4, "four slices of D = 128");
+          static_for<4>([&](auto sc) __attribute__((always_inline)) {
+            constexpr int sI = decltype(sc)::value, j = sI / SPG, sl = sI % SPG;
+            stage_slice(j, sl);
+            float kx[SL];
+#pragma unroll
+            for (int i = 0; i < SL; ++i) kx[i] = 0.f;
+            rebuild(mr, j, kx);
+            static_for<SP / 2>([&](auto cc) __attribute__((always_inline)) {
+              constexpr int c = decltype(cc)::value, p0 = j * PP + sl * SP + 2 * c;  // pairs p0, p0 + 1
+              const float4 e2 = lph4[((p0 >> 1) + lane) & 31];
+              const float ex[2] = {e2.x, e2.z}, ey[2] = {e2.y, e2.w};
+              float kr[4];
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                const float x = kx[4 * c + 2 * u], y = kx[4 * c + 2 * u + 1];
+                kr[2 * u] = x * ex[u] - y * ey[u];
+                kr[2 * u + 1] = fmaf(x, ey[u], y * ex[u]);
+              }
+              // the wait takes the four values as operands: every product is issued
+              // at least eight wait states after their last write
+              asm volatile("s_nop 7" : "+v"(kr[0]), "+v"(kr[1]), "+v"(kr[2]), "+v"(kr[3]));
+              static_for<4>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int i = decltype(ic)::value, k = 2 * p0 + i;
+                acc = __builtin_amdgcn_mfma_f32_4x4x1f32(qa[k >> 4], kr[i], acc, 4, k & 15, 0);
+              });
+            });
+          });
+#pragma unroll
+          for (int hh = 0; hh < NH; ++hh) s[0][hh] = acc[hh];
+          return;
+        }
+      }
+      for (int j = 0; j < G; ++j) {
+        for (int sl = 0; sl < GS / SL; ++sl) {
+          stage_slice(j, sl);
 #pragma unroll
           for (int t = 0; t < TPT; ++t) {  // (unrolled: s[t] stays in registers)
             const int m = m0 + tid + kThreads * t;
@@ -222,21 +335,7 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
               float kx[SL];
   #pragma unroll
               for (int i = 0; i < SL; ++i) kx[i] = 0.f;
-              for (int r = 0; r < K.R; ++r) {
-                const int code = kfield(m, r * G + j);
-                const int ei = r * K.Nc + code;
-                const uint4* e = reinterpret_cast<const uint4*>(cbs) + ei * 4;
-  #pragma unroll
-                for (int v = 0; v < SL / 8; ++v) {
-                  const uint4 w = e[(v + (ei >> 2)) & 3];
-                  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-  #pragma unroll
-                  for (int u = 0; u < 4; ++u) {
-                    kx[8 * v + 2 * u] = add_f16_lo(kx[8 * v + 2 * u], wd[u]);
-                    kx[8 * v + 2 * u + 1] = add_f16_hi(kx[8 * v + 2 * u + 1], wd[u]);
-                  }
-                }
-              }
+              rebuild(m, j, kx);
   #pragma unroll
               for (int pp = 0; pp < SP; ++pp) {
                 const int p = j * PP + sl * SP + pp;
@@ -330,6 +429,9 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
     float acc = 0.f;
     for (int w = 0; w < NW; ++w) acc += red[hh * NW + w];
     lsum[hh] = acc;
+    // (summed here: left to the end, the wavefront sums read above stay live in
+    // registers through the value stage)
+    asm volatile("" : "+v"(lsum[hh]));
   }
 
   if constexpr (BITV) {
@@ -393,29 +495,11 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
   } else {
   // value histograms and contraction with the value codebook: RB rounds of a
   // group per pass (all of them where their histograms fit the table's LDS),
-  // bins [head][round][code]
+  // bins [round][code][head]
   const int RB = generic_hist_rounds(K, V, NH);
   const int NBIN = RB * V.Nc;
   for (int j = 0; j < G; ++j) {
     for (int r = 0; r < V.R; r += RB) {
-      __syncthreads();
-      for (int i = tid; i < NH * NBIN; i += kThreads) hist[i] = 0u;
-      __syncthreads();
-#pragma unroll
-      for (int t = 0; t < TPT; ++t) {
-        const int m = m0 + tid + kThreads * t;
-        if (m < L) {
-          uint32_t fx[NH];
-#pragma unroll
-          for (int hh = 0; hh < NH; ++hh) fx[hh] = (uint32_t)fmaf(s[t][hh], (float)(1 << kHistShift), 0.5f);
-          for (int rr = 0; rr < RB; ++rr) {
-            const int code = vfield(m, (r + rr) * G + j);
-#pragma unroll
-            for (int hh = 0; hh < NH; ++hh) atomicAdd(&hist[hh * NBIN + rr * V.Nc + code], fx[hh]);
-          }
-        }
-      }
-      __syncthreads();
       // the pass's rounds of group j are consecutive in the codebook: bin b
       // (round r + b / Nc, code b % Nc) at cvp[b * GS]
       const _Float16* cvp = a.vcb + ((((size_t)h * G + j) * V.R + r) * V.Nc) * GS;
@@ -428,26 +512,151 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
       // lanes of those outputs (adjacent, in one wavefront) are added with shuffles
       constexpr int NOV = NH * GS / 8;
       constexpr int PV = GS % 8 != 0 ? 0 : (kThreads / NOV > 64 ? 64 : kThreads / NOV);
+      // codebook bins per batch of loads
+      constexpr int CBB = GS >= kWideGroup ? 8 : 4;
+      const int pv_o = PV >= 2 ? tid / PV : 0, pv_part = PV >= 2 ? tid % PV : 0;
+      const bool pv_on = PV >= 2 && pv_o < NOV;
+      const int pv_ev = PV >= 2 ? pv_o % (GS / 8) : 0;
+      auto load_bins = [&](int l0, uint4 (&w)[CBB]) {
+#pragma unroll
+        for (int u = 0; u < CBB; ++u) {
+          const int l = l0 + u * PV;
+          w[u] = l < NBIN ? *reinterpret_cast<const uint4*>(cvp + (size_t)l * GS + 8 * pv_ev) : make_uint4(0u, 0u, 0u, 0u);
+        }
+      };
+      // Wide groups, where the wavefronts' partial sums fit the histogram's
+      // region: the contraction on v_mfma_f32_16x16x16_f16 (below).
+      constexpr int NHQ = (NH + 3) / 4;  // 16-row blocks of heads (rows of the A operand)
+      const bool mc_on = GS >= kWideGroup &&
+                         (size_t)NW * 16 * NHQ * 16 <= generic_uni_bytes(K, V, NH);
+      constexpr int MC_NT = GS / 16 > 0 ? GS / 16 : 1;    // output tiles of 16 columns
+      constexpr int MC_WPT = NW / MC_NT > 0 ? NW / MC_NT : 1;  // wavefronts per tile
+      constexpr int MC_SB = 4;                             // K-steps (16 bins each) per batch
+      const int mc_tile = wave / MC_WPT, mc_sub = wave % MC_WPT;
+      const int mc_set = mc_tile >> 1, mc_par = mc_tile & 1, mc_n = lane & 15, mc_kq = lane >> 4;
+      const int mc_steps = (NBIN + 15) / 16;
+      const uint32_t* cv32 = reinterpret_cast<const uint32_t*>(cvp);  // bin b's dwords at b * GS / 2
+      auto mc_load = [&](int st0, uint32_t (&w)[MC_SB][4]) {
+#pragma unroll
+        for (int sb = 0; sb < MC_SB; ++sb)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int st = st0 + sb * MC_WPT, bin = st * 16 + 4 * mc_kq + u;
+            w[sb][u] = (st < mc_steps && bin < NBIN) ? cv32[(size_t)bin * (GS / 2) + 16 * mc_set + mc_n] : 0u;
+          }
+      };
+      uint32_t mc_w[MC_SB][4];
+      static_assert(GS < kWideGroup || (NW % MC_NT == 0), "tiles per workgroup");
+      uint4 wpre[CBB];
+      __syncthreads();
+      for (int i = tid; i < NH * NBIN; i += kThreads) hist[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < TPT; ++t) {
+        const int m = m0 + tid + kThreads * t;
+        if (m < L) {
+          uint32_t fx[NH];
+#pragma unroll
+          for (int hh = 0; hh < NH; ++hh) fx[hh] = (uint32_t)fmaf(s[t][hh], (float)(1 << kHistShift), 0.5f);
+          for (int rr = 0; rr < RB; ++rr) {
+            const int bin = rr * V.Nc + vfield(m, (r + rr) * G + j);
+            if constexpr (NH % 2 == 0) {
+              // two heads per 64-bit add: a head's bin sums to at most
+              // 1024 * 2^20 < 2^32, so no half carries into its neighbour
+#pragma unroll
+              for (int hp = 0; hp < NH / 2; ++hp)
+                __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(hist) + (size_t)bin * (NH / 2) + hp,
+                                       (uint64_t)fx[2 * hp] | ((uint64_t)fx[2 * hp + 1] << 32), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+            } else {
+#pragma unroll
+              for (int hh = 0; hh < NH; ++hh) atomicAdd(&hist[bin * NH + hh], fx[hh]);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      if constexpr (GS >= kWideGroup) {
+        if (mc_on) {
+          // o[head][dim] = sum_bin H[head][bin] CV[bin][dim]. A: row = head (lane
+          // & 15; rows past NH are 0), K = bins 4 kq .. 4 kq + 3 of the step, as the
+          // bins' fixed-point counts scaled to at most 1024 and split into fp16 hi
+          // + lo parts (products keep ~22 bits). B: column n = dimension 32 set +
+          // 2 n + par, the same bins, from one codebook dword (two dimensions) per
+          // bin regrouped with byte permutes. Tile (set, par) is shared by
+          // MC_WPT wavefronts taking every MC_WPT-th step; their partial sums
+          // meet in LDS.
+          float4_t acc = {0.f, 0.f, 0.f, 0.f};
+          const int row = lane & 15;
+          for (int st0 = mc_sub; st0 < mc_steps; st0 += MC_SB * MC_WPT) {
+            mc_load(st0, mc_w);
+#pragma unroll
+            for (int sb = 0; sb < MC_SB; ++sb) {
+              const int st = st0 + sb * MC_WPT;
+              half4_t ahi, alo;
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                const int bin = st * 16 + 4 * mc_kq + u;
+                const uint32_t hv = (st < mc_steps && bin < NBIN && row < NH) ? hist[bin * NH + row] : 0u;
+                const float x = (float)hv * (1.0f / (float)(1 << kHistShift));
+                const _Float16 hi = (_Float16)x;
+                ahi[u] = hi;
+                alo[u] = (_Float16)(x - (float)hi);
+              }
+              const uint32_t sel = mc_par ? 0x07060302u : 0x05040100u;  // high or low halves: dim 2n + par
+              typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+              const half4_t bop = __builtin_bit_cast(
+                  half4_t, (u32x2_t){__builtin_amdgcn_perm(mc_w[sb][1], mc_w[sb][0], sel),
+                                     __builtin_amdgcn_perm(mc_w[sb][3], mc_w[sb][2], sel)});
+              acc = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bop, acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, bop, acc, 0, 0, 0);
+            }
+          }
+          __syncthreads();  // every wavefront is done with the histogram: its region takes the partial sums
+          float* psum = uni;  // [wavefront][16 NHQ lanes][4]: rows 4 kq .. 4 kq + 3 of column n
+          if (lane < 16 * NHQ) *reinterpret_cast<float4*>(psum + ((size_t)wave * 16 * NHQ + lane) * 4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+          __syncthreads();
+          for (int i = tid; i < NH * GS; i += kThreads) {
+            const int hh = i / GS, d = i % GS;
+            const int tile = (d >> 5) * 2 + (d & 1), l = (hh >> 2) * 16 + ((d & 31) >> 1);
+            float sum = 0.f;
+#pragma unroll
+            for (int u = 0; u < MC_WPT; ++u) sum += psum[((size_t)(tile * MC_WPT + u) * 16 * NHQ + l) * 4 + (hh & 3)];
+            oacc[hh * D + j * GS + d] += sum;
+          }
+        }
+      }
       if constexpr (PV >= 2) {
-        const int o = tid / PV, part = tid % PV;
-        if (o < NOV) {
-          const int hh = o / (GS / 8), ev = o % (GS / 8);
+        const int o = pv_o, part = pv_part;
+        if (pv_on && !mc_on) {
+          const int hh = o / (GS / 8), ev = pv_ev;
           float acc[8];
 #pragma unroll
           for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-#pragma unroll 4
-          for (int l = part; l < NBIN; l += PV) {
-            const uint4 w = *reinterpret_cast<const uint4*>(cvp + (size_t)l * GS + 8 * ev);
-            const float hv = (float)hist[hh * NBIN + l];
-            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+          auto consume = [&](const uint4 (&w)[CBB], int l0) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const half2_t xy = __builtin_bit_cast(half2_t, wd[u]);
-              acc[2 * u] = fmaf(hv, (float)xy.x, acc[2 * u]);
-              acc[2 * u + 1] = fmaf(hv, (float)xy.y, acc[2 * u + 1]);
+            for (int u = 0; u < CBB; ++u) {
+              const int l = l0 + u * PV;
+              if (l < NBIN) {
+                const float hv = (float)hist[l * NH + hh];
+                const uint32_t wd[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                  acc[2 * k] = fma_f16_lo(acc[2 * k], wd[k], hv);
+                  acc[2 * k + 1] = fma_f16_hi(acc[2 * k + 1], wd[k], hv);
+                }
+              }
             }
+          };
+          load_bins(part, wpre);
+          consume(wpre, part);
+#pragma unroll 1
+          for (int l0 = part + CBB * PV; l0 < NBIN; l0 += CBB * PV) {
+            uint4 w[CBB];
+            load_bins(l0, w);
+            consume(w, l0);
           }
-#pragma unroll
+          (void)ev;
           for (int off = PV / 2; off > 0; off >>= 1)
 #pragma unroll
             for (int k = 0; k < 8; ++k) acc[k] += __shfl_xor(acc[k], off, 64);
@@ -456,18 +665,18 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
             for (int k = 0; k < 8; ++k) oacc[hh * D + j * GS + 8 * ev + k] += acc[k] * (1.0f / (float)(1 << kHistShift));
         }
       } else if constexpr (PARTS == 1) {
-        for (int i = tid; i < NO; i += kThreads) {
+        for (int i = mc_on ? NO : tid; i < NO; i += kThreads) {
           const int hh = i / GS, e = i % GS;
           float acc = 0.f;
-          for (int l = 0; l < NBIN; ++l) acc = fmaf((float)hist[hh * NBIN + l], (float)cvp[l * GS + e], acc);
+          for (int l = 0; l < NBIN; ++l) acc = fmaf((float)hist[l * NH + hh], (float)cvp[l * GS + e], acc);
           oacc[hh * D + j * GS + e] += acc * (1.0f / (float)(1 << kHistShift));
         }
       } else {
         const int o = tid / PARTS, part = tid % PARTS;
-        if (o < NO) {  // whole groups of PARTS lanes
+        if (o < NO && !mc_on) {  // whole groups of PARTS lanes
           const int hh = o / GS, e = o % GS;
           float acc = 0.f;
-          for (int l = part; l < NBIN; l += PARTS) acc = fmaf((float)hist[hh * NBIN + l], (float)cvp[l * GS + e], acc);
+          for (int l = part; l < NBIN; l += PARTS) acc = fmaf((float)hist[l * NH + hh], (float)cvp[l * GS + e], acc);
 #pragma unroll
           for (int off = PARTS / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
           if (part == 0) oacc[hh * D + j * GS + e] += acc * (1.0f / (float)(1 << kHistShift));
@@ -534,8 +743,7 @@ size_t decode_bitv_smem(const CbShape& k, int nbits, int NH) {
   // the score phase's staging, or the weights [NH][chunk], u [NH][nbits] and
   // kBitSub positions' bit rows
   const size_t score = decode_generic_smem(k, k, NH);
-  const int P = k.D / 2, NW = generic_threads(NH, k.g) / 64;
-  const size_t fixed = (2 * NH * P + NH * k.D + ((NH * (NW > 2 ? NW : 2) + 2 * NH + 4) & ~3)) * sizeof(float);
+  const size_t fixed = generic_fixed_bytes(k, k, NH);
   const size_t bitv = fixed + ((size_t)NH * kGenericChunk + (size_t)NH * nbits) * sizeof(float) +
                       (size_t)kBitSub * (nbits / 8);
   return score > bitv ? score : bitv;
@@ -545,7 +753,7 @@ size_t decode_generic_smem(const CbShape& k, const CbShape& v, int NH) {
   // rotated queries (float2 per pair), output accumulators, reductions, then
   // the query x codebook table of one (group, round) or a value histogram,
   // then (wide groups, short records) the chunk's key and value records
-  return generic_fixed_bytes(k, NH) + generic_uni_bytes(k, v, NH) + generic_rec_bytes(k, v, NH);
+  return generic_fixed_bytes(k, v, NH) + generic_uni_bytes(k, v, NH) + generic_rec_bytes(k, v, NH);
 }
 
 bool decode_fast_path(const CbShape& k, const CbShape& v, int NH, int flags) {

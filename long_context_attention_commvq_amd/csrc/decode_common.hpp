@@ -1,9 +1,23 @@
 // Device helpers shared by the decode kernels.
 #pragma once
 
+#include <type_traits>
+#include <utility>
+
 #include "commvq_internal.hpp"
 
 namespace commvq {
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, each i a compile-time
+// constant (MFMA broadcast selectors must be immediates)
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));

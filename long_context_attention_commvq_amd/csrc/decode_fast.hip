@@ -105,17 +105,6 @@ __device__ __forceinline__ uint32_t add_h2(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) + __builtin_bit_cast(half2_t, b));
 }
 
-// f(std::integral_constant<int, i>) for i = 0 .. N-1, each i a compile-time
-// constant (MFMA broadcast selectors must be immediates)
-template <class F, int... Is>
-__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, Is...>) {
-  (f(std::integral_constant<int, Is>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 // 16 * byte B of w in one instruction (a byte-select operand); used for LDS
 // gather offsets of 16-byte codebook entries.
 template <int B>

@@ -56,6 +56,9 @@ def test_encode_paper_hyperparameters(D, g, Nc, R, H, N):
     dict(B=1, Hq=8, Hkv=1, g=64, Nc=64, R=11, lens=[1200], Lmax=1200),     # eight query heads: 128 KiB table
     dict(B=2, Hq=4, Hkv=1, g=128, Nc=64, R=21, lens=[700, 1], Lmax=800),
     dict(B=1, Hq=4, Hkv=2, g=32, Nc=16, R=6, lens=[999], Lmax=1024),
+    # four query heads per KV head, g = 32: four groups of one slice; a cache
+    # length off the 64-position grid (the last wavefront's lanes past it)
+    dict(B=2, Hq=8, Hkv=2, g=32, Nc=256, R=3, lens=[999, 517], Lmax=1000),
 ])
 def test_decode_paper_hyperparameters(case):
     B, Hq, Hkv, g, Nc, R, Lmax = (case[k] for k in ("B", "Hq", "Hkv", "g", "Nc", "R", "Lmax"))
