@@ -243,8 +243,11 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
       };
       // kx[0 .. SL) += every round's entry of group j's staged slice at m's codes
       auto rebuild = [&](int m, int j, float (&kx)[SL]) {
+        // each round's field is read during the previous round's additions
+        int code_next = kfield(m, j);
         for (int r = 0; r < K.R; ++r) {
-          const int code = kfield(m, r * G + j);
+          const int code = code_next;
+          if (r + 1 < K.R) code_next = kfield(m, (r + 1) * G + j);
           const int ei = r * K.Nc + code;
           const uint4* e = reinterpret_cast<const uint4*>(cbs) + ei * 4;
 #pragma unroll
@@ -512,6 +515,14 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
       // lanes of those outputs (adjacent, in one wavefront) are added with shuffles
       constexpr int NOV = NH * GS / 8;
       constexpr int PV = GS % 8 != 0 ? 0 : (kThreads / NOV > 64 ? 64 : kThreads / NOV);
+      // Wide groups, where the wavefronts' partial sums fit the histogram's
+      // region: the contraction on v_mfma_f32_16x16x16_f16 (below).
+      constexpr int NHQ = (NH + 3) / 4;  // 16-row blocks of heads (rows of the A operand)
+      const bool mc_on = GS >= kWideGroup && NBIN % 16 == 0 &&
+                         (size_t)NW * 16 * NHQ * 16 <= generic_uni_bytes(K, V, NH);
+      constexpr int MC_NT = GS / 16 > 0 ? GS / 16 : 1;    // output tiles of 16 columns
+      constexpr int MC_WPT = NW / MC_NT > 0 ? NW / MC_NT : 1;  // wavefronts per tile
+      static_assert(GS < kWideGroup || (NW % MC_NT == 0), "tiles per workgroup");
       // codebook bins per batch of loads
       constexpr int CBB = GS >= kWideGroup ? 8 : 4;
       const int pv_o = PV >= 2 ? tid / PV : 0, pv_part = PV >= 2 ? tid % PV : 0;
@@ -524,29 +535,7 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
           w[u] = l < NBIN ? *reinterpret_cast<const uint4*>(cvp + (size_t)l * GS + 8 * pv_ev) : make_uint4(0u, 0u, 0u, 0u);
         }
       };
-      // Wide groups, where the wavefronts' partial sums fit the histogram's
-      // region: the contraction on v_mfma_f32_16x16x16_f16 (below).
-      constexpr int NHQ = (NH + 3) / 4;  // 16-row blocks of heads (rows of the A operand)
-      const bool mc_on = GS >= kWideGroup &&
-                         (size_t)NW * 16 * NHQ * 16 <= generic_uni_bytes(K, V, NH);
-      constexpr int MC_NT = GS / 16 > 0 ? GS / 16 : 1;    // output tiles of 16 columns
-      constexpr int MC_WPT = NW / MC_NT > 0 ? NW / MC_NT : 1;  // wavefronts per tile
-      constexpr int MC_SB = 4;                             // K-steps (16 bins each) per batch
-      const int mc_tile = wave / MC_WPT, mc_sub = wave % MC_WPT;
-      const int mc_set = mc_tile >> 1, mc_par = mc_tile & 1, mc_n = lane & 15, mc_kq = lane >> 4;
-      const int mc_steps = (NBIN + 15) / 16;
-      const uint32_t* cv32 = reinterpret_cast<const uint32_t*>(cvp);  // bin b's dwords at b * GS / 2
-      auto mc_load = [&](int st0, uint32_t (&w)[MC_SB][4]) {
-#pragma unroll
-        for (int sb = 0; sb < MC_SB; ++sb)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int st = st0 + sb * MC_WPT, bin = st * 16 + 4 * mc_kq + u;
-            w[sb][u] = (st < mc_steps && bin < NBIN) ? cv32[(size_t)bin * (GS / 2) + 16 * mc_set + mc_n] : 0u;
-          }
-      };
-      uint32_t mc_w[MC_SB][4];
-      static_assert(GS < kWideGroup || (NW % MC_NT == 0), "tiles per workgroup");
+
       uint4 wpre[CBB];
       __syncthreads();
       for (int i = tid; i < NH * NBIN; i += kThreads) hist[i] = 0u;
@@ -558,8 +547,10 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
           uint32_t fx[NH];
 #pragma unroll
           for (int hh = 0; hh < NH; ++hh) fx[hh] = (uint32_t)fmaf(s[t][hh], (float)(1 << kHistShift), 0.5f);
+          int code_next = vfield(m, r * G + j);  // (each round's field read ahead)
           for (int rr = 0; rr < RB; ++rr) {
-            const int bin = rr * V.Nc + vfield(m, (r + rr) * G + j);
+            const int bin = rr * V.Nc + code_next;
+            if (rr + 1 < RB) code_next = vfield(m, (r + rr + 1) * G + j);
             if constexpr (NH % 2 == 0) {
               // two heads per 64-bit add: a head's bin sums to at most
               // 1024 * 2^20 < 2^32, so no half carries into its neighbour
@@ -578,38 +569,53 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
       __syncthreads();
       if constexpr (GS >= kWideGroup) {
         if (mc_on) {
-          // o[head][dim] = sum_bin H[head][bin] CV[bin][dim]. A: row = head (lane
-          // & 15; rows past NH are 0), K = bins 4 kq .. 4 kq + 3 of the step, as the
-          // bins' fixed-point counts scaled to at most 1024 and split into fp16 hi
-          // + lo parts (products keep ~22 bits). B: column n = dimension 32 set +
-          // 2 n + par, the same bins, from one codebook dword (two dimensions) per
-          // bin regrouped with byte permutes. Tile (set, par) is shared by
-          // MC_WPT wavefronts taking every MC_WPT-th step; their partial sums
-          // meet in LDS.
+          // o[head][dim] = sum_bin H[head][bin] CV[bin][dim] per 16-bin K-step.
+          // A: row = head (lane & 15; rows past NH are 0), K = bins 4 kq .. 4 kq + 3
+          // of the step, as the bins' fixed-point counts scaled to at most 1024 and
+          // split into fp16 hi + lo parts (products keep ~22 bits). B: column n =
+          // dimension 32 set + 2 n + par, the same bins, from one codebook dword
+          // (two dimensions) per bin regrouped with byte permutes. Tile (set, par)
+          // is shared by MC_WPT wavefronts taking every MC_WPT-th step, two steps'
+          // codebook dwords in flight; their partial sums meet in LDS.
+          const int tile = wave / MC_WPT, sub = wave % MC_WPT;
+          const int set = tile >> 1, par = tile & 1, n = lane & 15, kq = lane >> 4, row = lane & 15;
+          const int steps = NBIN / 16;
+          const uint32_t* cv32 = reinterpret_cast<const uint32_t*>(cvp);  // bin b's dwords at b * GS / 2
+          const uint32_t voff = (uint32_t)(4 * kq) * (GS / 2) + 16 * set + n;
+          const uint32_t hoff = (uint32_t)(4 * kq) * NH + (row < NH ? row : 0);
+          const bool hrow = row < NH;
+          const uint32_t sel = par ? 0x07060302u : 0x05040100u;  // high or low halves: dim 2n + par
+          auto load = [&](int st, uint32_t (&w)[4]) {
+            const uint32_t* base = cv32 + (size_t)st * 16 * (GS / 2);  // (uniform)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) w[u] = base[voff + u * (GS / 2)];
+          };
           float4_t acc = {0.f, 0.f, 0.f, 0.f};
-          const int row = lane & 15;
-          for (int st0 = mc_sub; st0 < mc_steps; st0 += MC_SB * MC_WPT) {
-            mc_load(st0, mc_w);
+          auto step = [&](int st, const uint32_t (&w)[4]) {
+            half4_t ahi, alo;
 #pragma unroll
-            for (int sb = 0; sb < MC_SB; ++sb) {
-              const int st = st0 + sb * MC_WPT;
-              half4_t ahi, alo;
-#pragma unroll
-              for (int u = 0; u < 4; ++u) {
-                const int bin = st * 16 + 4 * mc_kq + u;
-                const uint32_t hv = (st < mc_steps && bin < NBIN && row < NH) ? hist[bin * NH + row] : 0u;
-                const float x = (float)hv * (1.0f / (float)(1 << kHistShift));
-                const _Float16 hi = (_Float16)x;
-                ahi[u] = hi;
-                alo[u] = (_Float16)(x - (float)hi);
-              }
-              const uint32_t sel = mc_par ? 0x07060302u : 0x05040100u;  // high or low halves: dim 2n + par
-              typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-              const half4_t bop = __builtin_bit_cast(
-                  half4_t, (u32x2_t){__builtin_amdgcn_perm(mc_w[sb][1], mc_w[sb][0], sel),
-                                     __builtin_amdgcn_perm(mc_w[sb][3], mc_w[sb][2], sel)});
-              acc = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bop, acc, 0, 0, 0);
-              acc = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, bop, acc, 0, 0, 0);
+            for (int u = 0; u < 4; ++u) {
+              const uint32_t hv = hrow ? hist[(uint32_t)st * 16 * NH + hoff + u * NH] : 0u;
+              const float x = (float)hv * (1.0f / (float)(1 << kHistShift));
+              const _Float16 hi = (_Float16)x;
+              ahi[u] = hi;
+              alo[u] = (_Float16)(x - (float)hi);
+            }
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            const half4_t bop = __builtin_bit_cast(
+                half4_t, (u32x2_t){__builtin_amdgcn_perm(w[1], w[0], sel), __builtin_amdgcn_perm(w[3], w[2], sel)});
+            acc = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bop, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, bop, acc, 0, 0, 0);
+          };
+          uint32_t w0[4], w1[4];
+          if (sub < steps) load(sub, w0);
+          if (sub + MC_WPT < steps) load(sub + MC_WPT, w1);
+          for (int st = sub; st < steps; st += 2 * MC_WPT) {
+            step(st, w0);
+            if (st + 2 * MC_WPT < steps) load(st + 2 * MC_WPT, w0);
+            if (st + MC_WPT < steps) {
+              step(st + MC_WPT, w1);
+              if (st + 3 * MC_WPT < steps) load(st + 3 * MC_WPT, w1);
             }
           }
           __syncthreads();  // every wavefront is done with the histogram: its region takes the partial sums
