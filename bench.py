@@ -529,7 +529,8 @@ def bench_bitv(args):
     g.manual_seed(w.seed + 90)
     slices = [(torch.randint(0, 256, (B, H, Lmax, bpt), dtype=torch.uint8, device=dev, generator=g),
                torch.randint(0, 256, (B, H, Lmax, bpt), dtype=torch.uint8, device=dev, generator=g),
-               torch.randint(0, 256, (B, Lmax, nb // 8), dtype=torch.uint8, device=dev, generator=g)) for _ in range(NL)]
+               torch.randint(0, 256, (B, nb // 128, Lmax, 16), dtype=torch.uint8, device=dev, generator=g))
+              for _ in range(NL)]  # (value codes in the library's range-major storage)
     q = torch.from_numpy(synth.queries(w.seed + 91, B, Hq, D)).to(dev)
     lens = torch.full((B,), Lmax, dtype=torch.int32, device=dev)
     qpos = lens - 1

@@ -264,7 +264,12 @@ int64_t commvq_decode_bitv_workspace_bytes(int32_t batch, int32_t n_q_heads, int
  * bits are set in vbits[b][t] (bit i = bit i % 8 of byte i / 8); query head hq
  * reads columns [h D, h D + D) of that sum, h its KV head. The weights meet
  * the codes before the rows: u = sum_t p_t s_t, then u^T C.
- *   vbits     device bytes [batch][cache_len][n_bits / 8], 16-byte aligned
+ *   vbits     device bytes, 16-byte aligned: each token's bit string stored in
+ *             ranges of 128 bits, range-major, [batch][n_bits / 128][cache_len][16]
+ *             (bits 128 r .. 128 r + 127 of token t of sequence b are the 16
+ *             bytes at ((b * n_bits / 128 + r) * cache_len + t) * 16); for
+ *             n_bits < 128 one range of n_bits / 8 bytes, [batch][cache_len][n_bits / 8].
+ *             One range of consecutive tokens is thus one contiguous stream
  *   workspace >= commvq_decode_bitv_workspace_bytes(...) bytes, 256-byte
  *             aligned, no initialisation needed
  *   flags     0 or COMMVQ_DECODE_EXACT

@@ -265,13 +265,33 @@ class BitvWorkspace:
         self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
 
 
+def bitv_storage(bits):
+    """Token-major bit strings [B, L, Nc/8] (bit i of a token = bit i % 8 of byte
+    i / 8) -> the library's range-major storage [B, Nc/128, L, 16] (one range of
+    Nc/8 bytes when Nc < 128). A copy; works on torch tensors and numpy arrays."""
+    B, L, nby = bits.shape
+    rb = min(16, nby)
+    v = bits.reshape(B, L, nby // rb, rb)
+    if isinstance(v, torch.Tensor):
+        return v.permute(0, 2, 1, 3).contiguous()
+    import numpy as np
+    return np.ascontiguousarray(v.transpose(0, 2, 1, 3))
+
+
 def decode_attention_bitv(kq: Quantizer, rows: torch.Tensor, q: torch.Tensor, q_pos: torch.Tensor,
                           kcache: torch.Tensor, vbits: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
                           theta_base: float, sm_scale: float | None = None, out: torch.Tensor | None = None,
                           workspace: BitvWorkspace | None = None, flags: int = 0) -> torch.Tensor:
-    """Keys from packed caches [B, Hkv, Lmax, bpt]; values from binary codes
-    vbits uint8 [B, Lmax, Nc/8] and rows fp16 [Nc, Hkv * D]."""
+    """Keys from packed caches [B, Hkv, Lmax, bpt]; values from binary codes in
+    the range-major storage vbits uint8 [B, Nc/128, Lmax, 16] (bitv_storage of
+    the token-major strings) and rows fp16 [Nc, Hkv * D]."""
     B, Hq, D = q.shape
+    nby = rows.shape[0] // 8
+    rb = min(16, nby)
+    want = (B, nby // rb, kcache.shape[2], rb)
+    if vbits.dtype != torch.uint8 or tuple(vbits.shape) != want or not vbits.is_contiguous():
+        raise ValueError(f"vbits must be contiguous uint8 {want} (range-major storage), got {vbits.dtype} "
+                         f"{tuple(vbits.shape)}")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     if out is None:

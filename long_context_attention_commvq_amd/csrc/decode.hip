@@ -462,11 +462,17 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
 #pragma unroll
       for (int hh = 0; hh < NH; ++hh) acc[k][hh] = 0.f;
     const int n = min(L - m0, a.chunk);
-    const uint32_t* bits_g = reinterpret_cast<const uint32_t*>(a.vbits + ((size_t)b * a.cache_len + m0) * TB);
+    // range-major storage: ranges of RW dwords (16 bytes, or the whole string
+    // when shorter), [B][ranges][cache_len][RW]
+    const int RW = TB >= 16 ? 4 : TB / 4, NRG = (TB / 4) / RW;
+    const uint32_t* bits_g = reinterpret_cast<const uint32_t*>(a.vbits) + (size_t)b * NRG * a.cache_len * RW;
     for (int s0 = 0; s0 < n; s0 += kBitSub) {
       const int ns = min(kBitSub, n - s0);
       __syncthreads();  // (the previous rows are read; the weights and u are written)
-      for (int i = tid; i < ns * (TB / 4); i += kThreads) rows_l[i] = bits_g[(size_t)s0 * (TB / 4) + i];
+      for (int i = tid; i < ns * (TB / 4); i += kThreads) {
+        const int p = i / (TB / 4), dw = i % (TB / 4), rr = dw / RW, k = dw % RW;
+        rows_l[i] = bits_g[((size_t)rr * a.cache_len + m0 + s0 + p) * RW + k];
+      }
       __syncthreads();
       const uint8_t* rb = reinterpret_cast<const uint8_t*>(rows_l);
       for (int tl = slot; tl < ns; tl += slots) {

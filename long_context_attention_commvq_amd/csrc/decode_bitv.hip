@@ -71,9 +71,9 @@ __global__ __launch_bounds__(kBvThreads, 1) void bitv_values_kernel(DecodeArgs a
   const uint32_t jn = (uint32_t)(n >> 3);
   const uint32_t selh[2] = {0x0C040C00u + jn * 0x00010001u, 0x0C060C02u + jn * 0x00010001u};
   const uint32_t bmask = (1u << (n & 7)) * 0x00010001u;
-  const int nby = a.nbits / 8;
   const size_t plen = (size_t)npc * a.chunk;
-  const uint8_t* vb = a.vbits + (size_t)b * a.cache_len * nby + 16 * r;
+  // the range's 16 bytes of consecutive tokens are contiguous (range-major storage)
+  const uint8_t* vb = a.vbits + ((size_t)b * NR + r) * a.cache_len * 16;
   const _Float16* pwb = a.pw + (size_t)b * a.Hq * plen;
 
   // operands of the wavefront's k-step kk (ks = wave + 8 kk, 32 positions):
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kBvThreads, 1) void bitv_values_kernel(DecodeArgs a
   auto issue = [&](int kk) {
     const int slot = kk % kBvSlots;
     const int kb0 = m0 + 32 * (wave + kBvWaves * kk);
-    __builtin_amdgcn_global_load_lds(vb + (size_t)min(kb0 + (lane & 31), a.cache_len - 1) * nby,
+    __builtin_amdgcn_global_load_lds(vb + (size_t)min(kb0 + (lane & 31), a.cache_len - 1) * 16,
                                      (lds_void_t*)(ring + slot * 1024), 16, 0, 0);
     const int kb = kb0 + 8 * kg;
 #pragma unroll

@@ -54,7 +54,7 @@ def test_bit_value_decode_matches_oracle(case):
     qpos = np.maximum(lens, 1) - 1
     ref = O.decode_attention_bit_values(q, qpos, kp, vbits, lens, kcb, rows, 500000.0)
     kq = api.Quantizer(dev(kcb), g)
-    out = api.decode_attention_bitv(kq, dev(rows), dev(q), dev(qpos), dev(kp), dev(vbits), dev(lens), Lmax, 500000.0)
+    out = api.decode_attention_bitv(kq, dev(rows), dev(q), dev(qpos), dev(kp), dev(api.bitv_storage(vbits)), dev(lens), Lmax, 500000.0)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     err = row_errors(got.reshape(-1, D), ref.reshape(-1, D))
@@ -91,7 +91,7 @@ def test_bit_value_fast_path_matches_oracle_and_generic(case):
     qpos = np.maximum(lens, 1) - 1
     ref = O.decode_attention_bit_values(q, qpos, kp, vbits, lens, kcb, rows, 500000.0)
     kq = api.Quantizer(dev(kcb), g)
-    args = (kq, dev(rows), dev(q), dev(qpos), dev(kp), dev(vbits), dev(lens), Lmax, 500000.0)
+    args = (kq, dev(rows), dev(q), dev(qpos), dev(kp), dev(api.bitv_storage(vbits)), dev(lens), Lmax, 500000.0)
     fast = api.decode_attention_bitv(*args)
     exact = api.decode_attention_bitv(*args, flags=_lib.COMMVQ_DECODE_EXACT)
     torch.cuda.synchronize()
@@ -112,15 +112,19 @@ def test_bit_value_decode_rejects_bad_arguments():
     q = torch.zeros((1, 4, 64), dtype=torch.float32, device=DEV)
     pos = torch.zeros(1, dtype=torch.int32, device=DEV)
     codes = torch.zeros((1, 2, 16, kq.bytes_per_token), dtype=torch.uint8, device=DEV)
-    bits = torch.zeros((1, 16, 32), dtype=torch.uint8, device=DEV)
+    def bits(nb):  # zero codes of nb bits for the 16 cached positions, in the library's storage
+        return api.bitv_storage(torch.zeros((1, 16, nb // 8), dtype=torch.uint8, device=DEV))
     with pytest.raises(_lib.CommvqError) as e:
-        api.decode_attention_bitv(kq, torch.zeros((256, 100), dtype=torch.float16, device=DEV), q, pos, codes, bits,
-                                  pos + 1, 16, 500000.0)  # dim != Hkv * D
+        api.decode_attention_bitv(kq, torch.zeros((256, 100), dtype=torch.float16, device=DEV), q, pos, codes,
+                                  bits(256), pos + 1, 16, 500000.0)  # dim != Hkv * D
     assert e.value.status == _lib.COMMVQ_ERR_INVALID_ARG
     with pytest.raises(_lib.CommvqError) as e:
-        api.decode_attention_bitv(kq, torch.zeros((96, 128), dtype=torch.float16, device=DEV), q, pos, codes, bits,
-                                  pos + 1, 16, 500000.0)  # 96 bits: not a power of two
+        api.decode_attention_bitv(kq, torch.zeros((96, 128), dtype=torch.float16, device=DEV), q, pos, codes,
+                                  bits(96), pos + 1, 16, 500000.0)  # 96 bits: not a power of two
     assert e.value.status == _lib.COMMVQ_ERR_INVALID_ARG
+    with pytest.raises(ValueError):  # token-major strings instead of the range-major storage
+        api.decode_attention_bitv(kq, torch.zeros((256, 128), dtype=torch.float16, device=DEV), q, pos, codes,
+                                  torch.zeros((1, 16, 32), dtype=torch.uint8, device=DEV), pos + 1, 16, 500000.0)
 
 
 def test_bit_value_decode_full_size_128k_sampled():
@@ -139,7 +143,7 @@ def test_bit_value_decode_full_size_128k_sampled():
     lens = np.array([L], dtype=np.int32)
     kq = api.Quantizer(dev(kcb), g)
     print("[bit values full size] launching", flush=True)
-    out = api.decode_attention_bitv(kq, dev(rows), dev(q), dev(lens - 1), dev(kp), dev(vbits), dev(lens), L, 500000.0)
+    out = api.decode_attention_bitv(kq, dev(rows), dev(q), dev(lens - 1), dev(kp), dev(api.bitv_storage(vbits)), dev(lens), L, 500000.0)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     assert np.all(np.isfinite(got))
@@ -159,7 +163,7 @@ def test_bit_value_fast_path_graph_replay():
     rng = np.random.default_rng(9400)
     kcb = synth.codebook(9401, Hkv, D, g, Nc, R)
     kp = dev(rng.integers(0, 256, size=(B, Hkv, L, 16), dtype=np.uint8))
-    vb = dev(rng.integers(0, 256, size=(B, L, nb // 8), dtype=np.uint8))
+    vb = dev(api.bitv_storage(rng.integers(0, 256, size=(B, L, nb // 8), dtype=np.uint8)))
     rows = dev(bit_rows(9402, nb, Hkv * D))
     kq = api.Quantizer(dev(kcb), g)
     qs = [dev(synth.queries(9403 + i, B, Hq, D)) for i in range(2)]
@@ -201,7 +205,7 @@ def test_bit_value_fast_path_batch_two_long():
     q = synth.queries(9503, B, Hq, D)
     lens = np.array([40000, 33001], dtype=np.int32)
     kq = api.Quantizer(dev(kcb), g)
-    out = api.decode_attention_bitv(kq, dev(rows), dev(q), dev(lens - 1), dev(kp), dev(vbits), dev(lens), Lmax, 500000.0)
+    out = api.decode_attention_bitv(kq, dev(rows), dev(q), dev(lens - 1), dev(kp), dev(api.bitv_storage(vbits)), dev(lens), Lmax, 500000.0)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     for b, h in ((0, 3), (1, 6)):
