@@ -59,6 +59,12 @@ def test_encode_paper_hyperparameters(D, g, Nc, R, H, N):
     # four query heads per KV head, g = 32: four groups of one slice; a cache
     # length off the 64-position grid (the last wavefront's lanes past it)
     dict(B=2, Hq=8, Hkv=2, g=32, Nc=256, R=3, lens=[999, 517], Lmax=1000),
+    # 8 entries and 3 rounds: 24 bins per group, not whole 16-bin steps, so the
+    # contraction takes the per-lane path
+    dict(B=1, Hq=4, Hkv=1, g=64, Nc=8, R=3, lens=[777], Lmax=800),
+    # exact mode (exact phases, dot products on the vector ALUs) with the
+    # matrix-core contraction
+    dict(B=2, Hq=4, Hkv=1, g=64, Nc=64, R=11, lens=[1500, 90], Lmax=1536, exact=True),
 ])
 def test_decode_paper_hyperparameters(case):
     B, Hq, Hkv, g, Nc, R, Lmax = (case[k] for k in ("B", "Hq", "Hkv", "g", "Nc", "R", "Lmax"))
@@ -75,7 +81,8 @@ def test_decode_paper_hyperparameters(case):
     qpos = lens - 1
     ref = O.decode_attention_from_packed(q, qpos, kp, vp, lens, kcb, vcb, 500000.0)
     kq, vq = api.Quantizer(dev(kcb), g), api.Quantizer(dev(vcb), g)
-    out = api.decode_attention(kq, vq, dev(q), dev(qpos), dev(kp), dev(vp), dev(lens), Lmax, 500000.0)
+    out = api.decode_attention(kq, vq, dev(q), dev(qpos), dev(kp), dev(vp), dev(lens), Lmax, 500000.0,
+                               exact=bool(case.get("exact", False)))
     torch.cuda.synchronize()
     err = row_errors(out.cpu().numpy().reshape(-1, D), ref.reshape(-1, D))
     print(f"[decode {case}] max row rel err {err.max():.3e}", flush=True)
