@@ -50,6 +50,8 @@ __device__ __forceinline__ float add_f16_hi(float acc, uint32_t w) {
   return acc;
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
 // acc + x * (the fp16 in the low / high half of w), one v_fma_mix_f32 (exact
 // conversion, one rounding: the same result as fmaf(x, (float)half, acc))
 __device__ __forceinline__ float fma_f16_lo(float acc, uint32_t w, float x) {
@@ -116,6 +118,14 @@ __host__ __device__ inline bool generic_stage_records(const CbShape& k, const Cb
 }
 __host__ __device__ inline size_t generic_rec_bytes(const CbShape& k, const CbShape& v, int NH) {
   return generic_stage_records(k, v, NH) ? (size_t)kGenericChunk * (k.bpt + v.bpt) : 0;
+}
+// Wide groups on the matrix-core score path: a second slice buffer where it fits
+// after everything else, so that the next slice is copied (straight into LDS)
+// while the current one is used.
+__host__ __device__ inline size_t generic_slice_bytes(const CbShape& k) { return (size_t)k.R * k.Nc * 32 * sizeof(_Float16); }
+__host__ __device__ inline bool generic_dbl_slice(const CbShape& k, const CbShape& v, int NH) {
+  return generic_wide_mfma(k, v, NH) && generic_fixed_bytes(k, v, NH) + generic_uni_bytes(k, v, NH) +
+                                            generic_rec_bytes(k, v, NH) + generic_slice_bytes(k) <= 160 * 1024;
 }
 
 // n bytes from global memory to LDS, eight loads in flight per lane
@@ -242,14 +252,14 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
         __syncthreads();
       };
       // kx[0 .. SL) += every round's entry of group j's staged slice at m's codes
-      auto rebuild = [&](int m, int j, float (&kx)[SL]) {
+      auto rebuild = [&](int m, int j, float (&kx)[SL], const _Float16* slice) {
         // each round's field is read during the previous round's additions
         int code_next = kfield(m, j);
         for (int r = 0; r < K.R; ++r) {
           const int code = code_next;
           if (r + 1 < K.R) code_next = kfield(m, (r + 1) * G + j);
           const int ei = r * K.Nc + code;
-          const uint4* e = reinterpret_cast<const uint4*>(cbs) + ei * 4;
+          const uint4* e = reinterpret_cast<const uint4*>(slice) + ei * 4;
 #pragma unroll
           for (int v = 0; v < SL / 8; ++v) {
             const uint4 w = e[(v + (ei >> 2)) & 3];
@@ -259,6 +269,21 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
               kx[8 * v + 2 * u] = add_f16_lo(kx[8 * v + 2 * u], wd[u]);
               kx[8 * v + 2 * u + 1] = add_f16_hi(kx[8 * v + 2 * u + 1], wd[u]);
             }
+          }
+        }
+      };
+      // the slice copied straight into LDS (global_load_lds: lane l of a wavefront
+      // writes 16-byte slot base + l), each slot loading the (entry, chunk) the
+      // swizzled layout puts there; the caller waits (vmcnt) and synchronises
+      auto stage_async = [&](int j, int sl, _Float16* dst) {
+        const _Float16* src = a.kcb + ((size_t)h * G + j) * K.R * K.Nc * GS + sl * SL;
+        const int nv = K.R * K.Nc * (SL / 8);
+        for (int i0 = 0; i0 < nv; i0 += kThreads) {
+          const int sig = i0 + tid;
+          if (sig < nv) {
+            const int e = sig >> 2, v = ((sig & 3) - (e >> 2)) & 3;
+            __builtin_amdgcn_global_load_lds(src + (size_t)e * GS + v * 8,
+                                             (lds_void_t*)(reinterpret_cast<uint4*>(dst) + i0 + 64 * wave), 16, 0, 0);
           }
         }
       };
@@ -274,10 +299,15 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
           // q' for dimensions bq + 16 t only. fp32 operands and sums throughout.
           // Lane phase table: chunk c (pairs 2c, 2c + 1) of row d at slot (c + d) & 31,
           // so that the 64 lanes reading chunk c of their own rows spread over the banks.
+          const bool dbl = generic_dbl_slice(K, V, NH);
+          _Float16* cbs2 = reinterpret_cast<_Float16*>(reinterpret_cast<uint8_t*>(uni) + generic_uni_bytes(K, V, NH) +
+                                                       generic_rec_bytes(K, V, NH));
+          if (dbl) stage_async(0, 0, cbs);  // (first slice in flight while the lane phases are built)
           for (int i = tid; i < 64 * 64; i += kThreads) {
             const int d = i >> 6, p = i & 63;
             lph[d * 64 + ((((p >> 1) + d) & 31) << 1) + (p & 1)] = phase_hw((uint32_t)d, ph.lo[p], ph.hi[p]);
           }
+          if (dbl) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           __syncthreads();  // (the rotated query too)
           const int qi = lane & 3, bq = lane >> 2;
           const uint32_t mb = (uint32_t)(m0 + 64 * wave);
@@ -298,11 +328,18 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
           static_assert(GS % SL == 0 && (128 / GS) * SPG == 4, "four slices of D = 128");
           static_for<4>([&](auto sc) __attribute__((always_inline)) {
             constexpr int sI = decltype(sc)::value, j = sI / SPG, sl = sI % SPG;
-            stage_slice(j, sl);
+            _Float16* cur = (dbl && (sI & 1)) ? cbs2 : cbs;
+            if (dbl) {
+              // the next slice into the other buffer (read by no wavefront since the
+              // previous slice's closing barrier)
+              if constexpr (sI + 1 < 4) stage_async((sI + 1) / SPG, (sI + 1) % SPG, (sI & 1) ? cbs : cbs2);
+            } else {
+              stage_slice(j, sl);
+            }
             float kx[SL];
 #pragma unroll
             for (int i = 0; i < SL; ++i) kx[i] = 0.f;
-            rebuild(mr, j, kx);
+            rebuild(mr, j, kx, cur);
             static_for<SP / 2>([&](auto cc) __attribute__((always_inline)) {
               constexpr int c = decltype(cc)::value, p0 = j * PP + sl * SP + 2 * c;  // pairs p0, p0 + 1
               const float4 e2 = lph4[((p0 >> 1) + lane) & 31];
@@ -322,6 +359,12 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
                 acc = __builtin_amdgcn_mfma_f32_4x4x1f32(qa[k >> 4], kr[i], acc, 4, k & 15, 0);
               });
             });
+            if (dbl) {
+              // the next slice has landed (the compiler does not track these LDS
+              // writes) and every wavefront is done with this one
+              asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+              __syncthreads();
+            }
           });
 #pragma unroll
           for (int hh = 0; hh < NH; ++hh) s[0][hh] = acc[hh];
@@ -338,7 +381,7 @@ __global__ __launch_bounds__(generic_threads(NH, GS)) void decode_generic_kernel
               float kx[SL];
   #pragma unroll
               for (int i = 0; i < SL; ++i) kx[i] = 0.f;
-              rebuild(m, j, kx);
+              rebuild(m, j, kx, cbs);
   #pragma unroll
               for (int pp = 0; pp < SP; ++pp) {
                 const int p = j * PP + sl * SP + pp;
@@ -765,7 +808,8 @@ size_t decode_generic_smem(const CbShape& k, const CbShape& v, int NH) {
   // rotated queries (float2 per pair), output accumulators, reductions, then
   // the query x codebook table of one (group, round) or a value histogram,
   // then (wide groups, short records) the chunk's key and value records
-  return generic_fixed_bytes(k, v, NH) + generic_uni_bytes(k, v, NH) + generic_rec_bytes(k, v, NH);
+  return generic_fixed_bytes(k, v, NH) + generic_uni_bytes(k, v, NH) + generic_rec_bytes(k, v, NH) +
+         (generic_dbl_slice(k, v, NH) ? generic_slice_bytes(k) : 0);
 }
 
 bool decode_fast_path(const CbShape& k, const CbShape& v, int NH, int flags) {
