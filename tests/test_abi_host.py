@@ -352,3 +352,6 @@ def test_bitv_storage_layout():
         assert flat[((b * 8 + r) * 7 + t) * 16 + k] == tm[b, t, byte]
     small = rng.integers(0, 256, size=(1, 5, 8), dtype=np.uint8)  # 64 bits per token
     assert np.array_equal(api.bitv_storage(small).reshape(1, 5, 8), small)
+    import torch  # the same on torch tensors
+    tt = api.bitv_storage(torch.from_numpy(tm))
+    assert tt.is_contiguous() and np.array_equal(tt.numpy(), st)

@@ -40,6 +40,7 @@ def bit_rows(seed, n_bits, dim):
     dict(B=2, Hq=4, Hkv=2, D=64, g=4, Nc=16, R=2, nbits=256, lens=[700, 1], Lmax=800),
     dict(B=1, Hq=8, Hkv=1, D=128, g=8, Nc=256, R=2, nbits=512, lens=[2049], Lmax=2100),     # 8 query heads; chunk edge
     dict(B=3, Hq=8, Hkv=4, D=32, g=2, Nc=4, R=3, nbits=32, lens=[1024, 0, 5], Lmax=1100),   # a zero length
+    dict(B=2, Hq=4, Hkv=1, D=64, g=8, Nc=16, R=1, nbits=64, lens=[300, 17], Lmax=320),      # one 8-byte range per token
 ])
 def test_bit_value_decode_matches_oracle(case):
     B, Hq, Hkv, D, g, Nc, R, nb, Lmax = (case[k] for k in ("B", "Hq", "Hkv", "D", "g", "Nc", "R", "nbits", "Lmax"))
