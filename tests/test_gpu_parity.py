@@ -281,6 +281,11 @@ def test_decode_tiny_workload_end_to_end():
     dict(B=2, Hq=2, Hkv=1, D=64, g=2, Nc=16, R=1, lens=[33, 64], Lmax=64),
     dict(B=2, Hq=8, Hkv=4, D=128, g=8, Nc=256, R=2, Ncv=16, Rv=3, lens=[1024, 2047], Lmax=2048),
     dict(B=1, Hq=4, Hkv=1, D=256, g=16, Nc=256, R=1, lens=[1800], Lmax=1800),
+    # wide groups off D = 128 (vector-ALU dot products, the contraction on the
+    # matrix cores), and a value codebook of another size than the keys'
+    dict(B=2, Hq=8, Hkv=2, D=64, g=32, Nc=64, R=4, lens=[900, 1100], Lmax=1100),
+    dict(B=1, Hq=4, Hkv=1, D=256, g=64, Nc=64, R=3, lens=[1300], Lmax=1300),
+    dict(B=2, Hq=4, Hkv=1, D=128, g=64, Nc=64, R=2, Ncv=256, Rv=1, lens=[1000, 333], Lmax=1024),
 ])
 def test_decode_shapes(case):
     got, ref, err = run_decode_case(seed=zlib.crc32(repr(sorted(case.items())).encode()) % 10000, **case)
