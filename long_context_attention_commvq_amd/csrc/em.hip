@@ -123,8 +123,13 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
               if (om < m || (om == m && oi < mi)) m = om, mi = oi;
             }
             if (fitted && soft) {
+              // each exponential is kept in place of its distance for the sums below
               float sm = 0.f;
-              for (int l = lane; l < Nc; l += 64) sm += __expf((m - dist[n * Nc + l]) * invT);
+              for (int l = lane; l < Nc; l += 64) {
+                const float e = __expf((m - dist[n * Nc + l]) * invT);
+                dist[n * Nc + l] = e;
+                sm += e;
+              }
               sm = em_wave_sum(sm);
               if (lane == 0) {
                 rmin[n] = m;
@@ -147,7 +152,7 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
 #pragma unroll
             for (int n = 0; n < kEmSub; ++n) {
               if (n < ns) {
-                const float w = __expf((rmin[n] - dl[n]) * invT) * rsum[n];
+                const float w = dist[n * Nc + tid] * rsum[n];  // (the row pass's exponential)
                 if (w != 0.f) {
 #pragma unroll
                   for (int k = 0; k < GS; ++k) acc[k] = fmaf(w, res[(n0 + n) * GS + k], acc[k]);
