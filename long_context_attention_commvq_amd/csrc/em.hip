@@ -112,9 +112,21 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
           for (int n = wave; n < kEmSub; n += kEmThreads / 64) {
             float m = INFINITY;
             int mi = 0;  // (a valid index even if every distance is infinite or NaN)
-            for (int l = lane; l < Nc; l += 64) {
-              const float v = dist[n * Nc + l];
-              if (v < m) m = v, mi = l;  // a lane's entries ascend: the first of equal ones is kept
+            // Nc' = 256: the lane's four distances stay in registers for the
+            // exponentials below (the same values either way)
+            const bool nc256 = Nc == 256;
+            float v4[4];
+            if (nc256) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v4[i] = dist[n * Nc + lane + 64 * i];
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (v4[i] < m) m = v4[i], mi = lane + 64 * i;  // ascending entries: the first of equal ones is kept
+            } else {
+              for (int l = lane; l < Nc; l += 64) {
+                const float v = dist[n * Nc + l];
+                if (v < m) m = v, mi = l;  // a lane's entries ascend: the first of equal ones is kept
+              }
             }
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1) {
@@ -125,10 +137,19 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
             if (fitted && soft) {
               // each exponential is kept in place of its distance for the sums below
               float sm = 0.f;
-              for (int l = lane; l < Nc; l += 64) {
-                const float e = __expf((m - dist[n * Nc + l]) * invT);
-                dist[n * Nc + l] = e;
-                sm += e;
+              if (nc256) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const float e = __expf((m - v4[i]) * invT);
+                  dist[n * Nc + lane + 64 * i] = e;
+                  sm += e;
+                }
+              } else {
+                for (int l = lane; l < Nc; l += 64) {
+                  const float e = __expf((m - dist[n * Nc + l]) * invT);
+                  dist[n * Nc + l] = e;
+                  sm += e;
+                }
               }
               sm = em_wave_sum(sm);
               if (lane == 0) {
