@@ -29,7 +29,7 @@
 // workgroup's sums go to the accumulators with fp32 atomics, once per group
 // after its four tiles.
 
-#include "commvq_internal.hpp"
+#include "decode_common.hpp"
 
 namespace commvq {
 namespace {
@@ -37,12 +37,6 @@ namespace {
 constexpr int kEmThreads = 256, kEmTokens = 256, kEmSub = 16;
 constexpr int kEmTiles = 4;  // tiles of kEmTokens vectors per workgroup, one flush of the sums per group
 constexpr size_t kEmCodeScratch = size_t(4) << 20;  // codes of one encoder batch (nearest-entry path)
-
-__device__ __forceinline__ float em_wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
 
 __global__ __launch_bounds__(256) void em_fill_kernel(float* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0.f;
@@ -151,7 +145,7 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
                   sm += e;
                 }
               }
-              sm = em_wave_sum(sm);
+              sm = wave_sum(sm);  // (DPP butterfly; the shuffle butterfly measured 8 % slower overall)
               if (lane == 0) {
                 rmin[n] = m;
                 rsum[n] = 1.f / sm;  // (sm >= 1: the nearest entry's term is 1)
