@@ -38,6 +38,38 @@ constexpr int kEmThreads = 256, kEmTokens = 256, kEmSub = 16;
 constexpr int kEmTiles = 4;  // tiles of kEmTokens vectors per workgroup, one flush of the sums per group
 constexpr size_t kEmCodeScratch = size_t(4) << 20;  // codes of one encoder batch (nearest-entry path)
 
+// Wavefront minimum of (distance, entry) with the lowest entry on equal
+// distances, on the 64-bit key (distance bits << 32 | entry): distances are
+// non-negative (or +inf / NaN, which order above every finite one, as the
+// scalar compare they replace never selects them), so their bits order as the
+// values. DPP butterfly over each row of 16 lanes, then the four rows' results.
+template <int CTRL>
+__device__ __forceinline__ uint64_t em_dpp_u64(uint64_t k) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, 0xf, 0xf, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ uint64_t em_wave_key_min(uint64_t k) {
+  uint64_t o;
+  o = em_dpp_u64<0xb1>(k);   // quad_perm [1,0,3,2]
+  k = o < k ? o : k;
+  o = em_dpp_u64<0x4e>(k);   // quad_perm [2,3,0,1]
+  k = o < k ? o : k;
+  o = em_dpp_u64<0x124>(k);  // row_ror:4
+  k = o < k ? o : k;
+  o = em_dpp_u64<0x128>(k);  // row_ror:8
+  k = o < k ? o : k;
+  uint64_t r = k;
+#pragma unroll
+  for (int row = 0; row < 4; ++row) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 16 * row);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 16 * row);
+    const uint64_t rk = ((uint64_t)hi << 32) | lo;
+    r = row == 0 ? rk : (rk < r ? rk : r);
+  }
+  return r;
+}
+
 __global__ __launch_bounds__(256) void em_fill_kernel(float* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0.f;
 }
@@ -122,11 +154,10 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
                 if (v < m) m = v, mi = l;  // a lane's entries ascend: the first of equal ones is kept
               }
             }
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-              const float om = __shfl_xor(m, o, 64);
-              const int oi = __shfl_xor(mi, o, 64);
-              if (om < m || (om == m && oi < mi)) m = om, mi = oi;
+            {
+              const uint64_t key = em_wave_key_min(((uint64_t)__builtin_bit_cast(uint32_t, m) << 32) | (uint32_t)mi);
+              m = __builtin_bit_cast(float, (uint32_t)(key >> 32));
+              mi = (int)(uint32_t)key;
             }
             if (fitted && soft) {
               // each exponential is kept in place of its distance for the sums below
