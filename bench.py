@@ -639,9 +639,9 @@ def bench_em(args):
         # vector-ALU work per (vector, group, entry): at temperature 0 the step runs the matrix-core encoder
         # (distances on MFMA; one vector op per candidate score, every round of the codebook searched) and
         # adds each vector to its entry's sums; at temperature > 0 the fitting kernel spends g subtractions, g FMAs
-        # and a compare-select per candidate of each round searched, and two exponentials and g + 1 FMAs per entry
+        # and a compare-select per candidate of each round searched, and one exponential and g + 1 FMAs per entry
         # of the fitted round
-        per_entry = q.n_rounds if T == 0 else (r + 1) * (2 * g + 1) + (2 + g + 1)
+        per_entry = q.n_rounds if T == 0 else (r + 1) * (2 * g + 1) + (1 + g + 1)
         ops = N * H * G * Nc * per_entry
         out[label] = {"ms": ms, "vectors_per_s": N * H * G / (ms * 1e-3),
                       "achieved_T_lane_ops": ops / (ms * 1e-3) / 1e12,
