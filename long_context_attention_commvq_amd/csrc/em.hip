@@ -70,55 +70,23 @@ __device__ __forceinline__ uint64_t em_wave_key_min(uint64_t k) {
   return r;
 }
 
-// The same minimum and the same sum (wave_sum's order) on N rows at once, stage
-// by stage: the rows' DPP chains are independent, so their latencies overlap.
-template <int CTRL, int N>
-__device__ __forceinline__ void em_key_min_stage(uint64_t (&k)[N]) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const uint64_t o = em_dpp_u64<CTRL>(k[i]);
-    k[i] = o < k[i] ? o : k[i];
-  }
+// Minimum and sum over each 16-lane DPP row (every lane of the row ends with
+// its row's result): quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_ror 4, row_ror 8.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
 }
-template <int N>
-__device__ __forceinline__ void em_wave_key_min_rows(uint64_t (&k)[N]) {
-  em_key_min_stage<0xb1>(k);
-  em_key_min_stage<0x4e>(k);
-  em_key_min_stage<0x124>(k);
-  em_key_min_stage<0x128>(k);
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    uint64_t r = 0;
-#pragma unroll
-    for (int row = 0; row < 4; ++row) {
-      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k[i], 16 * row);
-      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k[i] >> 32), 16 * row);
-      const uint64_t rk = ((uint64_t)hi << 32) | lo;
-      r = row == 0 ? rk : (rk < r ? rk : r);
-    }
-    k[i] = r;
-  }
+__device__ __forceinline__ uint32_t row16_umin(uint32_t v) {
+  v = min(v, dpp_u<0xb1>(v));
+  v = min(v, dpp_u<0x4e>(v));
+  v = min(v, dpp_u<0x124>(v));
+  return min(v, dpp_u<0x128>(v));
 }
-template <int CTRL, int N>
-__device__ __forceinline__ void em_sum_stage(float (&v)[N]) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] += dpp_f<CTRL>(v[i]);
-}
-template <int N>
-__device__ __forceinline__ void em_wave_sum_rows(float (&v)[N]) {
-  em_sum_stage<0xb1>(v);
-  em_sum_stage<0x4e>(v);
-  em_sum_stage<0x124>(v);
-  em_sum_stage<0x128>(v);
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const int b = __builtin_bit_cast(int, v[i]);
-    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
-    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
-    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
-    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
-    v[i] = (r0 + r1) + (r2 + r3);
-  }
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xb1>(v);
+  v += dpp_f<0x4e>(v);
+  v += dpp_f<0x124>(v);
+  return v + dpp_f<0x128>(v);
 }
 
 __global__ __launch_bounds__(256) void em_fill_kernel(float* p, size_t n) {
@@ -186,48 +154,36 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
           __syncthreads();
           // rows: minimum and its lowest index; for the fitted round the soft
           // weights' sum, or (nearest entry) the vector added to its entry's sums
-          constexpr int kRows = kEmSub / (kEmThreads / 64);  // rows per wavefront
-          static_assert(kRows * (kEmThreads / 64) == kEmSub, "whole rows per wavefront");
+          static_assert(kEmSub == 4 * (kEmThreads / 64), "four rows per wavefront: one per 16-lane DPP row");
           if (fitted && soft && Nc == 256) {
-            // the wavefront's rows n = wave + 4 i side by side, each with the
-            // arithmetic of the per-row loop below (the same values); a lane's four
-            // distances of a row stay in registers for the exponentials
-            float v4[kRows][4];
-            uint64_t key[kRows];
+            // the wavefront's four rows n = wave + 4 i, one per 16-lane DPP row
+            // (i = lane / 16); lane j of it holds entries j + 16 t in registers.
+            // Only the row's smallest distance is needed here: distances are
+            // non-negative, +inf or NaN, so their bits order as unsigned integers
+            // with NaN above +inf, never chosen (the minimum of the per-row loop
+            // below, exactly)
+            const int n = wave + (kEmThreads / 64) * (lane >> 4);
+            float* drow = dist + n * Nc + (lane & 15);
+            float v[16];
+            uint32_t mb = 0x7f800000u;  // +inf
 #pragma unroll
-            for (int i = 0; i < kRows; ++i) {
-              const int n = wave + (kEmThreads / 64) * i;
-              float m = INFINITY;
-              int mi = 0;
-#pragma unroll
-              for (int t = 0; t < 4; ++t) v4[i][t] = dist[n * Nc + lane + 64 * t];
-#pragma unroll
-              for (int t = 0; t < 4; ++t)
-                if (v4[i][t] < m) m = v4[i][t], mi = lane + 64 * t;  // ascending entries: the first of equal ones is kept
-              key[i] = ((uint64_t)__builtin_bit_cast(uint32_t, m) << 32) | (uint32_t)mi;
+            for (int t = 0; t < 16; ++t) {
+              v[t] = drow[16 * t];
+              mb = min(mb, __builtin_bit_cast(uint32_t, v[t]));
             }
-            em_wave_key_min_rows(key);
-            float sm[kRows];
+            const float m = __builtin_bit_cast(float, row16_umin(mb));
+            // each exponential is kept in place of its distance for the sums below
+            float sm = 0.f;
 #pragma unroll
-            for (int i = 0; i < kRows; ++i) {
-              const int n = wave + (kEmThreads / 64) * i;
-              const float m = __builtin_bit_cast(float, (uint32_t)(key[i] >> 32));
-              sm[i] = 0.f;
-#pragma unroll
-              for (int t = 0; t < 4; ++t) {
-                const float e = __expf((m - v4[i][t]) * invT);
-                dist[n * Nc + lane + 64 * t] = e;
-                sm[i] += e;
-              }
+            for (int t = 0; t < 16; ++t) {
+              const float e = __expf((m - v[t]) * invT);
+              drow[16 * t] = e;
+              sm += e;
             }
-            em_wave_sum_rows(sm);
-            if (lane == 0) {
-#pragma unroll
-              for (int i = 0; i < kRows; ++i) {
-                const int n = wave + (kEmThreads / 64) * i;
-                rmin[n] = __builtin_bit_cast(float, (uint32_t)(key[i] >> 32));
-                rsum[n] = 1.f / sm[i];  // (sm >= 1: the nearest entry's term is 1)
-              }
+            sm = row16_sum(sm);
+            if ((lane & 15) == 0) {
+              rmin[n] = m;
+              rsum[n] = 1.f / sm;  // (sm >= 1: the nearest entry's term is 1)
             }
           } else
           for (int n = wave; n < kEmSub; n += kEmThreads / 64) {
