@@ -89,13 +89,32 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v + dpp_f<0x128>(v);
 }
 
+// g consecutive floats from LDS, 16 bytes at a time where g allows (rows of the
+// codebook and of the residuals then start on 16-byte boundaries)
+template <int GS>
+__device__ __forceinline__ void lds_row(const float* p, float (&o)[GS]) {
+  if constexpr (GS % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < GS; k += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(p + k);
+      o[k] = v.x;
+      o[k + 1] = v.y;
+      o[k + 2] = v.z;
+      o[k + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < GS; ++k) o[k] = p[k];
+  }
+}
+
 __global__ __launch_bounds__(256) void em_fill_kernel(float* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0.f;
 }
 
 template <int GS>
 __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
-  extern __shared__ float em_smem[];
+  extern __shared__ __attribute__((aligned(16))) float em_smem[];
   const CbShape s = a.s;
   const int Nc = s.Nc, G = s.G, r = a.round;
   const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -137,14 +156,15 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
           float dl[kEmSub];
           if (tid < Nc) {
             float c[GS];
-#pragma unroll
-            for (int k = 0; k < GS; ++k) c[k] = cr[tid * GS + k];
+            lds_row<GS>(cr + tid * GS, c);
 #pragma unroll
             for (int n = 0; n < kEmSub; ++n) {
+              float e[GS];
+              lds_row<GS>(res + (n0 + n) * GS, e);
               float d = 0.f;
 #pragma unroll
               for (int k = 0; k < GS; ++k) {
-                const float df = res[(n0 + n) * GS + k] - c[k];
+                const float df = e[k] - c[k];
                 d = fmaf(df, df, d);
               }
               dl[n] = d;
@@ -251,8 +271,10 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
               if (n < ns) {
                 const float w = dist[n * Nc + tid] * rsum[n];  // (the row pass's exponential)
                 if (w != 0.f) {
+                  float e[GS];
+                  lds_row<GS>(res + (n0 + n) * GS, e);
 #pragma unroll
-                  for (int k = 0; k < GS; ++k) acc[k] = fmaf(w, res[(n0 + n) * GS + k], acc[k]);
+                  for (int k = 0; k < GS; ++k) acc[k] = fmaf(w, e[k], acc[k]);
                   acc[GS] += w;
                 }
               }
