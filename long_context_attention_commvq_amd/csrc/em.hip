@@ -177,28 +177,36 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
           static_assert(kEmSub == 4 * (kEmThreads / 64), "four rows per wavefront: one per 16-lane DPP row");
           if (fitted && soft && Nc == 256) {
             // the wavefront's four rows n = wave + 4 i, one per 16-lane DPP row
-            // (i = lane / 16); lane j of it holds entries j + 16 t in registers.
-            // Only the row's smallest distance is needed here: distances are
-            // non-negative, +inf or NaN, so their bits order as unsigned integers
-            // with NaN above +inf, never chosen (the minimum of the per-row loop
-            // below, exactly)
+            // (i = lane / 16); lane j of it holds entries 4 j + 64 t + 0..3 in
+            // registers (16-byte LDS accesses, a row's lanes contiguous). Only the
+            // row's smallest distance is needed here: distances are non-negative,
+            // +inf or NaN, so their bits order as unsigned integers with NaN above
+            // +inf, never chosen (the minimum of the per-row loop below, exactly)
             const int n = wave + (kEmThreads / 64) * (lane >> 4);
-            float* drow = dist + n * Nc + (lane & 15);
-            float v[16];
+            float4* drow = reinterpret_cast<float4*>(dist + n * Nc) + (lane & 15);
+            float4 v[4];
             uint32_t mb = 0x7f800000u;  // +inf
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
+            for (int t = 0; t < 4; ++t) {
               v[t] = drow[16 * t];
-              mb = min(mb, __builtin_bit_cast(uint32_t, v[t]));
+              mb = min(mb, min(min(__builtin_bit_cast(uint32_t, v[t].x), __builtin_bit_cast(uint32_t, v[t].y)),
+                               min(__builtin_bit_cast(uint32_t, v[t].z), __builtin_bit_cast(uint32_t, v[t].w))));
             }
             const float m = __builtin_bit_cast(float, row16_umin(mb));
             // each exponential is kept in place of its distance for the sums below
             float sm = 0.f;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-              const float e = __expf((m - v[t]) * invT);
+            for (int t = 0; t < 4; ++t) {
+              float4 e;
+              e.x = __expf((m - v[t].x) * invT);
+              e.y = __expf((m - v[t].y) * invT);
+              e.z = __expf((m - v[t].z) * invT);
+              e.w = __expf((m - v[t].w) * invT);
               drow[16 * t] = e;
-              sm += e;
+              sm += e.x;
+              sm += e.y;
+              sm += e.z;
+              sm += e.w;
             }
             sm = row16_sum(sm);
             if ((lane & 15) == 0) {
@@ -266,10 +274,19 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
             }
             __syncthreads();
           } else if (soft && tid < Nc) {
+            float rs[kEmSub];  // the rows' 1 / sum, 16 bytes at a time
+#pragma unroll
+            for (int n = 0; n < kEmSub; n += 4) {
+              const float4 r4 = *reinterpret_cast<const float4*>(rsum + n);
+              rs[n] = r4.x;
+              rs[n + 1] = r4.y;
+              rs[n + 2] = r4.z;
+              rs[n + 3] = r4.w;
+            }
 #pragma unroll
             for (int n = 0; n < kEmSub; ++n) {
               if (n < ns) {
-                const float w = dist[n * Nc + tid] * rsum[n];  // (the row pass's exponential)
+                const float w = dist[n * Nc + tid] * rs[n];  // (the row pass's exponential)
                 if (w != 0.f) {
                   float e[GS];
                   lds_row<GS>(res + (n0 + n) * GS, e);
