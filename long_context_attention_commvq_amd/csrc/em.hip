@@ -286,14 +286,14 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
 #pragma unroll
             for (int n = 0; n < kEmSub; ++n) {
               if (n < ns) {
+                // (no branch on w == 0: a weight that underflows adds exact zeros, and a
+                // non-finite residual makes every weight of its row NaN, not 0)
                 const float w = dist[n * Nc + tid] * rs[n];  // (the row pass's exponential)
-                if (w != 0.f) {
-                  float e[GS];
-                  lds_row<GS>(res + (n0 + n) * GS, e);
+                float e[GS];
+                lds_row<GS>(res + (n0 + n) * GS, e);
 #pragma unroll
-                  for (int k = 0; k < GS; ++k) acc[k] = fmaf(w, e[k], acc[k]);
-                  acc[GS] += w;
-                }
+                for (int k = 0; k < GS; ++k) acc[k] = fmaf(w, e[k], acc[k]);
+                acc[GS] += w;
               }
             }
           }
