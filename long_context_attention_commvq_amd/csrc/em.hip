@@ -153,7 +153,6 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
           const float* cr = cbf + (size_t)rr * Nc * GS;
           const bool fitted = rr == r;
           // distances: thread l to entry l, for the sub-tile's vectors
-          float dl[kEmSub];
           if (tid < Nc) {
             float c[GS];
             lds_row<GS>(cr + tid * GS, c);
@@ -167,7 +166,6 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
                 const float df = e[k] - c[k];
                 d = fmaf(df, df, d);
               }
-              dl[n] = d;
               dist[n * Nc + tid] = d;
             }
           }
