@@ -128,6 +128,8 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
   float* hacc = rsum + 2 * kEmSub;               // [Nc][GS + 1]: nearest-entry sums (temperature 0 only)
   const bool soft = a.temperature > 0.f;
   const float invT = soft ? 1.f / a.temperature : 0.f;
+  // exp((m - d) / T) = 2^((m - d) * log2(e) / T): one factor, then the hardware exp2
+  const float kexp = invT * 1.44269504f;
   for (int j = 0; j < G; ++j) {
     __syncthreads();  // the previous group's reads of LDS are done
     const _Float16* cbj = a.cb + ((size_t)h * G + j) * s.R * Nc * GS;
@@ -192,16 +194,16 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
             }
             const float m = __builtin_bit_cast(float, row16_umin(mb));
             // each exponential is kept in place of its distance for the sums below
-            float sm = 0.f;
+            float sm;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               float4 e;
-              e.x = __expf((m - v[t].x) * invT);
-              e.y = __expf((m - v[t].y) * invT);
-              e.z = __expf((m - v[t].z) * invT);
-              e.w = __expf((m - v[t].w) * invT);
+              e.x = __builtin_amdgcn_exp2f((m - v[t].x) * kexp);
+              e.y = __builtin_amdgcn_exp2f((m - v[t].y) * kexp);
+              e.z = __builtin_amdgcn_exp2f((m - v[t].z) * kexp);
+              e.w = __builtin_amdgcn_exp2f((m - v[t].w) * kexp);
               drow[16 * t] = e;
-              sm += e.x;
+              sm = t == 0 ? e.x : sm + e.x;
               sm += e.y;
               sm += e.z;
               sm += e.w;
@@ -242,13 +244,13 @@ __global__ __launch_bounds__(kEmThreads) void em_accumulate_kernel(EmArgs a) {
               if (nc256) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                  const float e = __expf((m - v4[i]) * invT);
+                  const float e = __builtin_amdgcn_exp2f((m - v4[i]) * kexp);
                   dist[n * Nc + lane + 64 * i] = e;
                   sm += e;
                 }
               } else {
                 for (int l = lane; l < Nc; l += 64) {
-                  const float e = __expf((m - dist[n * Nc + l]) * invT);
+                  const float e = __builtin_amdgcn_exp2f((m - dist[n * Nc + l]) * kexp);
                   dist[n * Nc + l] = e;
                   sm += e;
                 }
